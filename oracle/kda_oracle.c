@@ -1,0 +1,202 @@
+/*
+ * kda_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain fp64 CPU oracle for Kimi Delta Attention (KDA).  Only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg may load this library; the
+ * product path never does.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [TL-KDA]  "TileLang 实战：KDA 从零到一 -- Chunked 线性注意力", section 1:
+ *             the recurrence S_t = S_{t-1} D_t (I - beta_t k_t k_t^T)
+ *             + beta_t v_t k_t^T, o_t = S_t q_t, with D_t = diag(e^{g_t}) and
+ *             S stored as (d_v, d_k).
+ *   [SGL-PR]  "SGLang PR #26586 (KDA packed decode)", section "实现拆解" item 1
+ *             and the fused_recurrent_kda_packed_decode_kernel snippet: the
+ *             gate g = -exp(A_log) * softplus(a + dt_bias), beta = sigmoid(b),
+ *             the optional in-kernel L2 norm of q and k (eps 1e-6 inside the
+ *             square root), q scaled after normalisation, the update order
+ *             decay -> delta -> write -> read, the packed qkv offsets, the
+ *             GQA head map and the pad slot (index < 0 -> zero output, no
+ *             state write).
+ *
+ * The per-token update below is the recurrence of [TL-KDA] section 1 written
+ * as the four steps of [SGL-PR]:
+ *     S <- S * diag(e^g)            (decay along the key axis)
+ *     u <- beta * (v - S k)         (delta)
+ *     S <- S + u k^T                (write)
+ *     o <- S (scale * q)            (read after the write: o_t = S_t q_t)
+ * Expanding S D (I - beta k k^T) + beta v k^T gives exactly these steps.
+ *
+ * softplus is evaluated exactly as max(x,0) + log1p(exp(-|x|)) (no threshold).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double softplus_exact(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* One (sequence, head) chain of the token recurrence.
+ * Activations are packed token-major: x[(tok*H + h)*d + c].
+ * S is (dv, dk) row-major, updated in place. */
+static void oracle_chain(const double *q, const double *k, const double *v,
+                         const double *a, const double *b, double A_exp,
+                         const double *dt, double *S, double *o,
+                         int64_t tok0, int64_t len, int H, int h, int dk, int dv,
+                         double scale, double *eg, double *u)
+{
+    for (int64_t t = 0; t < len; ++t) {
+        const int64_t tok = tok0 + t;
+        const double *qt = q + (tok * H + h) * (int64_t)dk;
+        const double *kt = k + (tok * H + h) * (int64_t)dk;
+        const double *vt = v + (tok * H + h) * (int64_t)dv;
+        const double *at = a + (tok * H + h) * (int64_t)dk;
+        const double beta = sigmoid(b[tok * H + h]);
+        for (int c = 0; c < dk; ++c)
+            eg[c] = exp(-A_exp * softplus_exact(at[c] + dt[c]));
+        /* decay, then delta: u = beta (v - S' k) */
+        for (int r = 0; r < dv; ++r) {
+            double *Sr = S + (int64_t)r * dk;
+            double w = 0.0;
+            for (int c = 0; c < dk; ++c) {
+                Sr[c] *= eg[c];
+                w += Sr[c] * kt[c];
+            }
+            u[r] = beta * (vt[r] - w);
+        }
+        /* write, then read with the updated state */
+        double *ot = o + (tok * H + h) * (int64_t)dv;
+        for (int r = 0; r < dv; ++r) {
+            double *Sr = S + (int64_t)r * dk;
+            double acc = 0.0;
+            for (int c = 0; c < dk; ++c) {
+                Sr[c] += u[r] * kt[c];
+                acc += Sr[c] * qt[c];
+            }
+            ot[r] = scale * acc;
+        }
+    }
+}
+
+/*
+ * Chunk-free forward over packed variable-length sequences.
+ *   q,k,a : [T_total, H, dk]   v, o : [T_total, H, dv]   b : [T_total, H]
+ *   A_log : [H]  dt_bias : [H, dk]
+ *   h0    : [n_seq, H, dv, dk] or NULL (zero initial state)
+ *   hT    : [n_seq, H, dv, dk] or NULL
+ *   cu_seqlens : [n_seq + 1] token offsets (int64)
+ *   chains: optional list of chain ids (seq * H + head) to compute; NULL = all.
+ *           Outputs of chains not listed are left untouched.
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int kda_oracle_fwd(const double *q, const double *k, const double *v,
+                   const double *a, const double *b, const double *A_log,
+                   const double *dt_bias, const double *h0,
+                   const int64_t *cu_seqlens, int n_seq, int H, int dk, int dv,
+                   double scale, const int32_t *chains, int n_chains,
+                   double *o, double *hT, int n_threads)
+{
+    if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !cu_seqlens || !o)
+        return -1;
+    if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    const int total = chains ? n_chains : n_seq * H;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : err)
+#endif
+    for (int i = 0; i < total; ++i) {
+        const int id = chains ? chains[i] : i;
+        const int s = id / H, h = id % H;
+        if (s < 0 || s >= n_seq) { err |= 1; continue; }
+        double *S = (double *)malloc(sizeof(double) * ((size_t)dv * dk + dk + dv));
+        if (!S) { err |= 1; continue; }
+        double *eg = S + (size_t)dv * dk, *u = eg + dk;
+        const size_t off = ((size_t)s * H + h) * (size_t)dv * dk;
+        if (h0) memcpy(S, h0 + off, sizeof(double) * (size_t)dv * dk);
+        else memset(S, 0, sizeof(double) * (size_t)dv * dk);
+        oracle_chain(q, k, v, a, b, exp(A_log[h]), dt_bias + (size_t)h * dk, S, o,
+                     cu_seqlens[s], cu_seqlens[s + 1] - cu_seqlens[s], H, h, dk, dv,
+                     scale, eg, u);
+        if (hT) memcpy(hT + off, S, sizeof(double) * (size_t)dv * dk);
+        free(S);
+    }
+    (void)n_threads;
+    return err ? -1 : 0;
+}
+
+/*
+ * One T=1 decode step over a state pool, as in [SGL-PR]:
+ *   qkv  : [B, 2*H*K + HV*V]  (q heads, then k heads, then v heads)
+ *   a    : [B, HV*K]   b : [B, HV]   A_log : [HV]   dt_bias : [HV*K]
+ *   pool : [P, HV, V, K] updated in place for the referenced slots
+ *   state_idx : [B]; a negative entry is a pad: zero output row, no state write.
+ *   o    : [B, HV, V]
+ * Value head hv reads q/k head hv / (HV / H).
+ */
+int kda_oracle_decode(const double *qkv, const double *a, const double *b,
+                      const double *A_log, const double *dt_bias, double *pool,
+                      const int64_t *state_idx, int B, int H, int HV, int K, int V,
+                      int64_t P, double scale, int l2norm, double *o, int n_threads)
+{
+    if (!qkv || !a || !b || !A_log || !dt_bias || !pool || !state_idx || !o) return -1;
+    if (B < 0 || H <= 0 || HV <= 0 || HV % H != 0 || K <= 0 || V <= 0) return -1;
+    const int64_t row = 2 * (int64_t)H * K + (int64_t)HV * V;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : err)
+#endif
+    for (int i = 0; i < B * HV; ++i) {
+        const int n = i / HV, hv = i % HV, hq = hv / (HV / H);
+        double *on = o + ((int64_t)n * HV + hv) * V;
+        const int64_t idx = state_idx[n];
+        if (idx < 0) {
+            for (int r = 0; r < V; ++r) on[r] = 0.0;
+            continue;
+        }
+        if (idx >= P) { err |= 1; continue; }
+        double *buf = (double *)malloc(sizeof(double) * (3 * (size_t)K + V));
+        if (!buf) { err |= 1; continue; }
+        double *qv = buf, *kv = buf + K, *eg = buf + 2 * K, *u = buf + 3 * K;
+        const double *x = qkv + (int64_t)n * row;
+        for (int c = 0; c < K; ++c) {
+            qv[c] = x[(int64_t)hq * K + c];
+            kv[c] = x[(int64_t)H * K + (int64_t)hq * K + c];
+        }
+        if (l2norm) {
+            double sq = 0.0, sk = 0.0;
+            for (int c = 0; c < K; ++c) { sq += qv[c] * qv[c]; sk += kv[c] * kv[c]; }
+            const double nq = sqrt(sq + 1e-6), nk = sqrt(sk + 1e-6);
+            for (int c = 0; c < K; ++c) { qv[c] /= nq; kv[c] /= nk; }
+        }
+        for (int c = 0; c < K; ++c) qv[c] *= scale;
+        const double A_exp = exp(A_log[hv]);
+        for (int c = 0; c < K; ++c)
+            eg[c] = exp(-A_exp * softplus_exact(a[(int64_t)n * HV * K + (int64_t)hv * K + c] +
+                                                dt_bias[(int64_t)hv * K + c]));
+        const double beta = sigmoid(b[(int64_t)n * HV + hv]);
+        const double *vv = x + 2 * (int64_t)H * K + (int64_t)hv * V;
+        double *S = pool + (idx * HV + hv) * (int64_t)V * K;
+        for (int r = 0; r < V; ++r) {
+            double *Sr = S + (int64_t)r * K;
+            double w = 0.0;
+            for (int c = 0; c < K; ++c) { Sr[c] *= eg[c]; w += Sr[c] * kv[c]; }
+            u[r] = beta * (vv[r] - w);
+        }
+        for (int r = 0; r < V; ++r) {
+            double *Sr = S + (int64_t)r * K;
+            double acc = 0.0;
+            for (int c = 0; c < K; ++c) { Sr[c] += u[r] * kv[c]; acc += Sr[c] * qv[c]; }
+            on[r] = acc;
+        }
+        free(buf);
+    }
+    (void)n_threads;
+    return err ? -1 : 0;
+}
