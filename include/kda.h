@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * Two entry points, both hand-written HIP for CDNA4:
+ *
+ *   kda_chunk_fwd    chunkwise prefill over dense or packed variable-length
+ *                    sequences, returning the outputs and the final states;
+ *   kda_decode_step  one fused T=1 decode step over a pool of states.
+ *
+ * The method ([TL-KDA] section 1): per (sequence, head), with the state S
+ * stored as (d_v, d_k),
+ *     S_t = S_{t-1} Diag(e^{g_t}) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t (scale * q_t),
+ * with the gate and beta of [SGL-PR]:
+ *     g_t = -exp(A_log[h]) * softplus(g_raw_t + dt_bias[h, :]),
+ *     beta_t = sigmoid(beta_raw_t).
+ *
+ * Sources, cited by page title and section:
+ *   [TL-KDA]  "TileLang 实战：KDA 从零到一 -- Chunked 线性注意力"
+ *   [LA-06]   "06 · linear 路线（一）：kernel trick、RNN 等价与三种计算形式"
+ *   [FKDA-LM] "FlashKDA 里的 L 矩阵和 Mqk 矩阵是什么"
+ *   [SGL-PR]  "SGLang PR #26586 (KDA packed decode)"
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers owned by the caller, contiguous
+ *     and row-major as documented per argument, aligned to 16 bytes.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     validation error the call returns a negative kda_status and launches
+ *     nothing.  After a launch, a launch failure is reported as KDA_ERR_HIP.
+ *   - The calls enqueue work on `stream` and return without synchronising;
+ *     results are ready once the caller synchronises the stream.  A kernel
+ *     fault surfaces at that synchronisation.
+ *   - The library allocates no memory, keeps no global mutable state and is
+ *     deterministic (no atomics in the arithmetic): the same inputs give
+ *     bitwise-identical outputs.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = -1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    KDA_ERR_UNSUPPORTED = -3, /* valid but not built (head dim, chunk size, dtype) */
+    KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    KDA_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+} kda_status;
+
+typedef enum {
+    KDA_F32 = 0,   /* float32 activations */
+    KDA_BF16 = 1   /* bfloat16 activations (round to nearest even on output) */
+} kda_dtype;
+
+/*
+ * kda_chunk_fwd -- chunkwise KDA prefill ([FKDA-LM] paragraphs "30秒速览",
+ * "L 矩阵的构造", "Mqk 矩阵的构造", "为什么 CHUNK16", "K2 内核如何消费";
+ * sequence loop inside the workgroup as in [TL-KDA] section 6.4).
+ *
+ * Per (sequence, head, d_v slab) one workgroup walks the chunks of C = 16
+ * tokens in order, keeping its fp32 state slab on chip:
+ *   G = chunk-local cumulative gate (log domain),
+ *   L  (16x16, strictly lower) and Mqk (16x16, lower incl. diagonal) by MFMA,
+ *   INV = (I - L)^{-1} by Neumann squaring,
+ *   U = INV (beta * (v - (k e^G) S^T)),  O = (q e^G) S^T + Mqk U (times scale),
+ *   S <- S Diag(e^{G_C}) + U^T (k e^{G_C - G})   (after the output).
+ *
+ * Layout (T_all = B*T for dense input, = T for packed input):
+ *   q, k, g_raw : [T_all, H, dk]   activation dtype, q and k expected
+ *                                  L2-normalised by the caller
+ *   v, o        : [T_all, H, dv]   activation dtype
+ *   beta_raw    : [T_all, H]       activation dtype (pre-sigmoid)
+ *   A_log       : [H]              float32
+ *   dt_bias     : [H, dk]          float32
+ *   h0          : [n_seq, H, dv, dk] float32 initial states, or NULL for zero
+ *   h_T         : [n_seq, H, dv, dk] float32 final states, or NULL to skip
+ *   cu_seqlens  : NULL for dense input (n_seq must equal B, every sequence
+ *                 has T tokens), or [n_seq + 1] int32 token offsets read on
+ *                 the device (then B must be 1 and cu_seqlens[n_seq] == T;
+ *                 the offsets must be non-decreasing -- not checked on the
+ *                 host, because they live in device memory).
+ *   chunk       : must be 16.
+ *   dk, dv      : 64 or 128 each.
+ *   scale       : multiplies q (usually dk^-1/2).
+ * A zero-length sequence leaves its outputs untouched and writes h_T = h0
+ * (or zeros).  T == 0 is accepted and launches nothing except the h_T copy.
+ * Returns KDA_OK or a negative kda_status.
+ */
+int kda_chunk_fwd(const void *q, const void *k, const void *v,
+                  const void *g_raw, const void *beta_raw,
+                  const float *A_log, const float *dt_bias,
+                  const float *h0, const int32_t *cu_seqlens, int chunk,
+                  void *o, float *h_T,
+                  int B, int T, int H, int dk, int dv, int n_seq,
+                  float scale, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * kda_decode_step -- fused T=1 KDA decode over a state pool ([SGL-PR],
+ * section "实现拆解" item 1 and the packed decode kernel snippet).
+ *
+ * For every row n and value head hv (q/k head hq = hv / (HV / H)):
+ *   idx = state_idx[n]; if idx < 0 (pad slot): o[n, hv, :] = 0, no state access.
+ *   q, k taken from the packed row, optionally L2-normalised
+ *   (x / sqrt(sum x^2 + 1e-6)), then q *= scale;
+ *   g = -exp(A_log[hv]) * softplus(a[n, hv, :] + dt_bias[hv, :]), beta = sigmoid(b[n, hv]);
+ *   S' = S Diag(e^g); u = beta (v - S' k); S = S' + u k^T; o = S q.
+ * The state slot is read and written in place, in one pass over its bytes.
+ *
+ * Layout:
+ *   qkv        : [B, 2*H*K + HV*V] bf16  (all q heads, then all k heads, then v heads)
+ *   a          : [B, HV*K] bf16     b : [B, HV] bf16
+ *   A_log      : [HV] float32       dt_bias : [HV*K] float32
+ *   state_pool : [P, HV, V, K] float32, updated in place
+ *   state_idx  : [B] int32 slot per row; < 0 marks a pad row.  Live entries
+ *                must be distinct and < P (duplicates race; not checked on
+ *                the host because the indices live in device memory).
+ *   o          : [B, HV, V] bf16
+ *   K, V       : 128 each.  HV % H == 0.
+ *   flags      : bit 0 set = L2-normalise q and k in the kernel.
+ * Returns KDA_OK or a negative kda_status.
+ */
+int kda_decode_step(const void *qkv, const void *a, const void *b,
+                    const float *A_log, const float *dt_bias,
+                    float *state_pool, const int32_t *state_idx, void *o,
+                    int B, int H, int HV, int K, int V, int P,
+                    float scale, int flags, hipStream_t stream);
+
+#define KDA_DECODE_L2NORM 1
+
+/* Human-readable name of a kda_status value (static string). */
+const char *kda_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,138 @@
+"""Python binding of libkda (MI355X / gfx950 Kimi Delta Attention).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/kda.h.  PyTorch provides device memory and
+the current stream.  There is no CPU fallback: if the library is not built or
+a tensor is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lib = None
+
+KDA_F32, KDA_BF16 = 0, 1
+KDA_DECODE_L2NORM = 1
+
+EXPORTS = ("kda_chunk_fwd", "kda_decode_step", "kda_status_str")
+
+
+class KDAError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (built by `__graft_entry__.build()` or
+    `python kimi_delta_attention_kda_amd/build.py`)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise KDAError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, F, I, P]
+    lib.kda_chunk_fwd.restype = I
+    lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
+    lib.kda_decode_step.restype = I
+    lib.kda_status_str.argtypes = [I]
+    lib.kda_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise KDAError(f"libkda error {rc}: {load_library().kda_status_str(rc).decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(name, t, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise KDAError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if not t.is_contiguous():
+        raise KDAError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise KDAError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
+              chunk: int = 16, scale=None, output_final_state: bool = True,
+              o=None, h_T=None, stream=None):
+    """Chunkwise KDA prefill.
+
+    q, k, g_raw: [B, T, H, dk]; v: [B, T, H, dv]; beta_raw: [B, T, H] -- all
+    float32 or all bfloat16 (q, k L2-normalised by the caller).
+    A_log: [H] float32; dt_bias: [H, dk] float32.
+    h0: [N, H, dv, dk] float32 or None.  cu_seqlens: [N+1] int32 (then B == 1).
+    Returns (o [B, T, H, dv], h_T [N, H, dv, dk] float32 or None)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    act = q.dtype
+    if act not in (torch.float32, torch.bfloat16):
+        raise KDAError("activations must be float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw)):
+        _dev(name, t, act)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("h0", h0)):
+        _dev(name, t, torch.float32)
+    _dev("cu_seqlens", cu_seqlens, torch.int32)
+    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or tuple(beta_raw.shape) != (B, T, H):
+        raise KDAError("inconsistent activation shapes")
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if scale is None:
+        scale = dk ** -0.5
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=act, device=q.device)
+    _dev("o", o, act)
+    if output_final_state and h_T is None:
+        h_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
+    _dev("h_T", h_T, torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(load_library().kda_chunk_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
+        _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), B, T, H, dk, dv, n_seq,
+        float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
+    return o, h_T
+
+
+def decode_step(qkv, a, b, A_log, dt_bias, state_pool, state_idx, num_heads: int,
+                num_v_heads: int, head_k_dim: int = 128, head_v_dim: int = 128, scale=None,
+                l2norm: bool = True, o=None, stream=None):
+    """One fused T=1 decode step; `state_pool` [P, HV, V, K] float32 is updated
+    in place.  qkv: [B, 2*H*K + HV*V] bf16; a: [B, HV*K] bf16; b: [B, HV] bf16;
+    A_log: [HV] f32; dt_bias: [HV*K] f32; state_idx: [B] int32 (< 0 = pad).
+    Returns o [B, HV, V] bf16."""
+    B = qkv.shape[0]
+    H, HV, K, V = num_heads, num_v_heads, head_k_dim, head_v_dim
+    for name, t in (("qkv", qkv), ("a", a), ("b", b)):
+        _dev(name, t, torch.bfloat16)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("state_pool", state_pool)):
+        _dev(name, t, torch.float32)
+    _dev("state_idx", state_idx, torch.int32)
+    if qkv.shape[-1] != 2 * H * K + HV * V or a.numel() != B * HV * K or b.numel() != B * HV \
+            or tuple(state_pool.shape[1:]) != (HV, V, K) or state_idx.numel() != B:
+        raise KDAError("inconsistent decode shapes")
+    if scale is None:
+        scale = K ** -0.5
+    if o is None:
+        o = torch.empty((B, HV, V), dtype=torch.bfloat16, device=qkv.device)
+    _dev("o", o, torch.bfloat16)
+    if stream is None:
+        stream = torch.cuda.current_stream(qkv.device).cuda_stream
+    _check(load_library().kda_decode_step(
+        _ptr(qkv), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool),
+        _ptr(state_idx), _ptr(o), B, H, HV, K, V, state_pool.shape[0], float(scale),
+        KDA_DECODE_L2NORM if l2norm else 0, ctypes.c_void_p(stream)))
+    return o

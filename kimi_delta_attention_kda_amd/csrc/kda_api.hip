@@ -1,0 +1,85 @@
+// kda_api.hip -- extern "C" entry points of libkda (see include/kda.h):
+// argument validation on the host, then one kernel launch on the caller's
+// stream.  No allocation, no synchronisation, no global mutable state.
+#include <stdint.h>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_str(int status)
+{
+    switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (head dims, chunk size or dtype)";
+    case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw,
+                  const void *beta_raw, const float *A_log, const float *dt_bias,
+                  const float *h0, const int32_t *cu_seqlens, int chunk, void *o, float *h_T,
+                  int B, int T, int H, int dk, int dv, int n_seq, float scale,
+                  kda_dtype dtype, hipStream_t stream)
+{
+    if (chunk != 16) return KDA_ERR_UNSUPPORTED;
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return KDA_ERR_UNSUPPORTED;
+    if (dtype == KDA_F32 && dk != 64) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || H <= 0 || n_seq < 0) return KDA_ERR_SHAPE;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_SHAPE;
+    } else if (n_seq != B) {
+        return KDA_ERR_SHAPE;
+    }
+    const long long tokens = cu_seqlens ? (long long)T : (long long)B * T;
+    if (tokens * H * (dk > dv ? dk : dv) > 0x7fffffffLL * 8) return KDA_ERR_SHAPE;
+    if ((long long)n_seq * H * 2 > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!A_log || !dt_bias) return KDA_ERR_NULL;
+    if (n_seq > 0 && tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !o)) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, cu_seqlens};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    if (n_seq == 0) return KDA_OK;
+
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
+    a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.cu_seqlens = cu_seqlens;
+    a.o = o; a.h_T = h_T; a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
+    const hipError_t e = kda::launch_chunk_fwd(a, dtype == KDA_BF16 ? 1 : 0, dk, dv, stream);
+    if (e == hipErrorInvalidValue) return KDA_ERR_UNSUPPORTED;
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_decode_step(const void *qkv, const void *a, const void *b, const float *A_log,
+                    const float *dt_bias, float *state_pool, const int32_t *state_idx, void *o,
+                    int B, int H, int HV, int K, int V, int P, float scale, int flags,
+                    hipStream_t stream)
+{
+    if (K != 128 || V != 128) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || H <= 0 || HV <= 0 || HV % H != 0 || P < 0) return KDA_ERR_SHAPE;
+    if ((long long)B * HV > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (B == 0) return KDA_OK;
+    if (!qkv || !a || !b || !A_log || !dt_bias || !state_pool || !state_idx || !o) return KDA_ERR_NULL;
+    const void *ptrs[] = {qkv, a, b, A_log, dt_bias, state_pool, state_idx, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_decode(
+        static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(a),
+        static_cast<const uint16_t *>(b), A_log, dt_bias, state_pool, state_idx,
+        static_cast<uint16_t *>(o), B, H, HV, scale, flags & KDA_DECODE_L2NORM, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// kda_decode.hip -- fused T=1 KDA decode step for gfx950.
+//
+// Follows the packed decode of [SGL-PR] ("SGLang PR #26586 (KDA packed
+// decode)", section "实现拆解" item 1 and the kernel snippet): q/k/v are
+// sliced out of one packed row by offset, the gate
+// g = -exp(A_log) * softplus(a + dt_bias) and beta = sigmoid(b) are computed
+// in registers, q and k are optionally L2-normalised (eps 1e-6 inside the
+// square root) and q is scaled, then per state row
+//   S' = S Diag(e^g);  u = beta (v - S' k);  S = S' + u k^T;  o = S q.
+// A negative slot index marks a pad row: its output is zeroed and its state
+// is not touched.
+//
+// MI355X mapping.  The step is HBM-bound (64 KiB of fp32 state read and
+// written per (row, value head) against ~1 KiB of activations), so the kernel
+// is one streaming pass:
+//   * one 256-thread workgroup per (row, value head); thread (g, j) with
+//     g = tid / 16 and j = tid % 16 owns state rows g, g+16, ... (8 rows) and
+//     columns [4j, 4j+4) u [64+4j, 64+4j+4): every wave-wide float4 access
+//     covers four contiguous 256-byte row halves;
+//   * all 16 float4 state loads of a thread are issued before any arithmetic
+//     (64 KiB in flight per workgroup);
+//   * the two row reductions S'k and S'q run over the 16 lanes of one row
+//     group; o uses S q = S' q + u (k . q) so the state is read once;
+//   * the updated state goes back with non-temporal stores.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+template <int K_, int V_>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
+    const uint16_t *__restrict__ b, const float *__restrict__ A_log,
+    const float *__restrict__ dt_bias, float *__restrict__ pool,
+    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV,
+    float scale, int l2norm)
+{
+    static_assert(K_ == 128 && V_ == 128, "decode kernel is built for K = V = 128");
+    constexpr int ROWS = V_ / 16;  // rows per thread
+    const int n = blockIdx.x / HV;
+    const int hv = blockIdx.x - n * HV;
+    const int tid = threadIdx.x;
+    const int j = tid & 15;
+    const int g = tid >> 4;
+
+    uint16_t *orow = o + ((size_t)n * HV + hv) * V_;
+    const int idx = state_idx[n];
+    if (idx < 0) {  // pad slot: zero output, no state access
+        if (tid < V_) orow[tid] = 0;
+        return;
+    }
+
+    float *S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_);
+    // Issue the state loads first: rows g + 16 r, two float4 per row.
+    f32x4 s[ROWS][2];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const float *row = S + (size_t)(g + 16 * r) * K_;
+        s[r][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * j));
+        s[r][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * j));
+    }
+
+    const int hq = hv / (HV / H);
+    const size_t D = 2 * (size_t)H * K_ + (size_t)HV * V_;
+    const uint16_t *x = qkv + (size_t)n * D;
+    const int cols[2] = {4 * j, 64 + 4 * j};
+    float qv[8], kv[8], eg[8];
+    const float A = expf(A_log[hv]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint2 qb = *reinterpret_cast<const uint2 *>(x + (size_t)hq * K_ + cols[h]);
+        const uint2 kb = *reinterpret_cast<const uint2 *>(x + (size_t)H * K_ + (size_t)hq * K_ + cols[h]);
+        const uint2 ab = *reinterpret_cast<const uint2 *>(a + ((size_t)n * HV + hv) * K_ + cols[h]);
+        const f32x4 dt = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + cols[h]);
+        const uint32_t qw[2] = {qb.x, qb.y}, kw[2] = {kb.x, kb.y}, aw[2] = {ab.x, ab.y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint16_t qe = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
+            const uint16_t ke = (uint16_t)(kw[e >> 1] >> (16 * (e & 1)));
+            const uint16_t ae = (uint16_t)(aw[e >> 1] >> (16 * (e & 1)));
+            qv[4 * h + e] = bf16_to_f32(qe);
+            kv[4 * h + e] = bf16_to_f32(ke);
+            eg[4 * h + e] = expf(-A * softplus_f(bf16_to_f32(ae) + dt[e]));
+        }
+    }
+    if (l2norm) {
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { sq += qv[c] * qv[c]; sk += kv[c] * kv[c]; }
+        sq = row16_sum(sq);
+        sk = row16_sum(sk);
+        const float iq = 1.0f / sqrtf(sq + 1e-6f), ik = 1.0f / sqrtf(sk + 1e-6f);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { qv[c] *= iq; kv[c] *= ik; }
+    }
+    float kq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { qv[c] *= scale; kq += kv[c] * qv[c]; }
+    kq = row16_sum(kq);
+    const float beta = sigmoid_f(bf16_to_f32(b[(size_t)n * HV + hv]));
+    const uint16_t *vrow = x + 2 * (size_t)H * K_ + (size_t)hv * V_;
+
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        float pk = 0.f, pq = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float sv = s[r][h][e] * eg[4 * h + e];
+                s[r][h][e] = sv;
+                pk += sv * kv[4 * h + e];
+                pq += sv * qv[4 * h + e];
+            }
+        pk = row16_sum(pk);
+        pq = row16_sum(pq);
+        const int row = g + 16 * r;
+        const float u = beta * (bf16_to_f32(vrow[row]) - pk);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[r][h][e] += u * kv[4 * h + e];
+        float *dst = S + (size_t)row * K_;
+        __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
+        __builtin_nontemporal_store(s[r][1], reinterpret_cast<f32x4 *>(dst + 64 + 4 * j));
+        if (j == 0) orow[row] = f32_to_bf16(pq + u * kq);
+    }
+}
+
+hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                         const float *A_log, const float *dt_bias, float *pool,
+                         const int32_t *state_idx, uint16_t *o, int B, int H, int HV,
+                         float scale, int l2norm, hipStream_t stream)
+{
+    hipLaunchKernelGGL((decode_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(256), 0, stream,
+                       qkv, a, b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -4,8 +4,13 @@ This module only draws random numbers and quantises them; it holds none of the
 attention arithmetic.  Both the HIP path (through its tests and benchmark) and
 the fp64 oracle consume exactly the arrays produced here.
 
-Recipe (numpy PCG64 `default_rng(seed)`, float32 draws, then RNE rounding to
-the I/O dtype):
+Recipe (numpy PCG64, float32 draws, then RNE rounding to the I/O dtype).
+Small draws (variable lengths first, then A_log, dt_bias and slot indices)
+come from `default_rng(seed)`.  Every large tensor is filled in blocks of 2^22
+elements, block i from `default_rng(child_i)` where the children are spawned
+from `SeedSequence(seed)` (one child per tensor, then one per block), so the
+blocks can be drawn in parallel and the values do not depend on the thread
+count.  The draws:
   * q, k ~ N(0,1), each head vector L2-normalised in float32 as
     x / sqrt(sum(x^2) + 1e-6) before rounding (the prefill consumes unit keys
     and queries; the decode path normalises in its kernel instead);
@@ -20,6 +25,8 @@ bf16 values are stored as their uint16 bit patterns.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 from typing import Optional
 
@@ -29,28 +36,93 @@ LOG16 = math.log(16.0)
 LOG4 = math.log(4.0)
 
 
+_BLOCK = 1 << 22
+
+
+def _threads():
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return 4
+
+
+def _blockwise(fn, n_elem, block=_BLOCK):
+    """Run fn(i) for every block index; numpy releases the GIL in the work."""
+    nblk = (n_elem + block - 1) // block
+    if nblk <= 1:
+        for i in range(nblk):
+            fn(i)
+        return
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fn, range(nblk)))
+
+
 # ----------------------------------------------------------------------------
 # bf16 helpers (bit level, round to nearest even)
 # ----------------------------------------------------------------------------
 def bf16_bits(x) -> np.ndarray:
     """float32 -> bf16 bit pattern (uint16), round to nearest even."""
-    u = np.ascontiguousarray(x, np.float32).view(np.uint32)
-    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return (rounded >> np.uint32(16)).astype(np.uint16)
+    src = np.ascontiguousarray(x, np.float32)
+    out = np.empty(src.shape, np.uint16)
+    fin, fout = src.reshape(-1).view(np.uint32), out.reshape(-1)
+
+    def work(i):
+        u = fin[i * _BLOCK:(i + 1) * _BLOCK]
+        r = u >> np.uint32(16)
+        r &= np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += u
+        r >>= np.uint32(16)
+        fout[i * _BLOCK:(i + 1) * _BLOCK] = r
+
+    _blockwise(work, fin.size)
+    return out
 
 
 def bf16_to_f32(bits) -> np.ndarray:
     return (np.ascontiguousarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _normal(rng, shape):
-    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+class _Streams:
+    """Independent PCG64 streams for the large tensors of one workload."""
+
+    def __init__(self, seed: int, n: int = 16):
+        self._kids = np.random.SeedSequence(seed).spawn(n)
+        self._next = 0
+
+    def normal(self, shape, scale: float = 1.0) -> np.ndarray:
+        ss = self._kids[self._next]
+        self._next += 1
+        out = np.empty(shape, np.float32)
+        flat = out.reshape(-1)
+        nblk = (flat.size + _BLOCK - 1) // _BLOCK
+        blocks = ss.spawn(nblk)
+
+        def fill(i):
+            seg = flat[i * _BLOCK:(i + 1) * _BLOCK]
+            np.random.default_rng(blocks[i]).standard_normal(out=seg, dtype=np.float32)
+            if scale != 1.0:
+                seg *= np.float32(scale)
+
+        _blockwise(fill, flat.size)
+        return out
 
 
 def _l2norm_f32(x):
-    x = x.astype(np.float32, copy=False)
-    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32) + np.float32(1e-6))
-    return (x / n).astype(np.float32)
+    """x / sqrt(sum(x^2) + 1e-6) over the last axis, in float32, in place."""
+    x = np.ascontiguousarray(x, np.float32)
+    rows = x.reshape(-1, x.shape[-1])
+    per = max(1, _BLOCK // x.shape[-1])
+
+    def work(i):
+        seg = rows[i * per:(i + 1) * per]
+        n = np.sqrt(np.einsum("ij,ij->i", seg, seg, dtype=np.float32)[:, None] + np.float32(1e-6))
+        seg /= n
+
+    _blockwise(work, rows.shape[0], per)
+    return x
 
 
 def _quant(x, dtype):
@@ -136,15 +208,16 @@ def prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str = "b
         n_tok, B_eff, T_eff = int(cu[-1]), 1, int(cu[-1])
     else:
         n_tok, B_eff, T_eff = B * T, B, T
-    q = _l2norm_f32(_normal(rng, (n_tok, H, dk)))
-    k = _l2norm_f32(_normal(rng, (n_tok, H, dk)))
-    v = _normal(rng, (n_tok, H, dv))
-    a = _normal(rng, (n_tok, H, dk))
-    b = _normal(rng, (n_tok, H))
+    st = _Streams(seed)
+    q = _l2norm_f32(st.normal((n_tok, H, dk)))
+    k = _l2norm_f32(st.normal((n_tok, H, dk)))
+    v = st.normal((n_tok, H, dv))
+    a = st.normal((n_tok, H, dk))
+    b = st.normal((n_tok, H))
     A_log = rng.uniform(0.0, A_log_hi, size=H).astype(np.float32)
     dt_bias = rng.uniform(-1.0, 1.0, size=(H, dk)).astype(np.float32)
     n_seq = B_eff if cu is None else len(cu) - 1
-    h0 = (0.02 * _normal(rng, (n_seq, H, dv, dk))).astype(np.float32) if with_h0 else None
+    h0 = st.normal((n_seq, H, dv, dk), 0.02) if with_h0 else None
     if gate_stress > 0:
         hit = rng.random(size=a.shape) < gate_stress
         a[hit] = np.float32(30.0)
@@ -208,15 +281,14 @@ def decode(seed: int, B: int, H: int, HV: int, K: int, V: int, P: int, n_pad: in
     then `n_pad` random rows set to -1."""
     assert P >= B and HV % H == 0
     rng = np.random.default_rng(seed)
+    st = _Streams(seed)
     D = 2 * H * K + HV * V
-    qkv = _normal(rng, (B, D))
-    a = _normal(rng, (B, HV * K))
-    b = _normal(rng, (B, HV))
+    qkv = st.normal((B, D))
+    a = st.normal((B, HV * K))
+    b = st.normal((B, HV))
     dt_bias = rng.uniform(-1.0, 1.0, size=HV * K).astype(np.float32)
     A_log = rng.uniform(0.0, LOG16, size=HV).astype(np.float32)
-    pool = np.empty((P, HV, V, K), np.float32)
-    for p in range(P):  # slot by slot keeps the float32 temporaries small
-        pool[p] = 0.02 * _normal(rng, (HV, V, K))
+    pool = st.normal((P, HV, V, K), 0.02)
     idx = rng.permutation(P)[:B].astype(np.int32)
     if n_pad:
         idx[rng.choice(B, size=n_pad, replace=False)] = -1

@@ -1,0 +1,69 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run the
+HIP path through the C ABI, run the oracle on the same stored values, and
+compare with the tolerances of the spec contract (fp32 I/O: max-abs
+<= 1e-4; bf16 I/O: max-abs <= 2e-2 and RMSE/RMS <= 5e-3), applied to the
+outputs and to the final states."""
+import numpy as np
+import torch
+
+import kimi_delta_attention_kda_amd as kda
+import oracle
+import synth
+
+TOL = {"f32": dict(max_abs=1e-4, rel_rmse=None), "bf16": dict(max_abs=2e-2, rel_rmse=5e-3)}
+
+
+def _t(x, dtype, dev):
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dev)
+
+
+def to_device(p: synth.Prefill, dev="cuda"):
+    """Device tensors in the [B, T, H, d] layout of the binding."""
+    B, T = (p.B, p.T) if p.cu_seqlens is None else (1, p.tokens)
+    sh = lambda x, d: x.reshape(B, T, p.H, d)
+    return dict(
+        q=_t(sh(p.q, p.dk), p.dtype, dev), k=_t(sh(p.k, p.dk), p.dtype, dev),
+        v=_t(sh(p.v, p.dv), p.dtype, dev), g_raw=_t(sh(p.a, p.dk), p.dtype, dev),
+        beta_raw=_t(p.b.reshape(B, T, p.H), p.dtype, dev),
+        A_log=torch.from_numpy(p.A_log).to(dev), dt_bias=torch.from_numpy(p.dt_bias).to(dev),
+        h0=None if p.h0 is None else torch.from_numpy(p.h0).to(dev),
+        cu_seqlens=None if p.cu_seqlens is None else torch.from_numpy(p.cu_seqlens).to(dev))
+
+
+def run_gpu(p: synth.Prefill, dev="cuda"):
+    d = to_device(p, dev)
+    o, hT = kda.chunk_fwd(**d, scale=p.scale)
+    torch.cuda.synchronize()
+    return (o.float().cpu().numpy().reshape(p.tokens, p.H, p.dv).astype(np.float64),
+            hT.cpu().numpy().astype(np.float64))
+
+
+def run_oracle(p: synth.Prefill, heads=None, seqs=None):
+    """Oracle on all chains, or on a subset of heads (and sequences)."""
+    f = p.f64(heads)
+    H = f["q"].shape[1]
+    chains = None if seqs is None else [s * H + h for s in seqs for h in range(H)]
+    return oracle.fwd(f["q"], f["k"], f["v"], f["a"], f["b"], f["A_log"], f["dt_bias"],
+                      h0=f["h0"], cu_seqlens=f["cu_seqlens"], scale=f["scale"], chains=chains)
+
+
+def metrics(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    err = got - ref
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return dict(max_abs=float(np.max(np.abs(err))) if err.size else 0.0,
+                rel_rmse=float(np.sqrt(np.mean(err * err)) / rms) if rms > 0 else 0.0,
+                finite=bool(np.isfinite(got).all()))
+
+
+def assert_close(got, ref, dtype, what=""):
+    m = metrics(got, ref)
+    tol = TOL[dtype]
+    msg = f"{what}: {m} tol {tol}"
+    assert m["finite"], msg
+    assert m["max_abs"] <= tol["max_abs"], msg
+    if tol["rel_rmse"] is not None:
+        assert m["rel_rmse"] <= tol["rel_rmse"], msg
+    return m

@@ -1,0 +1,93 @@
+"""The C-ABI library loads without a GPU, exports every function that
+include/kda.h declares, and rejects bad arguments on the host before any
+launch (these calls never reach the HIP runtime).  CPU only."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kimi_delta_attention_kda_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    txt = open(HDR).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        pytest.fail("libkda.so is not built: run __graft_entry__.build()")
+    return kda.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(kda.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.kda_status_str(code)
+    assert lib.kda_status_str(0) == b"ok"
+
+
+A = ctypes.c_void_p(0x10000)   # 16-byte aligned fake addresses: never dereferenced,
+B = ctypes.c_void_p(0x20000)   # every call below fails validation first
+MIS = ctypes.c_void_p(0x20004)
+
+
+def chunk(lib, **kw):
+    args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, h0=None, cu=None, chunk=16, o=A,
+                hT=None, B=1, T=16, H=1, dk=128, dv=128, n_seq=1, scale=0.1, dtype=1)
+    args.update(kw)
+    return lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["b"],
+                             args["A_log"], args["dt"], args["h0"], args["cu"], args["chunk"],
+                             args["o"], args["hT"], args["B"], args["T"], args["H"], args["dk"],
+                             args["dv"], args["n_seq"], args["scale"], args["dtype"], None)
+
+
+def test_chunk_validation(lib):
+    assert chunk(lib, chunk=32) == -3
+    assert chunk(lib, dk=96) == -3
+    assert chunk(lib, dtype=0, dk=128) == -3       # fp32 activations built for dk = 64
+    assert chunk(lib, dtype=7) == -3
+    assert chunk(lib, H=0) == -2
+    assert chunk(lib, n_seq=2) == -2                # dense input needs n_seq == B
+    assert chunk(lib, cu=A, B=2, n_seq=2) == -2     # packed input needs B == 1
+    assert chunk(lib, A_log=None) == -1
+    assert chunk(lib, q=None) == -1
+    assert chunk(lib, o=MIS) == -4
+    assert chunk(lib, n_seq=0, B=0) == 0            # nothing to do, no launch
+
+
+def decode(lib, **kw):
+    args = dict(qkv=A, a=A, b=A, A_log=B, dt=B, pool=A, idx=A, o=A, B=4, H=2, HV=4, K=128,
+                V=128, P=8, scale=0.1, flags=1)
+    args.update(kw)
+    return lib.kda_decode_step(args["qkv"], args["a"], args["b"], args["A_log"], args["dt"],
+                               args["pool"], args["idx"], args["o"], args["B"], args["H"],
+                               args["HV"], args["K"], args["V"], args["P"], args["scale"],
+                               args["flags"], None)
+
+
+def test_decode_validation(lib):
+    assert decode(lib, K=64) == -3
+    assert decode(lib, HV=3) == -2                   # HV % H != 0
+    assert decode(lib, pool=None) == -1
+    assert decode(lib, idx=MIS) == -4
+    assert decode(lib, B=0) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 16, 1, 64)
+    with pytest.raises(kda.KDAError):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(1, 16, 1), torch.zeros(1), torch.zeros(1, 64))

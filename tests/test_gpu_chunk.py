@@ -1,0 +1,121 @@
+"""GPU parity of kda_chunk_fwd against the fp64 oracle (through the C ABI),
+plus properties that must hold exactly: determinism, chunk-aligned
+continuation and varlen = separate runs are bitwise; continuation at an
+unaligned split and decode-vs-prefill agree within tolerance."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_kda_amd as kda
+import synth
+from kda_testlib import assert_close, metrics, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def check(p, heads=None, seqs=None, what=""):
+    say(what or p.name, "shapes", p.tokens, p.H, p.dk, p.dv, p.dtype)
+    o, hT = run_gpu(p)
+    ro, rh = run_oracle(p, heads, seqs)
+    if heads is not None:
+        o, hT = o[:, heads], hT[:, heads]
+    if seqs is not None:
+        off = p.offsets()
+        rows = np.concatenate([np.arange(off[s], off[s + 1]) for s in seqs])
+        o, ro, hT, rh = o[rows], ro[rows], hT[seqs], rh[seqs]
+    mo = assert_close(o, ro, p.dtype, what + " o")
+    mh = assert_close(hT, rh, p.dtype, what + " h_T")
+    say("  o", mo, " h_T", mh)
+    return mo, mh
+
+
+def test_workload0_tiny_fp32():
+    check(synth.prefill_workload(0), what="tiny-f32")
+
+
+SMALL = [
+    dict(B=2, T=100, H=3, dk=128, dv=128, dtype="bf16", with_h0=True),
+    dict(B=1, T=37, H=2, dk=64, dv=64, dtype="bf16"),
+    dict(B=1, T=53, H=2, dk=128, dv=64, dtype="bf16", with_h0=True),
+    dict(B=1, T=40, H=2, dk=64, dv=128, dtype="bf16"),
+    dict(B=3, T=33, H=2, dk=64, dv=64, dtype="f32", with_h0=True),
+    dict(B=1, T=0, H=2, dk=128, dv=128, dtype="bf16", lengths=[1, 16, 17, 0, 45, 130]),
+    dict(B=1, T=200, H=4, dk=128, dv=128, dtype="bf16", gate_stress=0.05),
+    dict(B=1, T=64, H=2, dk=64, dv=64, dtype="f32", gate_stress=0.1, A_log_hi=math.log(64)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_small(i):
+    kw = dict(SMALL[i])
+    lengths = kw.pop("lengths", None)
+    p = synth.prefill(100 + i, lengths=lengths, **kw)
+    check(p, what=f"small{i}")
+
+
+def test_workload1_full():
+    check(synth.prefill_workload(1), what="prefill-bf16 B4 H16 T4096")
+
+
+@pytest.fixture(scope="module")
+def w2():
+    return synth.prefill_workload(2)
+
+
+def test_workload2_sampled(w2):
+    lengths = np.diff(w2.offsets())
+    seqs = sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), 5, 17})
+    check(w2, heads=[0, 19], seqs=seqs, what="varlen-bf16 32 seqs (2 heads x 4 seqs sampled)")
+
+
+def test_workload3_sampled():
+    p = synth.prefill_workload(3)
+    check(p, heads=[0, 13, 31], what="long-bf16 T131072 (3 heads sampled)")
+
+
+def test_deterministic_and_continuation():
+    p = synth.prefill(7, B=1, T=160, H=2, dk=128, dv=128, dtype="bf16", with_h0=True)
+    say("determinism + continuation", p.tokens)
+    o1, h1 = run_gpu(p)
+    o2, h2 = run_gpu(p)
+    assert np.array_equal(o1, o2) and np.array_equal(h1, h2)
+    for n, exact in ((64, True), (71, False)):
+        a = synth.Prefill(**{**p.__dict__, "T": n, "q": p.q[:n], "k": p.k[:n], "v": p.v[:n],
+                             "a": p.a[:n], "b": p.b[:n]})
+        oa, ha = run_gpu(a)
+        b = synth.Prefill(**{**p.__dict__, "T": p.T - n, "q": p.q[n:], "k": p.k[n:], "v": p.v[n:],
+                             "a": p.a[n:], "b": p.b[n:], "h0": ha.astype(np.float32)})
+        ob, hb = run_gpu(b)
+        if exact:
+            assert np.array_equal(np.concatenate([oa, ob]), o1) and np.array_equal(hb, h1)
+        else:
+            assert_close(np.concatenate([oa, ob]), o1, "bf16", "continuation o")
+            assert_close(hb, h1, "bf16", "continuation h")
+
+
+def test_varlen_equals_separate_runs():
+    lengths = [19, 48, 3]
+    p = synth.prefill(8, B=1, T=0, H=2, dk=64, dv=64, dtype="bf16", lengths=lengths, with_h0=True)
+    say("varlen vs separate", lengths)
+    o, hT = run_gpu(p)
+    off = p.offsets()
+    for s in range(len(lengths)):
+        sl = slice(off[s], off[s + 1])
+        ps = synth.Prefill(**{**p.__dict__, "B": 1, "T": lengths[s], "q": p.q[sl], "k": p.k[sl],
+                              "v": p.v[sl], "a": p.a[sl], "b": p.b[sl], "h0": p.h0[s:s + 1],
+                              "cu_seqlens": None})
+        os_, hs = run_gpu(ps)
+        assert np.array_equal(os_, o[sl]) and np.array_equal(hs[0], hT[s])
+
+
+def test_zero_length_sequence_keeps_h0():
+    p = synth.prefill(9, B=1, T=0, H=2, dk=128, dv=128, dtype="bf16", lengths=[0, 5], with_h0=True)
+    say("zero-length sequence")
+    o, hT = run_gpu(p)
+    assert np.array_equal(hT[0], p.h0[0].astype(np.float64))
