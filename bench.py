@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = one kda_chunk_fwd over the prefill workload (bf16, B=4, H=16,
+T=4096, d_k=d_v=128, chunk 16, zero initial state, final states returned)
+followed by one kda_decode_step over the decode workload (B=256, H=HV=32,
+K=V=128, pool of 512 fp32 states, 8 pad rows).  Inputs are generated on the
+host, copied to HBM, and are resident before the timed region starts.
+
+Printed: one JSON line.  `value` is the prefill throughput in Mtok*head/s
+(token-heads per step / mean chunk_fwd device time); the decode step time is
+reported next to it.  Device times come from HIP events recorded on the
+stream the kernels run on.  `roofline` describes the prefill kernel against
+MI355X's HBM peak, `roofline_decode` the decode kernel.  `cpu_baseline` is the
+fp64 oracle (plain C, OpenMP over chains) timed on the host cores on the same
+prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def prefill_flops_per_tokhead(dk, dv, C=16):
+    """State contractions k~S, q~S, k^r U (6 dk dv) + intra-chunk L, Mqk,
+    INV u, Mqk U (4 C (dk + dv)) + Neumann inverse (6 x 2 C^3 per chunk)."""
+    return 6 * dk * dv + 4 * C * (dk + dv) + 12 * C * C
+
+
+def prefill_bytes(p, elem=2):
+    """Algorithmic HBM bytes: read q, k, a (dk each), v (dv), b (1); write o
+    (dv) per token-head; plus h0 read (if any) and h_T write per chain."""
+    per_tok = elem * (3 * p.dk + p.dv + 1) + elem * p.dv
+    state = 4 * p.dv * p.dk * p.n_seq * p.H
+    return p.tokens * p.H * per_tok + state * (2 if p.h0 is not None else 1)
+
+
+def decode_bytes(d):
+    """State read + write per live (row, head), plus packed qkv, a, b, o and
+    the per-head parameters."""
+    live = int((d.state_idx >= 0).sum())
+    state = 2 * 4 * d.V * d.K * live * d.HV
+    act = 2 * d.B * (2 * d.H * d.K + d.HV * d.V) + 2 * d.B * d.HV * d.K + 2 * d.B * d.HV
+    out = 2 * d.B * d.HV * d.V
+    par = 4 * d.HV + 4 * d.HV * d.K + 4 * d.B
+    return state + act + out + par
+
+
+def source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "chunk_fwd": ["kimi_delta_attention_kda_amd/csrc/kda_chunk_fwd.hip",
+                  "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
+    "decode": ["kimi_delta_attention_kda_amd/csrc/kda_decode.hip",
+               "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-workload", type=int, default=1, choices=[1, 2, 3])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (the path shards by head/sequence with "
+              "no exchange; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kimi_delta_attention_kda_amd as kda
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---------------- inputs (host -> HBM, outside the timed region)
+    p = synth.prefill_workload(args.prefill_workload)
+    B, T = (p.B, p.T) if p.cu_seqlens is None else (1, p.tokens)
+    sh = lambda x, d: x.reshape(B, T, p.H, d)
+    pin = dict(q=bf16(sh(p.q, p.dk)), k=bf16(sh(p.k, p.dk)), v=bf16(sh(p.v, p.dv)),
+               g_raw=bf16(sh(p.a, p.dk)), beta_raw=bf16(p.b.reshape(B, T, p.H)),
+               A_log=torch.from_numpy(p.A_log).to(dev), dt_bias=torch.from_numpy(p.dt_bias).to(dev),
+               h0=None if p.h0 is None else torch.from_numpy(p.h0).to(dev),
+               cu_seqlens=None if p.cu_seqlens is None else torch.from_numpy(p.cu_seqlens).to(dev))
+    o = torch.empty((B, T, p.H, p.dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((p.n_seq, p.H, p.dv, p.dk), dtype=torch.float32, device=dev)
+
+    d = synth.decode_workload()
+    din = dict(qkv=bf16(d.qkv), a=bf16(d.a), b=bf16(d.b), A_log=torch.from_numpy(d.A_log).to(dev),
+               dt_bias=torch.from_numpy(d.dt_bias).to(dev))
+    pool = torch.from_numpy(d.pool).to(dev)
+    sidx = torch.from_numpy(d.state_idx).to(dev)
+    od = torch.empty((d.B, d.HV, d.V), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill_call():
+        kda.chunk_fwd(**pin, scale=p.scale, o=o, h_T=hT)
+
+    def decode_call():
+        kda.decode_step(**din, state_pool=pool, state_idx=sidx, num_heads=d.H,
+                        num_v_heads=d.HV, scale=d.scale, o=od)
+
+    for _ in range(args.warmup):
+        prefill_call()
+        decode_call()
+    torch.cuda.synchronize()
+
+    # ---------------- timed region: K steps, events on the launch stream
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    host_dec = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev[s][0].record()
+        prefill_call()
+        ev[s][1].record()
+        th = time.perf_counter()
+        decode_call()
+        host_dec += time.perf_counter() - th
+        ev[s][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]
+    dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]
+    pre_avg = float(np.mean(pre_ms)) * 1e-3
+    dec_avg = float(np.mean(dec_ms)) * 1e-3
+
+    tokheads = p.tokens * p.H
+    flops = tokheads * prefill_flops_per_tokhead(p.dk, p.dv)
+    pbytes = prefill_bytes(p)
+    dbytes = decode_bytes(d)
+    value = tokheads / pre_avg / 1e6
+    pre_gbs = pbytes / pre_avg / 1e9
+    dec_gbs = dbytes / dec_avg / 1e9
+
+    # ---------------- CPU baseline: fp64 oracle on the same prefill workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        if args.prefill_workload == 1:
+            heads, sample = None, "whole prefill workload (64 chains x 4096 tokens)"
+        else:
+            heads, sample = [0, 1], "2 of the workload's heads, all sequences"
+        f = p.f64(heads)
+        tc = time.perf_counter()
+        oracle.fwd(f["q"], f["k"], f["v"], f["a"], f["b"], f["A_log"], f["dt_bias"], h0=f["h0"],
+                   cu_seqlens=f["cu_seqlens"], scale=f["scale"], n_threads=threads)
+        tcpu = time.perf_counter() - tc
+        th_cnt = f["q"].shape[0] * f["q"].shape[1]
+        cpu = {"value": th_cnt / tcpu / 1e6, "unit": "Mtok*head/s", "cores": threads,
+               "kind": "oracle", "sample": sample, "seconds": round(tcpu, 3)}
+
+    traffic = measured_traffic("chunk_fwd")
+    traffic_d = measured_traffic("decode")
+    line = {
+        "metric": "KDA chunk-fwd Mtok*head/s (+ % of HBM/MFMA roofline); decode step us at B=256",
+        "value": round(value, 2),
+        "unit": "Mtok*head/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"prefill: {p.name}, chunk 16 + decode: {d.name}",
+                   "prefill_tokens": p.tokens, "heads": p.H, "d_k": p.dk, "d_v": p.dv,
+                   "decode_rows": d.B, "parallelism": "single GPU"},
+        "prefill_us": round(pre_avg * 1e6, 2),
+        "prefill_tflops": round(flops / pre_avg / 1e12, 2),
+        "prefill_mfma_frac": round(flops / pre_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "decode_us": round(dec_avg * 1e6, 2),
+        "decode_host_us_per_call": round(host_dec / K * 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "chunk_fwd_kernel<bf16,128,128>",
+                     "algorithmic_bytes": pbytes},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                            "traffic": traffic_d, "kernel": "decode_kernel<128,128>",
+                            "algorithmic_bytes": dbytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -30,9 +30,13 @@
  *   - The calls enqueue work on `stream` and return without synchronising;
  *     results are ready once the caller synchronises the stream.  A kernel
  *     fault surfaces at that synchronisation.
- *   - The library allocates no memory, keeps no global mutable state and is
- *     deterministic (no atomics in the arithmetic): the same inputs give
- *     bitwise-identical outputs.
+ *   - kda_decode_step allocates nothing.  kda_chunk_fwd uses a device
+ *     workspace (ring buffers and flags for its producer/consumer teams,
+ *     about 64 MiB) that the library allocates on the first call on each
+ *     device and keeps until the process exits; calls that overlap in time
+ *     on one device share it and must not run concurrently.
+ *   - Results are deterministic (no atomics in the arithmetic): the same
+ *     inputs give bitwise-identical outputs.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -50,7 +54,8 @@ typedef enum {
     KDA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
     KDA_ERR_UNSUPPORTED = -3, /* valid but not built (head dim, chunk size, dtype) */
     KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
-    KDA_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+    KDA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
+    KDA_ERR_TIMEOUT = -6      /* a chunk-forward team wait gave up (see kda_chunk_fwd_check) */
 } kda_status;
 
 typedef enum {
@@ -63,13 +68,19 @@ typedef enum {
  * "L 矩阵的构造", "Mqk 矩阵的构造", "为什么 CHUNK16", "K2 内核如何消费";
  * sequence loop inside the workgroup as in [TL-KDA] section 6.4).
  *
- * Per (sequence, head, d_v slab) one workgroup walks the chunks of C = 16
- * tokens in order, keeping its fp32 state slab on chip:
+ * Per chunk of C = 16 tokens of one (sequence, head):
  *   G = chunk-local cumulative gate (log domain),
  *   L  (16x16, strictly lower) and Mqk (16x16, lower incl. diagonal) by MFMA,
  *   INV = (I - L)^{-1} by Neumann squaring,
  *   U = INV (beta * (v - (k e^G) S^T)),  O = (q e^G) S^T + Mqk U (times scale),
  *   S <- S Diag(e^{G_C}) + U^T (k e^{G_C - G})   (after the output).
+ * The state-independent part of each chunk (gate, decayed operands, L, Mqk,
+ * INV) is built by producer workgroups and handed through an on-device ring
+ * to consumer workgroups, one per d_v slab, that carry the fp32 state slab in
+ * registers through the sequential chunk loop.  The workgroups of one launch
+ * wait on each other, so the launch needs the GPU's compute units to itself:
+ * if other kernels occupy them, a wait may give up after about a second,
+ * which kda_chunk_fwd_check() reports.
  *
  * Layout (T_all = B*T for dense input, = T for packed input):
  *   q, k, g_raw : [T_all, H, dk]   activation dtype, q and k expected
@@ -132,6 +143,14 @@ int kda_decode_step(const void *qkv, const void *a, const void *b,
                     float scale, int flags, hipStream_t stream);
 
 #define KDA_DECODE_L2NORM 1
+
+/*
+ * kda_chunk_fwd_check -- synchronise `stream` and report whether the last
+ * kda_chunk_fwd on the current device completed its team waits
+ * (KDA_OK) or gave up on one (KDA_ERR_TIMEOUT; its outputs are then invalid).
+ * For tests and debugging; the normal path never needs it.
+ */
+int kda_chunk_fwd_check(hipStream_t stream);
 
 /* Human-readable name of a kda_status value (static string). */
 const char *kda_status_str(int status);

@@ -19,7 +19,7 @@ _lib = None
 KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
-EXPORTS = ("kda_chunk_fwd", "kda_decode_step", "kda_status_str")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_check", "kda_decode_step", "kda_status_str")
 
 
 class KDAError(RuntimeError):
@@ -40,6 +40,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.kda_decode_step.restype = I
+    lib.kda_chunk_fwd_check.argtypes = [P]
+    lib.kda_chunk_fwd_check.restype = I
     lib.kda_status_str.argtypes = [I]
     lib.kda_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -105,6 +107,14 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None
         _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), B, T, H, dk, dv, n_seq,
         float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
     return o, h_T
+
+
+def chunk_fwd_check(stream=None):
+    """Synchronise the stream and raise if the last chunk_fwd gave up on a
+    team wait (its outputs would be invalid)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    _check(load_library().kda_chunk_fwd_check(ctypes.c_void_p(stream)))
 
 
 def decode_step(qkv, a, b, A_log, dt_bias, state_pool, state_idx, num_heads: int,

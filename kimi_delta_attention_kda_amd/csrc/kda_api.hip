@@ -3,12 +3,35 @@
 // stream.  No allocation, no synchronisation, no global mutable state.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/kda.h"
 #include "kda_launch.hpp"
 
 namespace {
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Chunk-forward workspace: one block of device memory per device, allocated on
+// first use and kept until the process exits (team ring buffers + flags).
+constexpr int kMaxDevices = 64;
+std::mutex g_ws_mutex;
+void *g_ws[kMaxDevices] = {};
+
+hipError_t workspace(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    if (!g_ws[dev]) {
+        e = hipMalloc(&g_ws[dev], kda::chunk_workspace_bytes());
+        if (e != hipSuccess) { g_ws[dev] = nullptr; return e; }
+    }
+    *out = g_ws[dev];
+    return hipSuccess;
+}
 
 }  // namespace
 
@@ -23,6 +46,7 @@ const char *kda_status_str(int status)
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration (head dims, chunk size or dtype)";
     case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDA_ERR_HIP: return "HIP launch error";
+    case KDA_ERR_TIMEOUT: return "a chunk-forward team wait timed out (workgroups not co-resident)";
     default: return "unknown status";
     }
 }
@@ -53,13 +77,34 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
     if (n_seq == 0) return KDA_OK;
 
+    void *ws = nullptr;
+    if (workspace(&ws) != hipSuccess) return KDA_ERR_HIP;
     kda::ChunkArgs a;
+    a.ring = static_cast<unsigned char *>(ws);
+    a.flags = reinterpret_cast<int *>(a.ring + (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES);
+    a.ready = a.flags;
+    a.used = a.flags + KDA_MAX_TEAMS * KDA_RING;
+    a.err = a.used + KDA_MAX_TEAMS * KDA_RING;
+    a.n_teams = 0;
     a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
     a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.cu_seqlens = cu_seqlens;
     a.o = o; a.h_T = h_T; a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
     const hipError_t e = kda::launch_chunk_fwd(a, dtype == KDA_BF16 ? 1 : 0, dk, dv, stream);
     if (e == hipErrorInvalidValue) return KDA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_fwd_check(hipStream_t stream)
+{
+    void *ws = nullptr;
+    if (workspace(&ws) != hipSuccess) return KDA_ERR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
+    const int *err = reinterpret_cast<const int *>(static_cast<unsigned char *>(ws) +
+                                                   (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES) +
+                     2 * KDA_MAX_TEAMS * KDA_RING;
+    int h = 0;
+    if (hipMemcpy(&h, err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return KDA_ERR_HIP;
+    return h ? KDA_ERR_TIMEOUT : KDA_OK;
 }
 
 int kda_decode_step(const void *qkv, const void *a, const void *b, const float *A_log,

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.kda_status_str(code)
     assert lib.kda_status_str(0) == b"ok"
 
