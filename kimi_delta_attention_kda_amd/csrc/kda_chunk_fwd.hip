@@ -110,7 +110,25 @@ __device__ __forceinline__ void stores_done() {   // all of this wave's stores r
     __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
     asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
+// 16 bytes per lane from global memory straight into LDS (gfx950 LDS DMA): lane i
+// writes LDS bytes [lds + 16 i, lds + 16 i + 16).  `lds` must be wave-uniform.
+// The load is agent-coherent (sc1), so it reads L2 and never a stale L1 line.
+// Completion is counted by vmcnt; M0 is restored afterwards.
+__device__ __forceinline__ void lds_dma16(const void *src, unsigned lds) {
+    unsigned saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off sc1\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {       // at most N vector-memory ops of this wave in flight
+    static_assert(N >= 0 && N < 16, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
 __device__ __forceinline__ void sched_fence() {   // no instruction moves across this point
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -610,7 +628,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
 
     // LDS: producers use 4 scratch areas, consumers a 3-deep payload buffer.
     constexpr int PROD_BYTES = (int)sizeof(ProdScratch<BF16>) * NPW;
-    constexpr int CONS_BYTES = 3 * P::BYTES;
+    constexpr int CONS_BYTES = 3 * ((P::BYTES + 16 * NTHR - 1) / (16 * NTHR)) * 16 * NTHR;
     constexpr int LDS_BYTES = PROD_BYTES > CONS_BYTES ? PROD_BYTES : CONS_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
@@ -704,24 +722,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             if (n > SPIN_LIMIT) { st_flag(err, 1); known = q_total; return; }
         }
     };
-    constexpr int NFT = (P::BYTES + 16 * NTHR - 1) / (16 * NTHR);   // 16-byte pieces per thread
-    auto fetch = [&](int q, f32x4 (&t)[NFT]) {
-        const unsigned char *src = ring + (size_t)(q % KDA_RING) * KDA_RING_SLOT_BYTES;
+    // Payload q is copied by all NTHR threads, NFT 16-byte DMA pieces each,
+    // into LDS buffer q % 3 (a buffer holds PBUF bytes; the tail past the
+    // payload copies unused slot bytes).
+    constexpr int NFT = (P::BYTES + 16 * NTHR - 1) / (16 * NTHR);
+    constexpr int PBUF = NFT * 16 * NTHR;
+    static_assert(PBUF <= KDA_RING_SLOT_BYTES, "slot smaller than the DMA footprint");
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const unsigned lds0 = lds_addr(lds) + wu * 64 * 16;
+    auto dma = [&](int q) {
+        const unsigned char *src = ring + (size_t)(q % KDA_RING) * KDA_RING_SLOT_BYTES + tid * 16;
+        const unsigned dst = lds0 + (unsigned)(q % 3) * PBUF;
 #pragma unroll
-        for (int j = 0; j < NFT; ++j) {
-            const int off = (j * NTHR + tid) * 16;
-            if (off < P::BYTES) t[j] = *reinterpret_cast<const f32x4 *>(src + off);
-        }
+        for (int j = 0; j < NFT; ++j) lds_dma16(src + j * NTHR * 16, dst + j * NTHR * 16);
     };
-    auto deposit = [&](int q, const f32x4 (&t)[NFT]) {
-        unsigned char *dst = lds + (q % 3) * P::BYTES;
-#pragma unroll
-        for (int j = 0; j < NFT; ++j) {
-            const int off = (j * NTHR + tid) * 16;
-            if (off < P::BYTES) *reinterpret_cast<f32x4 *>(dst + off) = t[j];
-        }
-    };
-
     int chain = role.team, c = 0, nch = 0;
     ChainInfo ci{};
     f32x4 S[MT];
@@ -744,11 +758,28 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             if (args.h0 && computes) S[mt] = *reinterpret_cast<const f32x4 *>(args.h0 + hbase + 16 * mt + 4 * lq);
             else S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        vm_wait<0>();   // the state is never a pending load inside the chunk loop
     };
 
-    // One chunk q: payload q+2 is fetched into `tf` at the top, payload q+1
-    // (fetched one chunk earlier into `td`) goes to LDS buffer (q+1) % 3 at the end.
-    auto step = [&](int q, f32x4 (&tf)[NFT], const f32x4 (&td)[NFT]) {
+    // Output rows of the previous chunk, stored one step late so that the
+    // stores are older than the next DMA and never delay the payload wait.
+    f32x4 Op = {0.f, 0.f, 0.f, 0.f};
+    size_t op_base = 0;
+    int op_rem = 0;
+    const size_t o_row = (size_t)args.H * DV;
+    auto flush_o = [&]() {
+        if (computes) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * lq + i < op_rem) store_act<BF16>(args.o, op_base + (4 * lq + i) * o_row, Op[i]);
+        }
+        op_rem = 0;
+    };
+
+    // One chunk q, computed from LDS buffer q % 3.  Payload q+2 is requested
+    // at the top; payload q+1 (requested one step earlier) is waited for at
+    // the bottom, before the barrier that publishes it.
+    auto step = [&](int q) {
         // chain bookkeeping (zero-length chains: h_T = h0)
         while (!started || c >= nch) {
             if (started) { store_hT(); chain += args.n_teams; }
@@ -758,13 +789,12 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         }
         const size_t tok0 = ci.bos + (size_t)c * CH;
         const int rem = min(CH, ci.len - c * CH);
-        if (q + 2 < q_total) {
-            ensure_ready(q + 2);
-            l1_invalidate();
-            fetch(q + 2, tf);
-        }
+        const bool ahead = q + 2 < q_total;
+        if (ahead) ensure_ready(q + 2);
+        flush_o();
+        if (ahead) dma(q + 2);
         if (computes) {
-            const unsigned char *pl = lds + (q % 3) * P::BYTES;
+            const unsigned char *pl = lds + (q % 3) * PBUF;
             // R1: W = k~ S, Qs = q~ S ; then decay the state in place
             f32x4 W = {0.f, 0.f, 0.f, 0.f}, Qs = {0.f, 0.f, 0.f, 0.f};
             if constexpr (BF16) {
@@ -846,37 +876,33 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                     for (int i = 0; i < 4; ++i) S[mt] = mfma_f32(kr4[i], U[i], S[mt]);
                 }
             }
-            const int H = args.H, h = ci.head;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * lq + i;
-                if (r < rem) store_act<BF16>(args.o, ((tok0 + r) * H + h) * DV + v0 + ln, args.scale * O[i]);
-            }
+            for (int i = 0; i < 4; ++i) Op[i] = args.scale * O[i];
+            op_base = (tok0 * args.H + ci.head) * DV + v0 + ln;
+            op_rem = rem;
         }
-        if (q + 1 < q_total) deposit(q + 1, td);
+        if (ahead) vm_wait<NFT>();    // payload q+1 has landed (only q+2 may still fly)
+        else vm_wait<0>();
         lds_barrier();
         if (q + 1 < q_total && tid == 0) add_flag(&used[(q + 1) % KDA_RING], 1);
         ++c;
     };
 
-    f32x4 tA[NFT], tB[NFT];
     if (q_total > 0) {
         ensure_ready(0);
-        l1_invalidate();
-        fetch(0, tA);
-        deposit(0, tA);
+        dma(0);
         if (q_total > 1) {
             ensure_ready(1);
-            l1_invalidate();
-            fetch(1, tB);
+            dma(1);
+            vm_wait<NFT>();
+        } else {
+            vm_wait<0>();
         }
         lds_barrier();
         if (tid == 0) add_flag(&used[0], 1);
     }
-    for (int q = 0; q < q_total; q += 2) {
-        step(q, tA, tB);
-        if (q + 1 < q_total) step(q + 1, tB, tA);
-    }
+    for (int q = 0; q < q_total; ++q) step(q);
+    flush_o();
     // final state of the last open chain, then any trailing zero-length chains
     if (started) store_hT();
     for (chain = started ? chain + args.n_teams : role.team; chain < n_chains; chain += args.n_teams) {
