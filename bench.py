@@ -86,6 +86,60 @@ def measured_traffic(kernel):
     return t.get("bytes_per_launch")
 
 
+COPY_CALIB_ELEMS = 64 << 20     # float32 elements read and written by the calibration copy
+KERNEL_MATCH = {"chunk_fwd": "chunk_fwd_kernel", "decode": "decode_kernel"}
+
+
+def _counter_rows(d):
+    """(kernel name, counter name, value) from every rocprofv3 counter CSV under d."""
+    import csv
+    rows = []
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    for r in csv.DictReader(fh):
+                        rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def traffic_summary(fetch_dir, write_dir):
+    """HBM bytes per launch of each hot kernel from two rocprofv3 --pmc runs of
+    `bench.py --copy-calib` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+    Each counter is scaled by bytes / counter of the calibration copy (an
+    elementwise negate reading and writing COPY_CALIB_ELEMS float32), then the
+    per-kernel mean over dispatches is written to profiles/<kernel>_traffic.json
+    with the hash of the kernel's sources."""
+    import numpy as np
+    known = 4.0 * COPY_CALIB_ELEMS
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r[1] == counter]
+        if not rows:
+            raise SystemExit(f"no {counter} rows under {d}")
+        calib = [v for k, _, v in rows if "neg" in k.lower()]
+        if not calib:
+            raise SystemExit(f"no calibration copy dispatch in {d}")
+        scale = known / (1024.0 * float(np.median(calib)))
+        for kern, pat in KERNEL_MATCH.items():
+            vals = [v for k, _, v in rows if pat in k]
+            if vals:
+                out.setdefault(kern, {})[counter] = {"kib_per_dispatch": float(np.mean(vals)),
+                                                     "dispatches": len(vals), "scale": scale,
+                                                     "bytes": 1024.0 * float(np.mean(vals)) * scale}
+    for kern, c in out.items():
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        rec = {"kernel": kern, "source_hash": source_hash(KERNEL_SOURCES[kern]),
+               "bytes_per_launch": round(c["FETCH_SIZE"]["bytes"] + c["WRITE_SIZE"]["bytes"]),
+               "fetch_bytes": round(c["FETCH_SIZE"]["bytes"]), "write_bytes": round(c["WRITE_SIZE"]["bytes"]),
+               "counters": c, "calibration": f"torch.neg over {COPY_CALIB_ELEMS} float32 "
+                                              f"({int(known)} B read, {int(known)} B written)"}
+        with open(os.path.join(PROFILES, f"{kern}_traffic.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps({k: rec[k] for k in ("kernel", "bytes_per_launch", "fetch_bytes", "write_bytes")}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +147,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--prefill-workload", type=int, default=1, choices=[1, 2, 3])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run one calibration copy kernel of known size (for --pmc runs)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/<kernel>_traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (the path shards by head/sequence with "
               "no exchange; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
@@ -137,6 +198,13 @@ def main():
     def decode_call():
         kda.decode_step(**din, state_pool=pool, state_idx=sidx, num_heads=d.H,
                         num_v_heads=d.HV, scale=d.scale, o=od)
+
+    if args.copy_calib:
+        xc = torch.ones(COPY_CALIB_ELEMS, dtype=torch.float32, device=dev)
+        yc = torch.empty_like(xc)
+        torch.neg(xc, out=yc)
+        torch.cuda.synchronize()
+        del xc, yc
 
     for _ in range(args.warmup):
         prefill_call()
