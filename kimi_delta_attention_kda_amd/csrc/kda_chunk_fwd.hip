@@ -77,7 +77,6 @@ namespace kda {
 
 constexpr int CH = 16;              // chunk length (tokens)
 constexpr int NTHR = 256;           // threads per workgroup (4 waves), both roles
-constexpr int NPW = 4;              // producer waves per producer workgroup
 constexpr long SPIN_LIMIT = 1L << 20;   // polls (each an L2 round trip plus a short sleep): ~1 s
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
@@ -118,7 +117,7 @@ __device__ __forceinline__ void lds_dma16(const void *src, unsigned lds) {
     unsigned saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
                  "global_load_lds_dwordx4 %1, off sc1\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(src), "s"(lds) : "memory");
+                 : "=&s"(saved) : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {       // at most N vector-memory ops of this wave in flight
@@ -249,361 +248,203 @@ __device__ __forceinline__ ChainInfo chain_info(const ChunkArgs &a, int chain) {
 }
 
 // ============================================================== producer
-// A producer CREW of DK/64 waves (2 for d_k = 128) builds one chunk: each wave
-// owns 64 channels (one per lane) for all 16 tokens, writes its part of the
-// payload, and contracts its channels' share of L and Mqk.  The second wave
-// hands its partial 16x16 sums to the first (the "lead") through LDS; the lead
-// adds them, applies the masks and beta, forms INV and writes the rest.
-constexpr int CW = 64;   // channels per producer wave
+// A producer workgroup builds whole chunks with all four waves.  Lane
+// (wave w, lane 16 r + t) holds token t of the chunk and the 16-byte unit
+// u = 4 w + r of its k, q and g_raw rows, i.e. UC = 16 / element-size
+// channels [UC u, UC u + UC).  A DPP row (16 lanes) thus holds one channel
+// unit for all 16 tokens: the chunk-local cumulative gate is a 16-lane scan,
+// a lane's k~ / q~ values are exactly one 16-byte MFMA fragment of the payload
+// (the consumer's state tiles use the matching channel order, tile_chan()),
+// and a wave's registers are directly the A and B operands of its share of
+// the L / Mqk contractions (UC * 4 channels per wave).
 
+// Channel held by row 4 lq + i of the consumer's state tile mt (and by the
+// same rows of the k^r fragments and of e^{G_C}).  For bf16 the 8 K slots a
+// lane feeds to a 16x16x32 MFMA are then 8 contiguous channels.
 template <bool BF16>
-struct ProdScratch {   // per producer wave, in LDS
-    using E = typename Elem<BF16>::T;
-    static constexpr int PK = CW + (BF16 ? 8 : 4);
-    alignas(16) E R[CH][PK];     // k rows of the L / Mqk contraction
-    alignas(16) E Rq[CH][PK];    // q rows
-    alignas(16) E Cv[CH][PK];    // columns of the current pass
-    alignas(16) float X[CH][CH + 1];
-    alignas(16) float Pm[CH][CH + 1];
-    alignas(16) float beta[CH];
-    alignas(16) f32x4 partL[64];  // partial sums handed to the lead wave
-    alignas(16) f32x4 partM[64];
-    int flag;                     // sequence number of the posted partials
-    int ack;                      // sequence number the lead has consumed
+__device__ __forceinline__ int tile_chan(int mt, int lq, int i) {
+    if constexpr (BF16) return 32 * (mt >> 1) + 8 * lq + 4 * (mt & 1) + i;
+    else return 16 * mt + 4 * lq + i;
+}
+
+// Producer LDS: the chunk's v rows (read back transposed into the consumers'
+// C layout) and beta_raw, the k^r staging area, the per-wave partial 16x16
+// sums and beta.
+template <bool BF16, int DK, int DV>
+struct PG {
+    static constexpr int ES = BF16 ? 2 : 4;
+    static constexpr int UC = 16 / ES;              // elements per 16-byte unit
+    static constexpr int NU = DK / UC;              // k / q / g_raw units per token
+    static constexpr int NVU = DV / UC;             // v units per token
+    static constexpr int NWU = NU / 4;              // waves holding channel units
+    static constexpr int NVP = 16 * NVU / 64;       // v units per chunk / 64
+    static constexpr int NVL = (NVP + 3) / 4;       // v units per lane
+    static constexpr int IV = 0;                    // v: [token][unit]
+    static constexpr int IB = IV + 16 * NVU * 16;   // beta_raw: one float per token
+    static constexpr int KRS = IB + CH * 4;
+    static constexpr int PART = KRS + 16 * NU * 16;
+    static constexpr int SBETA = PART + NWU * 3 * 64 * 16;
+    static constexpr int BYTES = SBETA + CH * 4;
+    static_assert(NU % 4 == 0 && NU <= 16, "4..16 channel units");
+    static_assert(NVP >= 1 && (16 * NVU) % 64 == 0, "v units");
 };
 
-// One chunk's inputs for one producer wave: channel `lane` of its half
-// (k, q, g_raw) and its value columns, 16 tokens, kept as loaded.
-template <bool BF16, int DV, int NVW>
-struct ProdIn {
-    using Raw = typename std::conditional<BF16, uint32_t, float>::type;
-    Raw k[CH], q[CH], a[CH];
-    Raw v[CH][NVW];
-    float b;   // beta_raw of token `lane` for lanes < 16 (lead wave)
-    __device__ __forceinline__ static float get(Raw r) {
-        if constexpr (BF16) return bf16_to_f32((uint16_t)r);
-        else return r;
-    }
+// One chunk's inputs as one producer lane holds them: its k, q, g_raw units
+// (wave w < NWU), v units 64 m + lane for m = w, w + 4, ... (< NVP), and, in
+// wave 0, beta_raw of token `lane`.
+template <bool BF16, int DK, int DV>
+struct PIn {
+    uint4 k, q, a;
+    uint4 v[PG<BF16, DK, DV>::NVL];
+    float b;
 };
 
+// DPP: x of the lane n below in the same 16-lane row (0 past the row start),
+// and lane n of the row broadcast to the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
+                                                                 false));
+}
+__device__ __forceinline__ float scan16(float x) {   // inclusive prefix sum over the row's 16 tokens
+    x += dpp_f<0x111>(x);
+    x += dpp_f<0x112>(x);
+    x += dpp_f<0x114>(x);
+    x += dpp_f<0x118>(x);
+    return x;
+}
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) { return dpp_f<0x150 + N>(x); }
+
+// A team's chunk sequence (its chains one after the other, in chain order).
+struct Cursor {
+    int chain, q_base, nch;
+    ChainInfo ci;
+};
+__device__ __forceinline__ void cursor_seek(Cursor &c, int q, const ChunkArgs &a, int n_teams) {
+    while (q >= c.q_base + c.nch) {
+        c.q_base += c.nch;
+        c.chain += n_teams;
+        c.ci = chain_info(a, c.chain);
+        c.nch = (c.ci.len + CH - 1) / CH;
+    }
+}
+
+// Issue the loads of team chunk q's inputs into `in`.  Rows past the chunk's
+// live tokens repeat the last live row (always in bounds); their values are
+// masked where used.  The loads sit in no lane-divergent branch, so nothing
+// waits for them before their use one chunk later.
+template <bool BF16, int DK, int DV>
+__device__ __forceinline__ void prod_load(PIn<BF16, DK, DV> &in, const Cursor &c, int q, const ChunkArgs &a,
+                                          int w, int lane) {
+    using G = PG<BF16, DK, DV>;
+    const int cc = q - c.q_base;
+    const size_t tok0 = c.ci.bos + (size_t)cc * CH;
+    const int last = min(CH, c.ci.len - cc * CH) - 1;
+    const size_t H = a.H, h = c.ci.head;
+    if (w < G::NWU) {
+        const int t = lane & 15, u = 4 * w + (lane >> 4);
+        const size_t off = (((tok0 + min(t, last)) * H + h) * DK) * G::ES + u * 16;
+        in.k = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.k) + off);
+        in.q = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.q) + off);
+        in.a = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.g_raw) + off);
+    }
+#pragma unroll
+    for (int j = 0; j < G::NVL; ++j) {
+        const int m = w + 4 * j;
+        if (m < G::NVP) {
+            const int p = 64 * m + lane, tv = p / G::NVU, vu = p - tv * G::NVU;
+            const size_t off = (((tok0 + min(tv, last)) * H + h) * DV) * G::ES + vu * 16;
+            in.v[j] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v) + off);
+        }
+    }
+    if (w == 0) in.b = load_act<BF16>(a.beta_raw, (tok0 + min(lane, last)) * H + h);
+}
+
+// hi/lo bf16 parts of 8 values (two groups of 4).
+struct HL8 {
+    bf16x4 hi0, lo0, hi1, lo1;
+};
+__device__ __forceinline__ HL8 split8(const float (&x)[8]) {
+    HL8 s;
+    hilo4(f32x4{x[0], x[1], x[2], x[3]}, s.hi0, s.lo0);
+    hilo4(f32x4{x[4], x[5], x[6], x[7]}, s.hi1, s.lo1);
+    return s;
+}
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+    return r;
+}
+// acc += X Y^T over the 8 channels of each lane's unit (rows: the tokens of
+// the A-role lanes, columns: the tokens of the B-role lanes), to ~2^-16
+// relative: (Xhi + Xlo) Yhi + Xhi Ylo.
+__device__ __forceinline__ f32x4 contract8(const HL8 &X, const HL8 &Y, f32x4 acc) {
+    acc = mfma_bf16(cat4(X.hi0, X.lo0), cat4(Y.hi0, Y.hi0), acc);
+    acc = mfma_bf16(cat4(X.hi1, X.lo1), cat4(Y.hi1, Y.hi1), acc);
+    acc = mfma_bf16(cat4(X.hi0, X.hi1), cat4(Y.lo0, Y.lo1), acc);
+    return acc;
+}
+__device__ __forceinline__ f32x4 contract4(const float (&X)[4], const float (&Y)[4], f32x4 acc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = mfma_f32(X[i], Y[i], acc);
+    return acc;
+}
+
+// 16x16x16 product in C layout without any data movement: given XT = C layout
+// of X^T (lane (lq, ln) element i = X[ln][4lq+i], which is the A operand's
+// element) and Y in C layout (the B operand's element), return X Y in C layout.
 template <bool BF16>
-__device__ __forceinline__ typename std::conditional<BF16, uint32_t, float>::type
-ld_one(const void *p, size_t off) {
-    if constexpr (BF16) return static_cast<const uint16_t *>(p)[off];
-    else return static_cast<const float *>(p)[off];
-}
-
-// Loads of one chunk: part 0 = k, g_raw (needed first), part 1 = q, v, beta_raw.
-template <int PART, bool BF16, int DK, int DV, int NVW>
-__device__ __forceinline__ void prod_load(ProdIn<BF16, DV, NVW> &in, const ChunkArgs &a, size_t tok0,
-                                          int rem, int h, int c, int vbase, int nvcol, int lane, bool lead) {
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-        const size_t row = (tok0 + t) * a.H + h;
-        const bool live = t < rem;
-        if constexpr (PART == 0) {
-            in.k[t] = live ? ld_one<BF16>(a.k, row * DK + c) : 0;
-            in.a[t] = live ? ld_one<BF16>(a.g_raw, row * DK + c) : 0;
-        } else {
-            in.q[t] = live ? ld_one<BF16>(a.q, row * DK + c) : 0;
-#pragma unroll
-            for (int j = 0; j < NVW; ++j) {
-                const int vc = lane + 64 * j;
-                in.v[t][j] = (live && vc < nvcol) ? ld_one<BF16>(a.v, row * DV + vbase + vc) : 0;
-            }
-        }
-    }
-    if constexpr (PART == 1)
-        in.b = (lead && lane < rem) ? load_act<BF16>(a.beta_raw, (tok0 + lane) * a.H + h) : 0.f;
-}
-
-// C (16x16, C layout) += A B with A rows from LDS matrix Am (row-major, stride
-// CH+1) and B in C layout (registers); hi/lo bf16 splits on both sides
-// (error ~2^-16 relative).
-__device__ __forceinline__ f32x4 mm16_lds_reg(const float (*Am)[CH + 1], f32x4 B, f32x4 acc,
-                                              int ln, int lq) {
-    f32x4 a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = Am[ln][4 * lq + i];
-    bf16x4 ahi, alo;
-    hilo4(a, ahi, alo);
-    const bf16x8 b = split_hilo(B);
-    acc = mfma_bf16(dup4(ahi), b, acc);
-    acc = mfma_bf16(dup4(alo), b, acc);
-    return acc;
-}
-__device__ __forceinline__ void st_rows(float (*Dm)[CH + 1], f32x4 c, int ln, int lq) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Dm[4 * lq + i][ln] = c[i];
-}
-// fp32 path: D += A B with both operands from LDS, 4 fp32 MFMAs.
-__device__ __forceinline__ f32x4 mm16_f32(const float (*A)[CH + 1], const float (*B)[CH + 1],
-                                          f32x4 acc, int ln, int lq) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_f32(A[ln][4 * s + lq], B[4 * s + lq][ln], acc);
-    return acc;
-}
-
-// acc += rows(A) x cols(B)^T over the wave's 64 channels, both from LDS
-// [token][channel]; columns with token index > cmax read as zero.
-template <bool BF16, typename E, int PK>
-__device__ __forceinline__ f32x4 contract64(const E (*A)[PK], const E (*B)[PK], int cmax,
-                                            f32x4 acc, int ln, int lq) {
-    const bool live = ln <= cmax;
+__device__ __forceinline__ f32x4 prod16(f32x4 XT, f32x4 Y) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     if constexpr (BF16) {
-#pragma unroll
-        for (int s = 0; s < CW / 32; ++s) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&A[ln][32 * s + 8 * lq]);
-            bf16x8 bv = *reinterpret_cast<const bf16x8 *>(&B[ln][32 * s + 8 * lq]);
-            if (!live) bv = bf16x8{};
-            acc = mfma_bf16(av, bv, acc);
-        }
+        bf16x4 xh, xl, yh, yl;
+        hilo4(XT, xh, xl);
+        hilo4(Y, yh, yl);
+        const bf16x4 zero = {};
+        f32x4 acc = mfma_bf16(cat4(xh, xl), cat4(yh, yh), z);
+        return mfma_bf16(cat4(xh, xh), cat4(yl, zero), acc);
     } else {
+        f32x4 acc = z;
 #pragma unroll
-        for (int s = 0; s < CW / 4; ++s) {
-            const float bv = live ? B[ln][4 * s + lq] : 0.f;
-            acc = mfma_f32(A[ln][4 * s + lq], bv, acc);
-        }
+        for (int i = 0; i < 4; ++i) acc = mfma_f32(XT[i], Y[i], acc);
+        return acc;
     }
-    return acc;
+}
+__device__ __forceinline__ f32x4 plus_eye(f32x4 X, int ln, int lq) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) X[i] += (4 * lq + i == ln) ? 1.f : 0.f;
+    return X;
 }
 
-__device__ __forceinline__ bool lds_wait_geq(const int *p, int v, int *err) {
-    for (long n = 0; *reinterpret_cast<const volatile int *>(p) < v; ++n) {
-        __builtin_amdgcn_s_sleep(1);
-        if (n > SPIN_LIMIT) { st_flag(err, 1); return false; }
+template <bool BF16>
+__device__ __forceinline__ void unpack16(uint4 v, float (&x)[16 / (BF16 ? 2 : 4)]) {
+    if constexpr (BF16) {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __builtin_bit_cast(float, wv[j] << 16);
+            x[2 * j + 1] = __builtin_bit_cast(float, wv[j] & 0xffff0000u);
+        }
+    } else {
+        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __builtin_bit_cast(float, wv[j]);
     }
-    asm volatile("" ::: "memory");
-    return true;
 }
-
-// Produce this wave's half of one chunk's payload into ring slot `slot`.
-// `c` = this lane's channel; `hf` = half (0 = lead); `seq` = chunk number + 1.
-template <bool BF16, int DK, int DV, int NVW>
-__device__ void produce_half(const ProdIn<BF16, DV, NVW> &in, int rem, float A_exp, float dtl,
-                             ProdScratch<BF16> &me, ProdScratch<BF16> &mate, unsigned char *slot,
-                             int lane, int hf, int vbase, int nvcol, int seq, int &posted, int *err) {
-    constexpr int NPAIR = DK / 64;
-    using P = PL<BF16, DK, DV>;
-    using In = ProdIn<BF16, DV, NVW>;
-    const int ln = lane & 15, lq = lane >> 4;
-    const int c = CW * hf + lane;
-
-    // ---- v, re-laid out as the consumers' C-layout fragments
-#pragma unroll
-    for (int j = 0; j < NVW; ++j) {
-        const int vc = vbase + lane + 64 * j;
-        if (lane + 64 * j < nvcol) {
-            const int vt = vc >> 4, vl = vc & 15;
-#pragma unroll
-            for (int fq = 0; fq < 4; ++fq) {
-                if constexpr (BF16) {
-                    uint2 w;
-                    w.x = (in.v[4 * fq][j] & 0xffffu) | (in.v[4 * fq + 1][j] << 16);
-                    w.y = (in.v[4 * fq + 2][j] & 0xffffu) | (in.v[4 * fq + 3][j] << 16);
-                    *reinterpret_cast<uint2 *>(slot + P::V + ((vt * 64 + fq * 16 + vl) * 4) * 2) = w;
-                } else {
-                    const f32x4 w = {in.v[4 * fq][j], in.v[4 * fq + 1][j], in.v[4 * fq + 2][j], in.v[4 * fq + 3][j]};
-                    *reinterpret_cast<f32x4 *>(slot + P::V + ((vt * 64 + fq * 16 + vl) * 4) * 4) = w;
-                }
-            }
-        }
-    }
-
-    // ---- gate: e^{g} = 2^{-A log2(1 + 2^{x log2e})}; padded tokens do not decay
-    float al[CH];
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-        const float y = __builtin_fmaf(In::get(in.a[t]), kLog2e, dtl);
-        const float sp2 = y > 20.0f * kLog2e ? y : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(y));
-        al[t] = t < rem ? __builtin_amdgcn_exp2f(-A_exp * sp2) : 1.f;
-    }
-    if (hf == 0 && lane < CH) me.beta[lane] = lane < rem ? sigmoid_f(in.b) : 0.f;
-
-    // ---- k~, q~ (prefix products), e^{G_C}, k^r (suffix products)
-    float p = 1.f;
-#pragma unroll
-    for (int t = 0; t < CH; ++t) {
-        p *= al[t];
-        const float kd = In::get(in.k[t]) * p, qd = In::get(in.q[t]) * p;
-        if constexpr (BF16) {
-            const int off = (((c >> 5) * 4 + ((c >> 2) & 3)) * 16 + t) * 16 + (4 * ((c >> 4) & 1) + (c & 3)) * 2;
-            *reinterpret_cast<uint16_t *>(slot + P::KD + off) = f32_to_bf16(kd);
-            *reinterpret_cast<uint16_t *>(slot + P::QD + off) = f32_to_bf16(qd);
-        } else {
-            const int off = (((c >> 4) * 4 + ((c >> 2) & 3)) * 16 + t) * 16 + (c & 3) * 4;
-            *reinterpret_cast<float *>(slot + P::KD + off) = kd;
-            *reinterpret_cast<float *>(slot + P::QD + off) = qd;
-        }
-    }
-    const float Pc = p;
-    reinterpret_cast<float *>(slot + P::EG)[c] = Pc;
-    float kr[CH];
-    {
-        float sq = 1.f;
-#pragma unroll
-        for (int t = CH - 1; t >= 0; --t) {
-            kr[t] = In::get(in.k[t]) * sq;
-            sq *= al[t];
-        }
-    }
-    {
-        const int mt = c >> 4, cl = c & 15;
-#pragma unroll
-        for (int fq = 0; fq < 4; ++fq) {
-            if constexpr (BF16) {
-                uint2 v;
-                v.x = pack_bf16x2(kr[4 * fq], kr[4 * fq + 1]);
-                v.y = pack_bf16x2(kr[4 * fq + 2], kr[4 * fq + 3]);
-                *reinterpret_cast<uint2 *>(slot + P::KR + ((mt * 4 + fq) * 16 + cl) * 8) = v;
-            } else {
-                const f32x4 v = {kr[4 * fq], kr[4 * fq + 1], kr[4 * fq + 2], kr[4 * fq + 3]};
-                *reinterpret_cast<f32x4 *>(slot + P::KR + ((mt * 4 + fq) * 16 + cl) * 16) = v;
-            }
-        }
-    }
-
-    // ---- this wave's share of L and Mqk (each wave picks its own scheme)
-    const bool mild = __all(Pc >= 0x1p-100f);
-    f32x4 accL = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
-    if (mild) {
-        // one reference at the chunk end: rows k 2^{g_C - g}, q 2^{g_C - g}; columns k^r
-        float pr = __builtin_amdgcn_rcpf(Pc);
-#pragma unroll
-        for (int t = 0; t < CH; ++t) {
-            pr *= al[t];
-            me.R[t][lane] = to_elem<BF16>(In::get(in.k[t]) * pr);
-            me.Rq[t][lane] = to_elem<BF16>(In::get(in.q[t]) * pr);
-            me.Cv[t][lane] = to_elem<BF16>(kr[t]);
-        }
-        lds_done();
-        accL = contract64<BF16>(me.R, me.Cv, CH - 1, accL, ln, lq);
-        accM = contract64<BF16>(me.Rq, me.Cv, CH - 1, accM, ln, lq);
-    } else {
-        // four token blocks, decay clipped at 2^-24 per token; rows relative to
-        // the start of their own block
-        float ac[CH];
-#pragma unroll
-        for (int t = 0; t < CH; ++t) ac[t] = fmaxf(al[t], 0x1p-24f);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            float lp = 1.f;
-#pragma unroll
-            for (int t = 4 * b; t < 4 * b + 4; ++t) {
-                lp *= ac[t];
-                me.R[t][lane] = to_elem<BF16>(In::get(in.k[t]) * lp);
-                me.Rq[t][lane] = to_elem<BF16>(In::get(in.q[t]) * lp);
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            // columns for row block b: own block k 2^{g'_t - g'_ref}; earlier
-            // tokens k 2^{g'_t - g'_ref} <= 1 (products of the clipped decays after t)
-            float lp = 1.f;
-#pragma unroll
-            for (int t = 4 * b; t < 4 * b + 4; ++t) {
-                lp *= ac[t];
-                me.Cv[t][lane] = to_elem<BF16>(In::get(in.k[t]) * __builtin_amdgcn_rcpf(lp));
-            }
-            float F = 1.f;
-#pragma unroll
-            for (int t = 4 * b - 1; t >= 0; --t) {
-                me.Cv[t][lane] = to_elem<BF16>(In::get(in.k[t]) * F);
-                F *= ac[t];
-            }
-            lds_done();
-            const f32x4 pl = contract64<BF16>(me.R, me.Cv, 4 * b + 3, f32x4{0.f, 0.f, 0.f, 0.f}, ln, lq);
-            const f32x4 pm = contract64<BF16>(me.Rq, me.Cv, 4 * b + 3, f32x4{0.f, 0.f, 0.f, 0.f}, ln, lq);
-            if (lq == b) { accL = pl; accM = pm; }
-            lds_done();   // every lane has read Cv before the next variant overwrites it
-        }
-    }
-
-    // ---- combine the crew's partial sums in the lead wave
-    if constexpr (NPAIR == 2) {
-        if (hf == 1) {
-            stores_done();                       // this wave's payload is in L2
-            lds_wait_geq(&me.ack, posted, err);  // lead consumed the previous partials
-            me.partL[lane] = accL;
-            me.partM[lane] = accM;
-            lds_done();
-            *reinterpret_cast<volatile int *>(&me.flag) = seq;
-            posted = seq;
-            return;
-        }
-        lds_wait_geq(&mate.flag, seq, err);
-        lds_done();
-        const f32x4 oL = mate.partL[lane], oM = mate.partM[lane];
-        lds_done();
-        *reinterpret_cast<volatile int *>(&mate.ack) = seq;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { accL[i] += oL[i]; accM[i] += oM[i]; }
-    }
-    lds_done();
-    f32x4 L, M;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 4 * lq + i;
-        L[i] = r > ln ? -me.beta[r] * accL[i] : 0.f;
-        M[i] = r >= ln ? accM[i] : 0.f;
-    }
-
-    // ---- INV = (I + L)(I + L^2)(I + L^4)(I + L^8)
-    f32x4 X;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) X[i] = (4 * lq + i == ln ? 1.f : 0.f) + L[i];
+template <bool BF16>
+__device__ __forceinline__ void pack16(void *p, const float (&x)[16 / (BF16 ? 2 : 4)]) {
     if constexpr (BF16) {
-        f32x4 Pw = L;
-        st_rows(me.Pm, Pw, ln, lq);
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            lds_done();
-            const f32x4 P2 = mm16_lds_reg(me.Pm, Pw, f32x4{0.f, 0.f, 0.f, 0.f}, ln, lq);
-            st_rows(me.X, X, ln, lq);
-            lds_done();
-            X = mm16_lds_reg(me.X, P2, X, ln, lq);
-            Pw = P2;
-            st_rows(me.Pm, Pw, ln, lq);
-        }
+        uint4 v;
+        v.x = pack_bf16x2(x[0], x[1]);
+        v.y = pack_bf16x2(x[2], x[3]);
+        v.z = pack_bf16x2(x[4], x[5]);
+        v.w = pack_bf16x2(x[6], x[7]);
+        *reinterpret_cast<uint4 *>(p) = v;
     } else {
-        st_rows(me.Pm, L, ln, lq);
-        st_rows(me.X, X, ln, lq);
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            lds_done();
-            const f32x4 P2 = mm16_f32(me.Pm, me.Pm, f32x4{0.f, 0.f, 0.f, 0.f}, ln, lq);
-            lds_done();
-            st_rows(me.Pm, P2, ln, lq);
-            lds_done();
-            X = mm16_f32(me.X, me.Pm, X, ln, lq);
-            lds_done();
-            st_rows(me.X, X, ln, lq);
-        }
+        *reinterpret_cast<f32x4 *>(p) = f32x4{x[0], x[1], x[2], x[3]};
     }
-    // ---- INV and Mqk as A fragments (row ln, columns 4lq .. 4lq+3)
-    lds_done();
-    st_rows(me.X, X, ln, lq);
-    st_rows(me.Pm, M, ln, lq);
-    lds_done();
-    f32x4 xi, mi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { xi[i] = me.X[ln][4 * lq + i]; mi[i] = me.Pm[ln][4 * lq + i]; }
-    if constexpr (BF16) {
-        bf16x4 h, l;
-        hilo4(xi, h, l);
-        bf16x8 v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { v[i] = h[i]; v[4 + i] = l[i]; }
-        *reinterpret_cast<bf16x8 *>(slot + P::INV + lane * 16) = v;
-        hilo4(mi, h, l);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { v[i] = h[i]; v[4 + i] = l[i]; }
-        *reinterpret_cast<bf16x8 *>(slot + P::MQK + lane * 16) = v;
-    } else {
-        *reinterpret_cast<f32x4 *>(slot + P::INV + lane * 16) = xi;
-        *reinterpret_cast<f32x4 *>(slot + P::MQK + lane * 16) = mi;
-    }
-    if (lane < CH) reinterpret_cast<float *>(slot + P::BETA)[lane] = me.beta[lane];
 }
 
 // ============================================================== the kernel
@@ -621,13 +462,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     constexpr int NCW = BDV / 16;          // compute waves of a consumer workgroup
     constexpr int MT = DK / 16;
     constexpr int NP = KDA_PRODUCER_WGS;
-    constexpr int NPAIR = DK / CW;         // waves per producer crew
-    constexpr int NVW = (DV / NPAIR + 63) / 64;   // value columns per producer lane
     static_assert(NCW >= 1 && NCW <= 4, "consumer slab of 16..64 columns");
     static_assert(KDA_RING <= 64, "one lane per ring slot when polling");
 
-    // LDS: producers use 4 scratch areas, consumers a 3-deep payload buffer.
-    constexpr int PROD_BYTES = (int)sizeof(ProdScratch<BF16>) * NPW;
+    // LDS: producers use their input buffers and scratch, consumers a 3-deep payload buffer.
+    constexpr int PROD_BYTES = PG<BF16, DK, DV>::BYTES;
     constexpr int CONS_BYTES = 3 * ((P::BYTES + 16 * NTHR - 1) / (16 * NTHR)) * 16 * NTHR;
     constexpr int LDS_BYTES = PROD_BYTES > CONS_BYTES ? PROD_BYTES : CONS_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
@@ -644,54 +483,248 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
 
     if (role.member >= NS) {
         // ======================================================= producer
-        auto *scr = reinterpret_cast<ProdScratch<BF16> *>(lds);
-        if (lane == 0) { scr[w].flag = 0; scr[w].ack = 0; }
-        __syncthreads();
-        const int hf = w % NPAIR;                                  // half of the crew
-        const int crew = (role.member - NS) * (NPW / NPAIR) + w / NPAIR;
-        constexpr int STEP = NP * (NPW / NPAIR);                   // crews per team
-        ProdScratch<BF16> &me = scr[w];
-        ProdScratch<BF16> &mate = scr[w ^ (NPAIR - 1)];
-        const int c = CW * hf + lane;
-        const int nvcol = DV / NPAIR, vbase = nvcol * hf;
-        int q_base = 0, posted = 0;
-        ProdIn<BF16, DV, NVW> cur;
-        for (int chain = role.team; chain < n_chains; chain += args.n_teams) {
-            const ChainInfo ci = chain_info(args, chain);
-            const int nch = (ci.len + CH - 1) / CH;
-            const float A_exp = expf(args.A_log[ci.head]);
-            const float dtl = args.dt_bias[(size_t)ci.head * DK + c] * kLog2e;
-            int q = q_base + ((crew - q_base) % STEP + STEP) % STEP;
-            if (q < q_base + nch) {
-                const int cc = q - q_base;
-                prod_load<0, BF16, DK, DV, NVW>(cur, args, ci.bos + (size_t)cc * CH, min(CH, ci.len - cc * CH),
-                                                ci.head, c, vbase, nvcol, lane, hf == 0);
-            }
-            for (; q < q_base + nch; q += STEP) {
-                const int cc = q - q_base;
-                const int rem = min(CH, ci.len - cc * CH);
-                // this chunk's q, v, beta_raw, then the next chunk's k, g_raw:
-                // both overlap the slot wait and this chunk's gate
-                prod_load<1, BF16, DK, DV, NVW>(cur, args, ci.bos + (size_t)cc * CH, rem, ci.head, c, vbase,
-                                                nvcol, lane, hf == 0);
-                ProdIn<BF16, DV, NVW> nxt;
-                const int cn = cc + STEP;
-                if (cn < nch)
-                    prod_load<0, BF16, DK, DV, NVW>(nxt, args, ci.bos + (size_t)cn * CH, min(CH, ci.len - cn * CH),
-                                                    ci.head, c, vbase, nvcol, lane, hf == 0);
-                const int s = q % KDA_RING;
-                if (q >= KDA_RING) wait_geq(&used[s], NS * (q / KDA_RING), err);
-                produce_half<BF16, DK, DV, NVW>(cur, rem, A_exp, dtl, me, mate,
-                                                ring + (size_t)s * KDA_RING_SLOT_BYTES, lane, hf, vbase, nvcol,
-                                                q + 1, posted, err);
-                if (hf == 0) {
-                    stores_done();   // lead's stores; the other half drained before posting
-                    if (lane == 0) st_flag(&ready[s], q + 1);
-                }
+        using G = PG<BF16, DK, DV>;
+        constexpr int UC = G::UC;
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        const int p = role.member - NS;                 // chunks p, p + NP, p + 2 NP, ... of the team
+        const int t = ln, r = lq, u = 4 * wu + r;       // token, channel unit
+        const bool has_unit = wu < G::NWU;
+        float *sbeta = reinterpret_cast<float *>(lds + G::SBETA);
+        int q_total = 0;
+        for (int chain = role.team; chain < n_chains; chain += args.n_teams)
+            q_total += (chain_info(args, chain).len + CH - 1) / CH;
+        if (p >= q_total) return;
+        Cursor cp;
+        cp.chain = role.team;
+        cp.q_base = 0;
+        cp.ci = chain_info(args, cp.chain);
+        cp.nch = (cp.ci.len + CH - 1) / CH;
+        Cursor cd = cp;                                 // the chunk being loaded, one step ahead
+        PIn<BF16, DK, DV> cur, nxt;
+        prod_load<BF16, DK, DV>(cur, cp, p, args, wu, lane);
+        int cur_chain = -1;
+        float A_exp = 0.f, dtl[UC];
+        for (int it = 0;; ++it) {
+            const int q = p + it * NP;
+            if (q >= q_total) break;
+            cursor_seek(cp, q, args, args.n_teams);
+            const int rem = min(CH, cp.ci.len - (q - cp.q_base) * CH);
+            if (cp.chain != cur_chain) {
+                cur_chain = cp.chain;
+                A_exp = expf(args.A_log[cp.ci.head]);
 #pragma unroll
-                for (int t = 0; t < CH; ++t) { cur.k[t] = nxt.k[t]; cur.a[t] = nxt.a[t]; }
+                for (int c = 0; c < UC; ++c)
+                    dtl[c] = has_unit ? args.dt_bias[(size_t)cp.ci.head * DK + UC * u + c] * kLog2e : 0.f;
             }
-            q_base += nch;
+            const int s = q % KDA_RING;
+            unsigned char *slot = ring + (size_t)s * KDA_RING_SLOT_BYTES;
+            // slot free?  (polled before this step's loads are issued, so the poll's
+            // wait covers nothing else; spinning on scalar loads instead would
+            // starve the instruction fetch of neighbouring compute units)
+            if (q >= KDA_RING) wait_geq(&used[s], NS * (q / KDA_RING), err);
+            // the producer's next chunk loads while this one is built (the loads
+            // have had a whole step when the stores below are drained)
+            const int qn = q + NP;
+            if (qn < q_total) {
+                cursor_seek(cd, qn, args, args.n_teams);
+                prod_load<BF16, DK, DV>(nxt, cd, qn, args, wu, lane);
+            }
+            // v rows and beta_raw go to LDS for the transposing readers
+#pragma unroll
+            for (int j = 0; j < G::NVL; ++j) {
+                const int m = wu + 4 * j;
+                if (m < G::NVP) *reinterpret_cast<uint4 *>(lds + G::IV + (64 * m + lane) * 16) = cur.v[j];
+            }
+
+            if (has_unit) {
+                // ---- gate and its chunk-local cumulative sum (log2 units), per channel
+                float kf[UC], qf[UC], af[UC], gv[UC], Gm[UC], GC[UC];
+                unpack16<BF16>(cur.k, kf);
+                unpack16<BF16>(cur.q, qf);
+                unpack16<BF16>(cur.a, af);
+                const bool live = t < rem;
+                bool deep = false;
+#pragma unroll
+                for (int c = 0; c < UC; ++c) {
+                    kf[c] = live ? kf[c] : 0.f;
+                    qf[c] = live ? qf[c] : 0.f;
+                    const float y = __builtin_fmaf(af[c], kLog2e, dtl[c]);
+                    const float sp2 = y > 20.0f * kLog2e ? y : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(y));
+                    gv[c] = live ? -A_exp * sp2 : 0.f;    // padded tokens do not decay
+                    Gm[c] = scan16(gv[c]);
+                    GC[c] = row_bcast<15>(Gm[c]);
+                    deep |= GC[c] < -100.f;
+                }
+                // ---- k~ = k 2^G, q~ = q 2^G (payload fragments), k^r = k 2^{G_C - G}, e^{G_C}
+                float kd[UC], qd[UC], kr[UC], e1[UC];
+#pragma unroll
+                for (int c = 0; c < UC; ++c) {
+                    e1[c] = __builtin_amdgcn_exp2f(Gm[c]);
+                    kd[c] = kf[c] * e1[c];
+                    qd[c] = qf[c] * e1[c];
+                    kr[c] = kf[c] * __builtin_amdgcn_exp2f(GC[c] - Gm[c]);
+                }
+                pack16<BF16>(slot + P::KD + tid * 16, kd);
+                pack16<BF16>(slot + P::QD + tid * 16, qd);
+                pack16<BF16>(lds + G::KRS + tid * 16, kr);
+                if (t == CH - 1) {
+                    float *eg = reinterpret_cast<float *>(slot + P::EG);
+                    if constexpr (BF16) {
+                        *reinterpret_cast<f32x4 *>(eg + 16 * (2 * wu) + 4 * r) = f32x4{e1[0], e1[1], e1[2], e1[3]};
+                        *reinterpret_cast<f32x4 *>(eg + 16 * (2 * wu + 1) + 4 * r) = f32x4{e1[4], e1[5], e1[6], e1[7]};
+                    } else {
+                        *reinterpret_cast<f32x4 *>(eg + 16 * wu + 4 * r) = f32x4{e1[0], e1[1], e1[2], e1[3]};
+                    }
+                }
+                // ---- this wave's share of L (rows i), L^T and Mqk^T over its UC*4 channels
+                f32x4 pL = {0.f, 0.f, 0.f, 0.f}, pLT = pL, pMT = pL;
+                if (__ballot(deep) == 0) {
+                    // mild: one reference at the chunk end, rows k 2^{G - G_C} (<= 2^100), columns k^r (<= 1)
+                    float R[UC], Rq[UC];
+#pragma unroll
+                    for (int c = 0; c < UC; ++c) {
+                        const float f = __builtin_amdgcn_exp2f(Gm[c] - GC[c]);
+                        R[c] = kf[c] * f;
+                        Rq[c] = qf[c] * f;
+                    }
+                    if constexpr (BF16) {
+                        const HL8 hR = split8(R), hRq = split8(Rq), hC = split8(kr);
+                        pL = contract8(hR, hC, pL);
+                        pLT = contract8(hC, hR, pLT);
+                        pMT = contract8(hC, hRq, pMT);
+                    } else {
+                        pL = contract4(R, kr, pL);
+                        pLT = contract4(kr, R, pLT);
+                        pMT = contract4(kr, Rq, pMT);
+                    }
+                } else {
+                    // strong: 4-token row blocks; per-token decay clipped at 2^-24; block b's
+                    // reference is the clipped cumulative decay at the end of block b-1
+                    float Gp[UC], B1[UC], B2[UC], B3[UC], R[UC], Rq[UC];
+#pragma unroll
+                    for (int c = 0; c < UC; ++c) {
+                        Gp[c] = scan16(fmaxf(gv[c], -24.0f));
+                        B1[c] = row_bcast<3>(Gp[c]);
+                        B2[c] = row_bcast<7>(Gp[c]);
+                        B3[c] = row_bcast<11>(Gp[c]);
+                        const float ref = t < 4 ? 0.f : t < 8 ? B1[c] : t < 12 ? B2[c] : B3[c];
+                        const float f = __builtin_amdgcn_exp2f(Gp[c] - ref);     // <= 1
+                        R[c] = kf[c] * f;
+                        Rq[c] = qf[c] * f;
+                    }
+                    [[maybe_unused]] HL8 hR, hRq;
+                    if constexpr (BF16) { hR = split8(R); hRq = split8(Rq); }
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        float C[UC];
+#pragma unroll
+                        for (int c = 0; c < UC; ++c) {
+                            const float ref = b == 0 ? 0.f : b == 1 ? B1[c] : b == 2 ? B2[c] : B3[c];
+                            C[c] = t < 4 * b + 4 ? kf[c] * __builtin_amdgcn_exp2f(ref - Gp[c]) : 0.f;   // <= 2^96
+                        }
+                        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                        f32x4 Lb, LTb, MTb;
+                        if constexpr (BF16) {
+                            const HL8 hC = split8(C);
+                            Lb = contract8(hR, hC, z);
+                            LTb = contract8(hC, hR, z);
+                            MTb = contract8(hC, hRq, z);
+                        } else {
+                            Lb = contract4(R, C, z);
+                            LTb = contract4(C, R, z);
+                            MTb = contract4(C, Rq, z);
+                        }
+                        // keep the rows (of L) that lie in block b
+                        if (r == b) pL = Lb;
+                        if ((t >> 2) == b) { pLT = LTb; pMT = MTb; }
+                    }
+                }
+                f32x4 *pp = reinterpret_cast<f32x4 *>(lds + G::PART) + (wu * 3) * 64 + lane;
+                pp[0] = pL;
+                pp[64] = pLT;
+                pp[128] = pMT;
+            }
+            if (wu == 0 && lane < CH) sbeta[lane] = lane < rem ? sigmoid_f(cur.b) : 0.f;
+            lds_barrier();
+
+            if (wu == 0) {
+                // ---- L, L^T (C layout), masks and beta; INV by Neumann squaring in transposed pairs
+                f32x4 L = {0.f, 0.f, 0.f, 0.f}, LT = L, MQ = L;
+                const f32x4 *pp = reinterpret_cast<const f32x4 *>(lds + G::PART) + lane;
+#pragma unroll
+                for (int ww = 0; ww < G::NWU; ++ww) {
+                    L += pp[ww * 192];
+                    LT += pp[ww * 192 + 64];
+                    MQ += pp[ww * 192 + 128];
+                }
+                const f32x4 brow = *reinterpret_cast<const f32x4 *>(sbeta + 4 * lq);
+                const float bcol = sbeta[ln];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 4 * lq + i;
+                    L[i] = row > ln ? -brow[i] * L[i] : 0.f;      // L[row][ln], strictly lower
+                    LT[i] = ln > row ? -bcol * LT[i] : 0.f;       // L[ln][row]
+                    MQ[i] = ln >= row ? MQ[i] : 0.f;              // Mqk[ln][row], lower incl. diagonal
+                }
+                const f32x4 L2 = prod16<BF16>(LT, L), L2T = prod16<BF16>(L, LT);
+                const f32x4 L4 = prod16<BF16>(L2T, L2), L4T = prod16<BF16>(L2, L2T);
+                const f32x4 L8 = prod16<BF16>(L4T, L4);
+                // A^T = ((I + L)(I + L^2))^T,  B = (I + L^4)(I + L^8),  INV^T = B^T A^T
+                const f32x4 AT = prod16<BF16>(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
+                const f32x4 Bm = prod16<BF16>(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
+                const f32x4 IT = prod16<BF16>(Bm, AT);
+                if constexpr (BF16) {
+                    *reinterpret_cast<bf16x8 *>(slot + P::INV + lane * 16) = split_hilo(IT);
+                    *reinterpret_cast<bf16x8 *>(slot + P::MQK + lane * 16) = split_hilo(MQ);
+                } else {
+                    *reinterpret_cast<f32x4 *>(slot + P::INV + lane * 16) = IT;
+                    *reinterpret_cast<f32x4 *>(slot + P::MQK + lane * 16) = MQ;
+                }
+                if (lane < CH) reinterpret_cast<float *>(slot + P::BETA)[lane] = sbeta[lane];
+            } else {
+                // ---- k^r fragments (from the staging area) and v fragments (from the inputs)
+                constexpr int NKR = (DK / 16) * 64, NVF = (DV / 16) * 64;
+                using E = typename Elem<BF16>::T;
+                for (int idx = tid - 64; idx < NKR + NVF; idx += NTHR - 64) {
+                    const int l2 = idx & 63, lq2 = l2 >> 4, ln2 = l2 & 15;
+                    E x[4];
+                    int dst;
+                    if (idx < NKR) {
+                        const int mt = idx >> 6;
+                        const int ch = tile_chan<BF16>(mt, ln2 >> 2, ln2 & 3);
+                        const int uu = ch / UC, jj = ch - uu * UC;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int pos = 64 * (uu >> 2) + 16 * (uu & 3) + 4 * lq2 + i;
+                            x[i] = *reinterpret_cast<const E *>(lds + G::KRS + pos * 16 + jj * G::ES);
+                        }
+                        dst = P::KR + (mt * 64 + l2) * P::KRB;
+                    } else {
+                        const int vt = (idx - NKR) >> 6;
+                        const int col = 16 * vt + ln2, vu = col / UC, e = col - vu * UC;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int tau = 4 * lq2 + i;
+                            x[i] = tau < rem ? *reinterpret_cast<const E *>(lds + G::IV + (tau * G::NVU + vu) * 16 +
+                                                                              e * G::ES)
+                                             : E(0);
+                        }
+                        dst = P::V + (vt * 64 + l2) * 4 * G::ES;
+                    }
+                    if constexpr (BF16) {
+                        uint2 wv;
+                        wv.x = (uint32_t)x[0] | ((uint32_t)x[1] << 16);
+                        wv.y = (uint32_t)x[2] | ((uint32_t)x[3] << 16);
+                        *reinterpret_cast<uint2 *>(slot + dst) = wv;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(slot + dst) = f32x4{x[0], x[1], x[2], x[3]};
+                    }
+                }
+            }
+            stores_done();
+            lds_barrier();
+            if (tid == 0) st_flag(&ready[s], q + 1);
+            cur = nxt;
         }
         return;
     }
@@ -745,7 +778,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         if (computes && args.h_T) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
-                *reinterpret_cast<f32x4 *>(args.h_T + hbase + 16 * mt + 4 * lq) = S[mt];
+                *reinterpret_cast<f32x4 *>(args.h_T + hbase + tile_chan<BF16>(mt, lq, 0)) = S[mt];
         }
     };
     auto open_chain = [&]() {
@@ -755,7 +788,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         hbase = (((size_t)ci.seq * args.H + ci.head) * DV + v0 + ln) * DK;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            if (args.h0 && computes) S[mt] = *reinterpret_cast<const f32x4 *>(args.h0 + hbase + 16 * mt + 4 * lq);
+            if (args.h0 && computes)
+                S[mt] = *reinterpret_cast<const f32x4 *>(args.h0 + hbase + tile_chan<BF16>(mt, lq, 0));
             else S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         vm_wait<0>();   // the state is never a pending load inside the chunk loop
