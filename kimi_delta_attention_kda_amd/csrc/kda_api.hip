@@ -82,9 +82,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw
     kda::ChunkArgs a;
     a.ring = static_cast<unsigned char *>(ws);
     a.flags = reinterpret_cast<int *>(a.ring + (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES);
-    a.ready = a.flags;
-    a.used = a.flags + KDA_MAX_TEAMS * KDA_RING;
-    a.err = a.used + KDA_MAX_TEAMS * KDA_RING;
+    a.err = a.flags + (size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS;
     a.n_teams = 0;
     a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
     a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.cu_seqlens = cu_seqlens;
@@ -101,7 +99,7 @@ int kda_chunk_fwd_check(hipStream_t stream)
     if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
     const int *err = reinterpret_cast<const int *>(static_cast<unsigned char *>(ws) +
                                                    (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES) +
-                     2 * KDA_MAX_TEAMS * KDA_RING;
+                     (size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS;
     int h = 0;
     if (hipMemcpy(&h, err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return KDA_ERR_HIP;
     return h ? KDA_ERR_TIMEOUT : KDA_OK;

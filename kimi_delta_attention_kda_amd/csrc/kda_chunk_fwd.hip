@@ -296,7 +296,7 @@ template <bool BF16, int DK, int DV>
 struct PIn {
     uint4 k, q, a;
     uint4 v[PG<BF16, DK, DV>::NVL];
-    float b;
+    typename Elem<BF16>::T b;   // raw bits: converted only where used
 };
 
 // DPP: x of the lane n below in the same 16-lane row (0 past the row start),
@@ -358,7 +358,7 @@ __device__ __forceinline__ void prod_load(PIn<BF16, DK, DV> &in, const Cursor &c
             in.v[j] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v) + off);
         }
     }
-    if (w == 0) in.b = load_act<BF16>(a.beta_raw, (tok0 + min(lane, last)) * H + h);
+    if (w == 0) in.b = static_cast<const typename Elem<BF16>::T *>(a.beta_raw)[(tok0 + min(lane, last)) * H + h];
 }
 
 // hi/lo bf16 parts of 8 values (two groups of 4).
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     constexpr int MT = DK / 16;
     constexpr int NP = KDA_PRODUCER_WGS;
     static_assert(NCW >= 1 && NCW <= 4, "consumer slab of 16..64 columns");
-    static_assert(KDA_RING <= 64, "one lane per ring slot when polling");
+    static_assert(KDA_RING <= 32, "one lane per ring slot when polling; ready and used in their own lines");
 
     // LDS: producers use their input buffers and scratch, consumers a 3-deep payload buffer.
     constexpr int PROD_BYTES = PG<BF16, DK, DV>::BYTES;
@@ -476,8 +476,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, lq = lane >> 4;
     unsigned char *ring = args.ring + (size_t)role.team * KDA_RING * KDA_RING_SLOT_BYTES;
-    int *ready = args.ready + role.team * KDA_RING;
-    int *used = args.used + role.team * KDA_RING;
+    int *ready = args.flags + (size_t)role.team * KDA_TEAM_FLAG_INTS;
+    int *used = ready + 32;
     int *err = args.err;
     const int n_chains = args.n_seq * args.H;
 
@@ -502,6 +502,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         Cursor cd = cp;                                 // the chunk being loaded, one step ahead
         PIn<BF16, DK, DV> cur, nxt;
         prod_load<BF16, DK, DV>(cur, cp, p, args, wu, lane);
+        // `cur` is never a pending load inside the loop (there it is a copy of
+        // `nxt` made after the drain); without this wait the compiler would
+        // wait inside the loop for the next chunk's loads before using `cur`
+        vm_wait<0>();
         int cur_chain = -1;
         float A_exp = 0.f, dtl[UC];
         for (int it = 0;; ++it) {
@@ -644,7 +648,12 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 pp[64] = pLT;
                 pp[128] = pMT;
             }
-            if (wu == 0 && lane < CH) sbeta[lane] = lane < rem ? sigmoid_f(cur.b) : 0.f;
+            if (wu == 0 && lane < CH) {
+                float bv;
+                if constexpr (BF16) bv = bf16_to_f32(cur.b);
+                else bv = cur.b;
+                sbeta[lane] = lane < rem ? sigmoid_f(bv) : 0.f;
+            }
             lds_barrier();
 
             if (wu == 0) {
@@ -969,7 +978,7 @@ static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
     if (n_teams > n_chains) n_teams = n_chains;
     if (n_teams > KDA_MAX_TEAMS) n_teams = KDA_MAX_TEAMS;
     a.n_teams = n_teams;
-    e = hipMemsetAsync(a.flags, 0, sizeof(int) * (2 * (size_t)KDA_MAX_TEAMS * KDA_RING + 64), stream);
+    e = hipMemsetAsync(a.flags, 0, chunk_flag_bytes(), stream);
     if (e != hipSuccess) return e;
     const unsigned grid = 8u * TS * (unsigned)((n_teams + 7) / 8);
     hipLaunchKernelGGL((chunk_fwd_kernel<BF16, DK, DV, BDV>), dim3(grid), dim3(NTHR), 0, stream, a);

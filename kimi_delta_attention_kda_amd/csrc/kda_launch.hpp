@@ -11,6 +11,10 @@
 #define KDA_RING_SLOT_BYTES 24576
 #define KDA_PRODUCER_WGS 4
 #define KDA_MAX_TEAMS 256
+// Per-team flag block (ints): ready[KDA_RING] at 0, used[KDA_RING] at 32, so
+// each array has a cache line to itself and no line is shared between teams
+// (teams run on different XCDs).
+#define KDA_TEAM_FLAG_INTS 64
 
 namespace kda {
 
@@ -29,15 +33,16 @@ struct ChunkArgs {
     float scale;
     // workspace (device memory owned by the library)
     unsigned char *ring;   // KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES
-    int *flags;            // ready[KDA_MAX_TEAMS*KDA_RING], used[...], err  (zeroed per launch)
-    int *ready, *used, *err;
+    int *flags;            // [KDA_MAX_TEAMS][KDA_TEAM_FLAG_INTS], then err (zeroed per launch)
+    int *err;
     int n_teams;           // set by the launcher
 };
 
+// Bytes of the flag area (team blocks, then a 256-byte block for the error word).
+inline size_t chunk_flag_bytes() { return sizeof(int) * ((size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS + 64); }
 // Device bytes of the chunk-forward workspace.
 inline size_t chunk_workspace_bytes() {
-    return (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES +
-           sizeof(int) * (2 * (size_t)KDA_MAX_TEAMS * KDA_RING + 64);
+    return (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES + chunk_flag_bytes();
 }
 
 // dtype: 0 = float32, 1 = bfloat16 activations.
