@@ -121,8 +121,8 @@ __device__ __forceinline__ void lds_dma16(const void *src, unsigned lds) {
 }
 template <int N>
 __device__ __forceinline__ void vm_wait() {       // at most N vector-memory ops of this wave in flight
-    static_assert(N >= 0 && N < 16, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
     asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ unsigned lds_addr(const void *p) {
@@ -160,7 +160,8 @@ struct PL {
     static constexpr int MQK = INV + 64 * 16;
     static constexpr int BETA = MQK + 64 * 16;
     static constexpr int EG = BETA + 64;
-    static constexpr int V = EG + DK * 4;                  // v: fragment vt, lane: rows 4lq..4lq+3 of column 16vt+ln
+    static constexpr int V = (EG + DK * 4 + 1023) / 1024 * 1024;   // v (1 KiB aligned): fragment vt,
+                                                                   // lane: rows 4lq..4lq+3 of column 16vt+ln
     static constexpr int END = V + (DV / 16) * 64 * 4 * ES;
     static constexpr int BYTES = (END + 1023) / 1024 * 1024;   // copied size
 };
@@ -219,13 +220,31 @@ struct Role {
     int team;      // team id, or -1 when idle
     int member;    // 0 .. NS-1 consumer (slab), NS .. NS+NP-1 producer
 };
-__device__ __forceinline__ Role role_of(int NS, int NP, int n_teams) {
+// Workgroups are dispatched to the 8 XCDs round robin (blockIdx % 8); within
+// an XCD the first `pair_half` workgroups (one per CU) take every CU once and
+// workgroup y + pair_half then lands on the same CU as workgroup y.  With
+// pair_half > 0 a team occupies ceil(TS/2) CUs: the older workgroup of each
+// CU takes members 0, 1, ... (the consumers first), the younger one the
+// matching later member (the producers), so consumers share their CU with a
+// producer of their own team and win instruction arbitration against it.
+// With pair_half == 0 (one workgroup per CU) members are consecutive.
+__device__ __forceinline__ Role role_of(int NS, int NP, int n_teams, int pair_half, int teams_per_xcd) {
     const int TS = NS + NP;
     const int x = blockIdx.x % 8, y = blockIdx.x / 8;
+    int tx, member;
+    if (pair_half > 0) {
+        const int cpt = (TS + 1) / 2;                 // CUs per team
+        const int h = y >= pair_half ? 1 : 0, yy = y - h * pair_half;
+        tx = yy / cpt;
+        member = yy - tx * cpt + h * cpt;
+    } else {
+        tx = y / TS;
+        member = y - tx * TS;
+    }
     Role r;
-    r.team = (y / TS) * 8 + x;
-    r.member = y % TS;
-    if (r.team >= n_teams) r.team = -1;
+    r.team = tx * 8 + x;
+    r.member = member;
+    if (member >= TS || tx >= teams_per_xcd || r.team >= n_teams) r.team = -1;
     return r;
 }
 
@@ -267,9 +286,10 @@ __device__ __forceinline__ int tile_chan(int mt, int lq, int i) {
     else return 16 * mt + 4 * lq + i;
 }
 
-// Producer LDS: the chunk's v rows (read back transposed into the consumers'
-// C layout) and beta_raw, the k^r staging area, the per-wave partial 16x16
-// sums and beta.
+// Producer LDS: v and k^r transposed to [column / channel][token] (a
+// consumer fragment of 4 tokens of one column is then one contiguous read;
+// rows padded so the writers of neighbouring channels use different banks),
+// the per-wave partial 16x16 sums (L and Mqk^T) and beta.
 template <bool BF16, int DK, int DV>
 struct PG {
     static constexpr int ES = BF16 ? 2 : 4;
@@ -279,11 +299,11 @@ struct PG {
     static constexpr int NWU = NU / 4;              // waves holding channel units
     static constexpr int NVP = 16 * NVU / 64;       // v units per chunk / 64
     static constexpr int NVL = (NVP + 3) / 4;       // v units per lane
-    static constexpr int IV = 0;                    // v: [token][unit]
-    static constexpr int IB = IV + 16 * NVU * 16;   // beta_raw: one float per token
-    static constexpr int KRS = IB + CH * 4;
-    static constexpr int PART = KRS + 16 * NU * 16;
-    static constexpr int SBETA = PART + NWU * 3 * 64 * 16;
+    static constexpr int TP = 16 * ES + (BF16 ? 8 : 16);   // bytes per transposed row (16 tokens + pad)
+    static constexpr int VT = 0;                    // v^T: [DV][16 tokens]
+    static constexpr int KRT = VT + DV * TP;        // k^r^T: [DK][16 tokens]
+    static constexpr int PART = KRT + DK * TP;
+    static constexpr int SBETA = PART + NWU * 2 * 64 * 16;
     static constexpr int BYTES = SBETA + CH * 4;
     static_assert(NU % 4 == 0 && NU <= 16, "4..16 channel units");
     static_assert(NVP >= 1 && (16 * NVU) % 64 == 0, "v units");
@@ -467,15 +487,23 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
 
     // LDS: producers use their input buffers and scratch, consumers a 3-deep payload buffer.
     constexpr int PROD_BYTES = PG<BF16, DK, DV>::BYTES;
-    constexpr int CONS_BYTES = 3 * ((P::BYTES + 16 * NTHR - 1) / (16 * NTHR)) * 16 * NTHR;
+    constexpr int CONS_BYTES = 3 * ((P::BYTES + 16 * NTHR - 1) / (16 * NTHR)) * 16 * NTHR +
+                               (BDV < 64 ? 2 * (BDV / 16) * 64 * 16 : 0) + 16;   // helper-stored outputs, kshared
     constexpr int LDS_BYTES = PROD_BYTES > CONS_BYTES ? PROD_BYTES : CONS_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
-    const Role role = role_of(NS, NP, args.n_teams);
+    const Role role = role_of(NS, NP, args.n_teams, args.pair_half, args.teams_per_xcd);
     if (role.team < 0) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, lq = lane >> 4;
-    unsigned char *ring = args.ring + (size_t)role.team * KDA_RING * KDA_RING_SLOT_BYTES;
+    // Payload q is copied by all NTHR threads of a consumer, NFT 16-byte pieces
+    // each, into LDS buffer q % 3; a ring slot holds SLOT = PBUF bytes (the tail
+    // past the payload is copied but unused).
+    constexpr int NFT = (P::BYTES + 16 * NTHR - 1) / (16 * NTHR);
+    constexpr int PBUF = NFT * 16 * NTHR;
+    constexpr int SLOT = PBUF;
+    static_assert(SLOT <= KDA_RING_SLOT_BYTES, "slot larger than the workspace's");
+    unsigned char *ring = args.ring + (size_t)role.team * KDA_RING * SLOT;
     int *ready = args.flags + (size_t)role.team * KDA_TEAM_FLAG_INTS;
     int *used = ready + 32;
     int *err = args.err;
@@ -521,7 +549,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                     dtl[c] = has_unit ? args.dt_bias[(size_t)cp.ci.head * DK + UC * u + c] * kLog2e : 0.f;
             }
             const int s = q % KDA_RING;
-            unsigned char *slot = ring + (size_t)s * KDA_RING_SLOT_BYTES;
+            unsigned char *slot = ring + (size_t)s * SLOT;
             // slot free?  (polled before this step's loads are issued, so the poll's
             // wait covers nothing else; spinning on scalar loads instead would
             // starve the instruction fetch of neighbouring compute units)
@@ -533,11 +561,24 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 cursor_seek(cd, qn, args, args.n_teams);
                 prod_load<BF16, DK, DV>(nxt, cd, qn, args, wu, lane);
             }
-            // v rows and beta_raw go to LDS for the transposing readers
+            // v to LDS as [column][token] (padding tokens zero) for the fragment writers
+            using E = typename Elem<BF16>::T;
 #pragma unroll
             for (int j = 0; j < G::NVL; ++j) {
                 const int m = wu + 4 * j;
-                if (m < G::NVP) *reinterpret_cast<uint4 *>(lds + G::IV + (64 * m + lane) * 16) = cur.v[j];
+                if (m < G::NVP) {
+                    const int pv = 64 * m + lane, tv = pv / G::NVU, vu = pv - tv * G::NVU;
+                    const uint4 x = cur.v[j];
+                    const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                    for (int e = 0; e < G::UC; ++e) {
+                        E val;
+                        if constexpr (BF16) val = (E)(wv[e >> 1] >> (16 * (e & 1)));
+                        else val = __builtin_bit_cast(float, wv[e]);
+                        *reinterpret_cast<E *>(lds + G::VT + (G::UC * vu + e) * G::TP + tv * G::ES) =
+                            tv < rem ? val : E(0);
+                    }
+                }
             }
 
             if (has_unit) {
@@ -570,7 +611,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 }
                 pack16<BF16>(slot + P::KD + tid * 16, kd);
                 pack16<BF16>(slot + P::QD + tid * 16, qd);
-                pack16<BF16>(lds + G::KRS + tid * 16, kr);
+#pragma unroll
+                for (int c = 0; c < UC; ++c)
+                    *reinterpret_cast<E *>(lds + G::KRT + (UC * u + c) * G::TP + t * G::ES) = to_elem<BF16>(kr[c]);
                 if (t == CH - 1) {
                     float *eg = reinterpret_cast<float *>(slot + P::EG);
                     if constexpr (BF16) {
@@ -581,7 +624,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                     }
                 }
                 // ---- this wave's share of L (rows i), L^T and Mqk^T over its UC*4 channels
-                f32x4 pL = {0.f, 0.f, 0.f, 0.f}, pLT = pL, pMT = pL;
+                f32x4 pL = {0.f, 0.f, 0.f, 0.f}, pMT = pL;
                 if (__ballot(deep) == 0) {
                     // mild: one reference at the chunk end, rows k 2^{G - G_C} (<= 2^100), columns k^r (<= 1)
                     float R[UC], Rq[UC];
@@ -594,11 +637,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                     if constexpr (BF16) {
                         const HL8 hR = split8(R), hRq = split8(Rq), hC = split8(kr);
                         pL = contract8(hR, hC, pL);
-                        pLT = contract8(hC, hR, pLT);
                         pMT = contract8(hC, hRq, pMT);
                     } else {
                         pL = contract4(R, kr, pL);
-                        pLT = contract4(kr, R, pLT);
                         pMT = contract4(kr, Rq, pMT);
                     }
                 } else {
@@ -627,26 +668,23 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                             C[c] = t < 4 * b + 4 ? kf[c] * __builtin_amdgcn_exp2f(ref - Gp[c]) : 0.f;   // <= 2^96
                         }
                         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                        f32x4 Lb, LTb, MTb;
+                        f32x4 Lb, MTb;
                         if constexpr (BF16) {
                             const HL8 hC = split8(C);
                             Lb = contract8(hR, hC, z);
-                            LTb = contract8(hC, hR, z);
                             MTb = contract8(hC, hRq, z);
                         } else {
                             Lb = contract4(R, C, z);
-                            LTb = contract4(C, R, z);
                             MTb = contract4(C, Rq, z);
                         }
-                        // keep the rows (of L) that lie in block b
+                        // keep the rows (of L and Mqk) that lie in block b
                         if (r == b) pL = Lb;
-                        if ((t >> 2) == b) { pLT = LTb; pMT = MTb; }
+                        if ((t >> 2) == b) pMT = MTb;
                     }
                 }
-                f32x4 *pp = reinterpret_cast<f32x4 *>(lds + G::PART) + (wu * 3) * 64 + lane;
+                f32x4 *pp = reinterpret_cast<f32x4 *>(lds + G::PART) + (wu * 2) * 64 + lane;
                 pp[0] = pL;
-                pp[64] = pLT;
-                pp[128] = pMT;
+                pp[64] = pMT;
             }
             if (wu == 0 && lane < CH) {
                 float bv;
@@ -657,14 +695,18 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             lds_barrier();
 
             if (wu == 0) {
-                // ---- L, L^T (C layout), masks and beta; INV by Neumann squaring in transposed pairs
+                // ---- L, L^T (C layout; L^T read transposed from the L sums), masks and beta;
+                // INV by Neumann squaring in transposed pairs
                 f32x4 L = {0.f, 0.f, 0.f, 0.f}, LT = L, MQ = L;
                 const f32x4 *pp = reinterpret_cast<const f32x4 *>(lds + G::PART) + lane;
+                const float *pf = reinterpret_cast<const float *>(lds + G::PART);
 #pragma unroll
                 for (int ww = 0; ww < G::NWU; ++ww) {
-                    L += pp[ww * 192];
-                    LT += pp[ww * 192 + 64];
-                    MQ += pp[ww * 192 + 128];
+                    L += pp[ww * 128];
+                    MQ += pp[ww * 128 + 64];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)   // L[ln][4lq+i]: lane 16(ln/4) + 4lq + i, element ln % 4
+                        LT[i] += pf[(ww * 128 + 16 * (ln >> 2) + 4 * lq + i) * 4 + (ln & 3)];
                 }
                 const f32x4 brow = *reinterpret_cast<const f32x4 *>(sbeta + 4 * lq);
                 const float bcol = sbeta[ln];
@@ -693,41 +735,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             } else {
                 // ---- k^r fragments (from the staging area) and v fragments (from the inputs)
                 constexpr int NKR = (DK / 16) * 64, NVF = (DV / 16) * 64;
-                using E = typename Elem<BF16>::T;
                 for (int idx = tid - 64; idx < NKR + NVF; idx += NTHR - 64) {
                     const int l2 = idx & 63, lq2 = l2 >> 4, ln2 = l2 & 15;
-                    E x[4];
-                    int dst;
+                    int src, dst;   // 4 tokens of one channel / column: 4 * ES contiguous bytes
                     if (idx < NKR) {
                         const int mt = idx >> 6;
-                        const int ch = tile_chan<BF16>(mt, ln2 >> 2, ln2 & 3);
-                        const int uu = ch / UC, jj = ch - uu * UC;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int pos = 64 * (uu >> 2) + 16 * (uu & 3) + 4 * lq2 + i;
-                            x[i] = *reinterpret_cast<const E *>(lds + G::KRS + pos * 16 + jj * G::ES);
-                        }
+                        src = G::KRT + tile_chan<BF16>(mt, ln2 >> 2, ln2 & 3) * G::TP + 4 * lq2 * G::ES;
                         dst = P::KR + (mt * 64 + l2) * P::KRB;
                     } else {
                         const int vt = (idx - NKR) >> 6;
-                        const int col = 16 * vt + ln2, vu = col / UC, e = col - vu * UC;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int tau = 4 * lq2 + i;
-                            x[i] = tau < rem ? *reinterpret_cast<const E *>(lds + G::IV + (tau * G::NVU + vu) * 16 +
-                                                                              e * G::ES)
-                                             : E(0);
-                        }
+                        src = G::VT + (16 * vt + ln2) * G::TP + 4 * lq2 * G::ES;
                         dst = P::V + (vt * 64 + l2) * 4 * G::ES;
                     }
-                    if constexpr (BF16) {
-                        uint2 wv;
-                        wv.x = (uint32_t)x[0] | ((uint32_t)x[1] << 16);
-                        wv.y = (uint32_t)x[2] | ((uint32_t)x[3] << 16);
-                        *reinterpret_cast<uint2 *>(slot + dst) = wv;
-                    } else {
-                        *reinterpret_cast<f32x4 *>(slot + dst) = f32x4{x[0], x[1], x[2], x[3]};
-                    }
+                    if constexpr (BF16) *reinterpret_cast<uint2 *>(slot + dst) = *reinterpret_cast<const uint2 *>(lds + src);
+                    else *reinterpret_cast<f32x4 *>(slot + dst) = *reinterpret_cast<const f32x4 *>(lds + src);
                 }
             }
             stores_done();
@@ -740,19 +761,38 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
 
     // =========================================================== consumer
     const int slab = role.member;
-    const bool computes = w < NCW;
-    const int v0 = slab * BDV + 16 * (w < NCW ? w : 0);
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const bool computes = wu < NCW;
+    const int v0 = slab * BDV + 16 * (computes ? wu : 0);
     const int vt = v0 >> 4;
+    // Helper waves (those beyond the slab's compute waves, if any) poll the
+    // ring, copy the payloads into LDS and store the outputs, so that the
+    // compute waves never wait on memory inside the loop.  Without helpers
+    // every wave does a share.
+    constexpr int NH = 4 - NCW;                   // helper waves
+    constexpr int CPW = NH > 0 ? NH : 4;          // copying waves
+    const bool copier = NH > 0 ? wu >= NCW : true;
+    const int cw = NH > 0 ? wu - NCW : wu;        // index among the copying waves
+    const bool poller = cw == 0;                  // the one wave that polls the ready flags
+    unsigned char *obuf = lds + 3 * PBUF;         // [2][NCW][64 lanes] f32x4 outputs (helpers store them)
+    volatile int *kshared = reinterpret_cast<volatile int *>(lds + 3 * PBUF +
+                                                             (NH > 0 ? 2 * NCW * 64 * 16 : 0));
+    // Copied blocks (1 KiB each): the payload up to v, then this slab's v blocks only.
+    constexpr int FB = 64 * 4 * P::ES;            // bytes per v fragment
+    constexpr int VB0 = P::V / 1024;
+    constexpr int NSB = ((BDV / 16) * FB + 1023) / 1024;
+    constexpr int NCB = VB0 + NSB;
+    const int SB0 = (P::V + slab * (BDV / 16) * FB) / 1024;
     int q_total = 0;
     for (int chain = role.team; chain < n_chains; chain += args.n_teams)
         q_total += (chain_info(args, chain).len + CH - 1) / CH;
 
-    // Ready tracking: chunks <= known are ready.  One poll loads all RING flags
-    // (one lane per slot) and extends `known` over the run of ready chunks.
+    // Ready tracking (poller): chunks <= known are ready.  One poll loads all
+    // RING flags (one lane per slot) and extends `known` over the run of ready
+    // chunks; the poller publishes it in LDS for the other waves.
     int known = -1;
     auto ensure_ready = [&](int need) {
         if (need <= known) return;
-        if (ld_flag(err)) return;
         for (long n = 0;; ++n) {
             const int f = lane < KDA_RING ? ld_flag(&ready[lane]) : 0;
             const int cj = need + lane;
@@ -760,24 +800,47 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             const unsigned long long ok = __ballot(lane < KDA_RING && fj >= cj + 1);
             const int run = __builtin_ctzll(~ok);
             if (run > 0) { known = need + run - 1; return; }
+            // not ready yet: give up if another wait already did, else wait a little
+            if (ld_flag(err) || n > SPIN_LIMIT) { st_flag(err, 1); known = q_total; return; }
             __builtin_amdgcn_s_sleep(2);
-            if (n > SPIN_LIMIT) { st_flag(err, 1); known = q_total; return; }
         }
     };
-    // Payload q is copied by all NTHR threads, NFT 16-byte DMA pieces each,
-    // into LDS buffer q % 3 (a buffer holds PBUF bytes; the tail past the
-    // payload copies unused slot bytes).
-    constexpr int NFT = (P::BYTES + 16 * NTHR - 1) / (16 * NTHR);
-    constexpr int PBUF = NFT * 16 * NTHR;
-    static_assert(PBUF <= KDA_RING_SLOT_BYTES, "slot smaller than the DMA footprint");
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    const unsigned lds0 = lds_addr(lds) + wu * 64 * 16;
-    auto dma = [&](int q) {
-        const unsigned char *src = ring + (size_t)(q % KDA_RING) * KDA_RING_SLOT_BYTES + tid * 16;
-        const unsigned dst = lds0 + (unsigned)(q % 3) * PBUF;
-#pragma unroll
-        for (int j = 0; j < NFT; ++j) lds_dma16(src + j * NTHR * 16, dst + j * NTHR * 16);
+    // The non-polling waves read the published value (LDS; bounded wait).
+    auto await_ready = [&](int need) {
+        if (poller) {
+            ensure_ready(need);
+            if (lane == 0) *kshared = known;
+            return;
+        }
+        for (long n = 0; *kshared < need; ++n) {
+            __builtin_amdgcn_s_sleep(1);
+            if (n > SPIN_LIMIT) { st_flag(err, 1); return; }
+        }
     };
+    // This wave's share of the copy of payload q into LDS buffer q % 3:
+    // copy blocks j = cw, cw + CPW, ... < NCB (lane i moves bytes 16 i .. 16 i + 15).
+    auto dma = [&](int q) {
+        const unsigned char *src = ring + (size_t)(q % KDA_RING) * SLOT + lane * 16;
+        const unsigned dst = lds_addr(lds) + (unsigned)(q % 3) * PBUF;
+        for (int j = cw; j < NCB; j += CPW) {
+            const int b = j < VB0 ? j : SB0 + (j - VB0);
+            lds_dma16(src + b * 1024, dst + b * 1024);
+        }
+    };
+    // Wait until at most one copy share of this wave is in flight.
+    auto dma_wait_one = [&]() {
+        constexpr int N0 = (NCB + CPW - 1) / CPW;
+        constexpr int N1 = CPW > 1 ? (NCB - 1 + CPW - 1) / CPW : 0;
+        constexpr int N2 = CPW > 2 ? (NCB - 2 + CPW - 1) / CPW : 0;
+        constexpr int N3 = CPW > 3 ? (NCB - 3 + CPW - 1) / CPW : 0;
+        switch (cw) {
+        case 0: vm_wait<N0>(); break;
+        case 1: vm_wait<N1>(); break;
+        case 2: vm_wait<N2>(); break;
+        default: vm_wait<N3>(); break;
+        }
+    };
+
     int chain = role.team, c = 0, nch = 0;
     ChainInfo ci{};
     f32x4 S[MT];
@@ -804,17 +867,42 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         vm_wait<0>();   // the state is never a pending load inside the chunk loop
     };
 
-    // Output rows of the previous chunk, stored one step late so that the
-    // stores are older than the next DMA and never delay the payload wait.
+    // Output rows of the previous chunk, stored one step late (older than the
+    // next copy, so they never delay the payload wait).  With helper waves the
+    // compute waves leave them in LDS and the helpers store them.
     f32x4 Op = {0.f, 0.f, 0.f, 0.f};
-    size_t op_base = 0;
-    int op_rem = 0;
+    size_t op_tok = 0;
+    int op_rem = 0, op_head = 0;
     const size_t o_row = (size_t)args.H * DV;
-    auto flush_o = [&]() {
-        if (computes) {
+    auto flush_o = [&](int q) {     // outputs of chunk q - 1
+        if (op_rem > 0) {
+            if constexpr (NH == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * lq + i < op_rem) store_act<BF16>(args.o, op_base + (4 * lq + i) * o_row, Op[i]);
+                for (int i = 0; i < 4; ++i)
+                    if (4 * lq + i < op_rem)
+                        store_act<BF16>(args.o, (op_tok * args.H + op_head) * DV + v0 + ln + (4 * lq + i) * o_row,
+                                        Op[i]);
+            } else if (!computes) {
+                // lane: row lane / 4 of the tile, columns 4 (lane % 4) .. + 3 (one contiguous store)
+                const int row = lane >> 2, c4 = 4 * (lane & 3);
+                for (int wc = cw; wc < NCW; wc += NH) {
+                    const float *ot = reinterpret_cast<const float *>(obuf) + (((q - 1) & 1) * NCW + wc) * 256;
+                    float x[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[j] = ot[(16 * (row >> 2) + c4 + j) * 4 + (row & 3)];
+                    if (row < op_rem) {
+                        const size_t at = ((op_tok + row) * args.H + op_head) * DV + slab * BDV + 16 * wc + c4;
+                        if constexpr (BF16) {
+                            uint2 v2;
+                            v2.x = pack_bf16x2(x[0], x[1]);
+                            v2.y = pack_bf16x2(x[2], x[3]);
+                            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.o) + at) = v2;
+                        } else {
+                            *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = f32x4{x[0], x[1], x[2], x[3]};
+                        }
+                    }
+                }
+            }
         }
         op_rem = 0;
     };
@@ -833,46 +921,25 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         const size_t tok0 = ci.bos + (size_t)c * CH;
         const int rem = min(CH, ci.len - c * CH);
         const bool ahead = q + 2 < q_total;
-        if (ahead) ensure_ready(q + 2);
-        flush_o();
-        if (ahead) dma(q + 2);
+        if (copier) {
+            if (ahead) await_ready(q + 2);
+            flush_o(q);
+            if (ahead) dma(q + 2);
+        }
         if (computes) {
             const unsigned char *pl = lds + (q % 3) * PBUF;
-            // R1: W = k~ S, Qs = q~ S ; then decay the state in place
-            f32x4 W = {0.f, 0.f, 0.f, 0.f}, Qs = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF16) {
+            // all of this chunk's LDS operands first: their latency overlaps R1
+            using FragK = typename std::conditional<BF16, bf16x8, f32x4>::type;
+            constexpr int NF = P::NF;
+            FragK ak[NF], aq[NF];
+            f32x4 eg[MT];
 #pragma unroll
-                for (int s = 0; s < DK / 32; ++s) {
-                    bf16x8 b;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        b[i] = static_cast<__bf16>(S[2 * s][i]);
-                        b[4 + i] = static_cast<__bf16>(S[2 * s + 1][i]);
-                    }
-                    const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(pl + P::KD + (s * 64 + lane) * 16);
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(pl + P::QD + (s * 64 + lane) * 16);
-                    W = mfma_bf16(ak, b, W);
-                    Qs = mfma_bf16(aq, b, Qs);
-                }
-            } else {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const f32x4 ak = *reinterpret_cast<const f32x4 *>(pl + P::KD + (mt * 64 + lane) * 16);
-                    const f32x4 aq = *reinterpret_cast<const f32x4 *>(pl + P::QD + (mt * 64 + lane) * 16);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        W = mfma_f32(ak[i], S[mt][i], W);
-                        Qs = mfma_f32(aq[i], S[mt][i], Qs);
-                    }
-                }
+            for (int s = 0; s < NF; ++s) {
+                ak[s] = *reinterpret_cast<const FragK *>(pl + P::KD + (s * 64 + lane) * 16);
+                aq[s] = *reinterpret_cast<const FragK *>(pl + P::QD + (s * 64 + lane) * 16);
             }
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const f32x4 e = *reinterpret_cast<const f32x4 *>(pl + P::EG + (16 * mt + 4 * lq) * 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[mt][i] *= e[i];
-            }
-            // R2: u = beta (v - W)
+            for (int mt = 0; mt < MT; ++mt) eg[mt] = *reinterpret_cast<const f32x4 *>(pl + P::EG + (16 * mt + 4 * lq) * 4);
             const f32x4 beta = *reinterpret_cast<const f32x4 *>(pl + P::BETA + lq * 16);
             f32x4 vv;
             if constexpr (BF16) {
@@ -882,23 +949,57 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             } else {
                 vv = *reinterpret_cast<const f32x4 *>(pl + P::V + (vt * 64 + lane) * 16);
             }
+            // R1: W = k~ S, Qs = q~ S ; then decay the state in place
+            f32x4 W = {0.f, 0.f, 0.f, 0.f}, Qs = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (BF16) {
+#pragma unroll
+                for (int s = 0; s < NF; ++s) {
+                    bf16x8 b;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        b[i] = static_cast<__bf16>(S[2 * s][i]);
+                        b[4 + i] = static_cast<__bf16>(S[2 * s + 1][i]);
+                    }
+                    W = mfma_bf16(ak[s], b, W);
+                    Qs = mfma_bf16(aq[s], b, Qs);
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        W = mfma_f32(ak[mt][i], S[mt][i], W);
+                        Qs = mfma_f32(aq[mt][i], S[mt][i], Qs);
+                    }
+                }
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[mt][i] *= eg[mt][i];
+            }
+            // R2: u = beta (v - W)
             f32x4 u;
 #pragma unroll
             for (int i = 0; i < 4; ++i) u[i] = beta[i] * (vv[i] - W[i]);
             // R3: U = INV u ; R4: O = Qs + Mqk U ; R5: S += k^r^T U
             f32x4 U = {0.f, 0.f, 0.f, 0.f}, O;
             if constexpr (BF16) {
+                // INV and Mqk arrive as [hi | lo]; the state-side operand carries
+                // the split instead: [x_hi | x_hi] then [x_lo | 0] gives
+                // (A_hi + A_lo) x_hi + A_hi x_lo.
                 const bf16x8 inv = *reinterpret_cast<const bf16x8 *>(pl + P::INV + lane * 16);
                 const bf16x8 mqk = *reinterpret_cast<const bf16x8 *>(pl + P::MQK + lane * 16);
-                bf16x4 ih, il, mh, ml;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { ih[i] = inv[i]; il[i] = inv[4 + i]; mh[i] = mqk[i]; ml[i] = mqk[4 + i]; }
-                const bf16x8 bu = split_hilo(u);
-                U = mfma_bf16(dup4(ih), bu, U);
-                U = mfma_bf16(dup4(il), bu, U);
-                const bf16x8 bU = split_hilo(U);
-                O = mfma_bf16(dup4(mh), bU, Qs);
-                O = mfma_bf16(dup4(ml), bU, O);
+                const bf16x4 zero = {};
+                bf16x4 uh, ul;
+                hilo4(u, uh, ul);
+                U = mfma_bf16(inv, cat4(uh, uh), U);
+                U = mfma_bf16(inv, cat4(ul, zero), U);
+                bf16x4 Uh, Ul;
+                hilo4(U, Uh, Ul);
+                O = mfma_bf16(mqk, cat4(Uh, Uh), Qs);
+                O = mfma_bf16(mqk, cat4(Ul, zero), O);
+                const bf16x8 bU = cat4(Uh, Ul);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const bf16x4 kr4 = *reinterpret_cast<const bf16x4 *>(pl + P::KR + (mt * 64 + lane) * 8);
@@ -921,31 +1022,41 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) Op[i] = args.scale * O[i];
-            op_base = (tok0 * args.H + ci.head) * DV + v0 + ln;
-            op_rem = rem;
+            if constexpr (NH > 0) reinterpret_cast<f32x4 *>(obuf)[((q & 1) * NCW + wu) * 64 + lane] = Op;
         }
-        if (ahead) vm_wait<NFT>();    // payload q+1 has landed (only q+2 may still fly)
-        else vm_wait<0>();
+        op_tok = tok0;
+        op_head = ci.head;
+        op_rem = rem;
+        if (copier) {
+            if (ahead) dma_wait_one();    // payload q+1 has landed (only q+2 may still fly)
+            else vm_wait<0>();
+        }
         lds_barrier();
-        if (q + 1 < q_total && tid == 0) add_flag(&used[(q + 1) % KDA_RING], 1);
+        if (q + 1 < q_total && tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[(q + 1) % KDA_RING], 1);
         ++c;
     };
 
     if (q_total > 0) {
-        ensure_ready(0);
-        dma(0);
-        if (q_total > 1) {
-            ensure_ready(1);
-            dma(1);
-            vm_wait<NFT>();
-        } else {
-            vm_wait<0>();
+        if (poller) {
+            ensure_ready(0);
+            if (q_total > 1) ensure_ready(1);
+            if (lane == 0) *kshared = known;
         }
         lds_barrier();
-        if (tid == 0) add_flag(&used[0], 1);
+        if (copier) {
+            dma(0);
+            if (q_total > 1) {
+                dma(1);
+                dma_wait_one();
+            } else {
+                vm_wait<0>();
+            }
+        }
+        lds_barrier();
+        if (tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[0], 1);
     }
     for (int q = 0; q < q_total; ++q) step(q);
-    flush_o();
+    if (copier) flush_o(q_total);
     // final state of the last open chain, then any trailing zero-length chains
     if (started) store_hT();
     for (chain = started ? chain + args.n_teams : role.team; chain < n_chains; chain += args.n_teams) {
@@ -978,9 +1089,17 @@ static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
     if (n_teams > n_chains) n_teams = n_chains;
     if (n_teams > KDA_MAX_TEAMS) n_teams = KDA_MAX_TEAMS;
     a.n_teams = n_teams;
+    teams_per_xcd = (n_teams + 7) / 8;
+    a.teams_per_xcd = teams_per_xcd;
+    // paired placement needs two resident workgroups per CU and XCDs of n_cu / 8 CUs
+    const int cus_per_xcd = n_cu / 8;
+    const int cpt = (TS + 1) / 2;
+    a.pair_half = (occ >= 2 && n_cu % 8 == 0 && teams_per_xcd * cpt <= cus_per_xcd) ? cus_per_xcd : 0;
     e = hipMemsetAsync(a.flags, 0, chunk_flag_bytes(), stream);
     if (e != hipSuccess) return e;
-    const unsigned grid = 8u * TS * (unsigned)((n_teams + 7) / 8);
+    const unsigned per_xcd = a.pair_half > 0 ? (unsigned)(cus_per_xcd + teams_per_xcd * cpt)
+                                             : (unsigned)(teams_per_xcd * TS);
+    const unsigned grid = 8u * per_xcd;
     hipLaunchKernelGGL((chunk_fwd_kernel<BF16, DK, DV, BDV>), dim3(grid), dim3(NTHR), 0, stream, a);
     return hipGetLastError();
 }

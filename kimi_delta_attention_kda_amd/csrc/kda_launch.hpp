@@ -7,8 +7,10 @@
 
 // Chunk-forward team ring: slots per team, bytes per slot, producer
 // workgroups per team, and the largest number of teams one launch uses.
+#ifndef KDA_RING
 #define KDA_RING 8
-#define KDA_RING_SLOT_BYTES 24576
+#endif
+#define KDA_RING_SLOT_BYTES 24576   // largest slot; a launch uses its payload's copy size
 #define KDA_PRODUCER_WGS 4
 #define KDA_MAX_TEAMS 256
 // Per-team flag block (ints): ready[KDA_RING] at 0, used[KDA_RING] at 32, so
@@ -36,6 +38,8 @@ struct ChunkArgs {
     int *flags;            // [KDA_MAX_TEAMS][KDA_TEAM_FLAG_INTS], then err (zeroed per launch)
     int *err;
     int n_teams;           // set by the launcher
+    int teams_per_xcd;     // set by the launcher
+    int pair_half;         // workgroups per XCD in the first dispatch round (0: no CU pairing)
 };
 
 // Bytes of the flag area (team blocks, then a 256-byte block for the error word).
