@@ -309,9 +309,15 @@ struct PG {
     static_assert(NVP >= 1 && (16 * NVU) % 64 == 0, "v units");
 };
 
+// The producer wave that forms INV (a serial chain of small MFMA products).
+// Its SIMD partner on the CU is a consumer wave that mostly waits (a helper
+// when the consumer slab has fewer than four compute waves), so the chain is
+// not starved by the consumer's higher-priority compute.
+constexpr int PROD_INV_WAVE = 3;
+
 // One chunk's inputs as one producer lane holds them: its k, q, g_raw units
 // (wave w < NWU), v units 64 m + lane for m = w, w + 4, ... (< NVP), and, in
-// wave 0, beta_raw of token `lane`.
+// wave PROD_INV_WAVE, beta_raw of token `lane`.
 template <bool BF16, int DK, int DV>
 struct PIn {
     uint4 k, q, a;
@@ -378,7 +384,7 @@ __device__ __forceinline__ void prod_load(PIn<BF16, DK, DV> &in, const Cursor &c
             in.v[j] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.v) + off);
         }
     }
-    if (w == 0) in.b = static_cast<const typename Elem<BF16>::T *>(a.beta_raw)[(tok0 + min(lane, last)) * H + h];
+    if (w == PROD_INV_WAVE) in.b = static_cast<const typename Elem<BF16>::T *>(a.beta_raw)[(tok0 + min(lane, last)) * H + h];
 }
 
 // hi/lo bf16 parts of 8 values (two groups of 4).
@@ -686,7 +692,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 pp[0] = pL;
                 pp[64] = pMT;
             }
-            if (wu == 0 && lane < CH) {
+            if (wu == PROD_INV_WAVE && lane < CH) {
                 float bv;
                 if constexpr (BF16) bv = bf16_to_f32(cur.b);
                 else bv = cur.b;
@@ -694,7 +700,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             }
             lds_barrier();
 
-            if (wu == 0) {
+            if (wu == PROD_INV_WAVE) {
                 // ---- L, L^T (C layout; L^T read transposed from the L sums), masks and beta;
                 // INV by Neumann squaring in transposed pairs
                 f32x4 L = {0.f, 0.f, 0.f, 0.f}, LT = L, MQ = L;
@@ -717,13 +723,15 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                     LT[i] = ln > row ? -bcol * LT[i] : 0.f;       // L[ln][row]
                     MQ[i] = ln >= row ? MQ[i] : 0.f;              // Mqk[ln][row], lower incl. diagonal
                 }
-                const f32x4 L2 = prod16<BF16>(LT, L), L2T = prod16<BF16>(L, LT);
-                const f32x4 L4 = prod16<BF16>(L2T, L2), L4T = prod16<BF16>(L2, L2T);
-                const f32x4 L8 = prod16<BF16>(L4T, L4);
+                // fp32 MFMA products: the C-layout operands feed 16x16x4 f32 MFMAs
+                // directly, with no bf16 splitting (the chain is latency bound)
+                const f32x4 L2 = prod16<false>(LT, L), L2T = prod16<false>(L, LT);
+                const f32x4 L4 = prod16<false>(L2T, L2), L4T = prod16<false>(L2, L2T);
+                const f32x4 L8 = prod16<false>(L4T, L4);
                 // A^T = ((I + L)(I + L^2))^T,  B = (I + L^4)(I + L^8),  INV^T = B^T A^T
-                const f32x4 AT = prod16<BF16>(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
-                const f32x4 Bm = prod16<BF16>(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
-                const f32x4 IT = prod16<BF16>(Bm, AT);
+                const f32x4 AT = prod16<false>(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
+                const f32x4 Bm = prod16<false>(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
+                const f32x4 IT = prod16<false>(Bm, AT);
                 if constexpr (BF16) {
                     *reinterpret_cast<bf16x8 *>(slot + P::INV + lane * 16) = split_hilo(IT);
                     *reinterpret_cast<bf16x8 *>(slot + P::MQK + lane * 16) = split_hilo(MQ);
@@ -735,7 +743,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             } else {
                 // ---- k^r fragments (from the staging area) and v fragments (from the inputs)
                 constexpr int NKR = (DK / 16) * 64, NVF = (DV / 16) * 64;
-                for (int idx = tid - 64; idx < NKR + NVF; idx += NTHR - 64) {
+                const int ft = wu < PROD_INV_WAVE ? tid : tid - 64;   // threads of the other three waves
+                for (int idx = ft; idx < NKR + NVF; idx += NTHR - 64) {
                     const int l2 = idx & 63, lq2 = l2 >> 4, ln2 = l2 & 15;
                     int src, dst;   // 4 tokens of one channel / column: 4 * ES contiguous bytes
                     if (idx < NKR) {
