@@ -325,13 +325,8 @@ struct PIn {
     typename Elem<BF16>::T b;   // raw bits: converted only where used
 };
 
-// DPP: x of the lane n below in the same 16-lane row (0 past the row start),
-// and lane n of the row broadcast to the row.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
-                                                                 false));
-}
+// DPP (dpp_f of kda_device.hpp): row_shr n gives x of the lane n below in the
+// same 16-lane row (0 past the row start); row_newbcast n broadcasts lane n.
 __device__ __forceinline__ float scan16(float x) {   // inclusive prefix sum over the row's 16 tokens
     x += dpp_f<0x111>(x);
     x += dpp_f<0x112>(x);

@@ -45,12 +45,21 @@ __device__ __forceinline__ float softplus_f(float x) {
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
+// DPP move of x from another lane (CTRL = dpp_ctrl; lanes whose source is
+// outside the 16-lane row read 0).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
+                                                                 false));
+}
+
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), in VALU: quad
+// butterflies, then the mirrored half row, then the mirrored row.
 __device__ __forceinline__ float row16_sum(float x) {
-    x += __shfl_xor(x, 1, 16);
-    x += __shfl_xor(x, 2, 16);
-    x += __shfl_xor(x, 4, 16);
-    x += __shfl_xor(x, 8, 16);
+    x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);   // row_half_mirror
+    x += dpp_f<0x140>(x);   // row_mirror
     return x;
 }
 
