@@ -13,11 +13,16 @@
 // MI355X mapping.  The step is HBM-bound (64 KiB of fp32 state read and
 // written per (row, value head) against ~1 KiB of activations), so the kernel
 // is one streaming pass:
-//   * one 256-thread workgroup per (row, value head); thread (g, j) with
-//     g = tid / 16 and j = tid % 16 owns state rows g, g+16, ... (8 rows) and
-//     columns [4j, 4j+4) u [64+4j, 64+4j+4): every wave-wide float4 access
-//     covers four contiguous 256-byte row halves;
-//   * all 16 float4 state loads of a thread are issued before any arithmetic
+//   * one 512-thread workgroup per (row, value head).  State rows are
+//     independent given k, q and the gate, so each 256-thread half takes 64
+//     of the 128 rows: in half p, thread (g, j) with g = t / 16 and
+//     j = t % 16 (t = tid % 256) owns rows 64p + g + 16r (r < 4) and columns
+//     [4j, 4j+4) u [64+4j, 64+4j+4): every wave-wide float4 access covers
+//     four contiguous 256-byte row halves.  Halving the rows per thread
+//     (72 VGPRs instead of 107) lets 7 waves share a SIMD; keeping both
+//     halves in one workgroup keeps the dispatch count at one per item
+//     (a workgroup per half, or per quarter, measured slower);
+//   * all 8 float4 state loads of a thread are issued before any arithmetic
 //     (64 KiB in flight per workgroup);
 //   * the two row reductions S'k and S'q run over the 16 lanes of one row
 //     group; o uses S q = S' q + u (k . q) so the state is read once;
@@ -28,7 +33,7 @@
 namespace kda {
 
 template <int K_, int V_>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(512) void decode_kernel(
     const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float *__restrict__ pool,
@@ -36,22 +41,48 @@ __global__ __launch_bounds__(256) void decode_kernel(
     float scale, int l2norm)
 {
     static_assert(K_ == 128 && V_ == 128, "decode kernel is built for K = V = 128");
-    constexpr int ROWS = V_ / 16;  // rows per thread
+    constexpr int ROWS = V_ / 32;  // rows per thread
     const int n = blockIdx.x / HV;
     const int hv = blockIdx.x - n * HV;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x & 255;
+    const int r0 = (threadIdx.x >> 8) * (V_ / 2);  // first state row of this half
     const int j = tid & 15;
     const int g = tid >> 4;
+
+    // Activation loads go out before the state loads: vmcnt retires in issue
+    // order, so the gate arithmetic then overlaps the state's latency instead
+    // of waiting behind it.  v is loaded here too, so no load follows the
+    // first state store (vmcnt counts stores as well).
+    const int hq = hv / (HV / H);
+    const size_t D = 2 * (size_t)H * K_ + (size_t)HV * V_;
+    const uint16_t *x = qkv + (size_t)n * D;
+    const int cols[2] = {4 * j, 64 + 4 * j};
+    uint2 qb[2], kb[2], ab[2];
+    f32x4 dt[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        qb[h] = *reinterpret_cast<const uint2 *>(x + (size_t)hq * K_ + cols[h]);
+        kb[h] = *reinterpret_cast<const uint2 *>(x + (size_t)H * K_ + (size_t)hq * K_ + cols[h]);
+        ab[h] = *reinterpret_cast<const uint2 *>(a + ((size_t)n * HV + hv) * K_ + cols[h]);
+        dt[h] = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + cols[h]);
+    }
+    const uint16_t *vrow = x + 2 * (size_t)H * K_ + (size_t)hv * V_ + r0;
+    uint16_t vraw[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) vraw[r] = vrow[g + 16 * r];
+    const uint16_t braw = b[(size_t)n * HV + hv];
+    const float A_l = A_log[hv];
 
     uint16_t *orow = o + ((size_t)n * HV + hv) * V_;
     const int idx = state_idx[n];
     if (idx < 0) {  // pad slot: zero output, no state access
-        if (tid < V_) orow[tid] = 0;
+        if (threadIdx.x < V_) orow[threadIdx.x] = 0;
         return;
     }
 
-    float *S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_);
-    // Issue the state loads first: rows g + 16 r, two float4 per row.
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the state loads
+    float *S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_) + (size_t)r0 * K_;
+    // state rows g + 16 r of this half, two float4 per row
     f32x4 s[ROWS][2];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
@@ -60,19 +91,11 @@ __global__ __launch_bounds__(256) void decode_kernel(
         s[r][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * j));
     }
 
-    const int hq = hv / (HV / H);
-    const size_t D = 2 * (size_t)H * K_ + (size_t)HV * V_;
-    const uint16_t *x = qkv + (size_t)n * D;
-    const int cols[2] = {4 * j, 64 + 4 * j};
     float qv[8], kv[8], eg[8];
-    const float A = expf(A_log[hv]);
+    const float A = __builtin_amdgcn_exp2f(A_l * kLog2e);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint2 qb = *reinterpret_cast<const uint2 *>(x + (size_t)hq * K_ + cols[h]);
-        const uint2 kb = *reinterpret_cast<const uint2 *>(x + (size_t)H * K_ + (size_t)hq * K_ + cols[h]);
-        const uint2 ab = *reinterpret_cast<const uint2 *>(a + ((size_t)n * HV + hv) * K_ + cols[h]);
-        const f32x4 dt = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + cols[h]);
-        const uint32_t qw[2] = {qb.x, qb.y}, kw[2] = {kb.x, kb.y}, aw[2] = {ab.x, ab.y};
+        const uint32_t qw[2] = {qb[h].x, qb[h].y}, kw[2] = {kb[h].x, kb[h].y}, aw[2] = {ab[h].x, ab[h].y};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint16_t qe = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
@@ -80,7 +103,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
             const uint16_t ae = (uint16_t)(aw[e >> 1] >> (16 * (e & 1)));
             qv[4 * h + e] = bf16_to_f32(qe);
             kv[4 * h + e] = bf16_to_f32(ke);
-            eg[4 * h + e] = expf(-A * softplus_f(bf16_to_f32(ae) + dt[e]));
+            eg[4 * h + e] = gate_decay(bf16_to_f32(ae) + dt[h][e], A);
         }
     }
     if (l2norm) {
@@ -97,8 +120,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) { qv[c] *= scale; kq += kv[c] * qv[c]; }
     kq = row16_sum(kq);
-    const float beta = sigmoid_f(bf16_to_f32(b[(size_t)n * HV + hv]));
-    const uint16_t *vrow = x + 2 * (size_t)H * K_ + (size_t)hv * V_;
+    const float beta = sigmoid_f(bf16_to_f32(braw));
 
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
@@ -115,7 +137,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
         pk = row16_sum(pk);
         pq = row16_sum(pq);
         const int row = g + 16 * r;
-        const float u = beta * (bf16_to_f32(vrow[row]) - pk);
+        const float u = beta * (bf16_to_f32(vraw[r]) - pk);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -123,7 +145,7 @@ __global__ __launch_bounds__(256) void decode_kernel(
         float *dst = S + (size_t)row * K_;
         __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
         __builtin_nontemporal_store(s[r][1], reinterpret_cast<f32x4 *>(dst + 64 + 4 * j));
-        if (j == 0) orow[row] = f32_to_bf16(pq + u * kq);
+        if (j == 0) orow[r0 + row] = f32_to_bf16(pq + u * kq);
     }
 }
 
@@ -132,7 +154,7 @@ hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t 
                          const int32_t *state_idx, uint16_t *o, int B, int H, int HV,
                          float scale, int l2norm, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((decode_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(512), 0, stream,
                        qkv, a, b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
     return hipGetLastError();
 }

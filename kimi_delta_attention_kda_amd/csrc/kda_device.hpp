@@ -45,6 +45,16 @@ __device__ __forceinline__ float softplus_f(float x) {
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// e^{-A softplus(z)}, the per-channel decay of the decode gate, written as
+// 2^{-A log2(1 + 2^{z log2 e})} so that it costs two hardware transcendentals
+// (v_exp_f32, v_log_f32) and no branch; above z = 20 softplus(z) is taken as z
+// as in softplus_f.  For z far below zero 1 + e^z rounds to 1 and the decay
+// to 1, an absolute error below 2^-24 A in the exponent.
+__device__ __forceinline__ float gate_decay(float z, float A) {
+    const float l2 = z > 20.0f ? z * kLog2e : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(z * kLog2e));
+    return __builtin_amdgcn_exp2f(-A * l2);
+}
+
 // DPP move of x from another lane (CTRL = dpp_ctrl; lanes whose source is
 // outside the 16-lane row read 0).
 template <int CTRL>
