@@ -142,7 +142,7 @@ __device__ __forceinline__ void lds_done() {      // this wave's LDS ops complet
 //   C (16 x 16): rows 4lq .. 4lq+3 of column ln.
 // bf16: KD/QD fragment s (32 channels): lane 16 B = channels {32s+4lq+i, 32s+16+4lq+i};
 //       KR fragment mt: lane 8 B = k^r[16mt+ln][4lq .. 4lq+3];
-//       INV/MQK: lane 16 B = {hi(X[ln][4lq+i]), lo(X[ln][4lq+i])}.
+//       INV/MQK: lane 8 B = X[ln][4lq .. 4lq+3].
 // f32:  KD/QD fragment mt: lane 16 B = channels 16mt+4lq+i;  KR fragment mt:
 //       lane 16 B = k^r[16mt+ln][4lq+i];  INV/MQK: lane 16 B = X[ln][4lq+i].
 // Both: BETA[16] and EG[dk] fp32; V fragment vt: lane = v[4lq .. 4lq+3][16vt+ln]
@@ -157,8 +157,8 @@ struct PL {
     static constexpr int QD = KD + NF * 64 * 16;
     static constexpr int KR = QD + NF * 64 * 16;
     static constexpr int INV = KR + MT * 64 * KRB;
-    static constexpr int MQK = INV + 64 * 16;
-    static constexpr int BETA = MQK + 64 * 16;
+    static constexpr int MQK = INV + 64 * KRB;
+    static constexpr int BETA = MQK + 64 * KRB;
     static constexpr int EG = BETA + 64;
     static constexpr int V = (EG + DK * 4 + 1023) / 1024 * 1024;   // v (1 KiB aligned): fragment vt,
                                                                    // lane: rows 4lq..4lq+3 of column 16vt+ln
@@ -188,19 +188,8 @@ __device__ __forceinline__ typename Elem<BF16>::T to_elem(float x) {
     else return x;
 }
 
-// bf16 hi/lo split of 4 values into one 8-wide operand [hi0..hi3, lo0..lo3].
-__device__ __forceinline__ bf16x8 split_hilo(f32x4 x) {
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const __bf16 hi = static_cast<__bf16>(x[i]);
-        r[i] = hi;
-        r[4 + i] = static_cast<__bf16>(x[i] - static_cast<float>(hi));
-    }
-    return r;
-}
-// A operand pairing with split_hilo B operands: the row values (hi or lo part)
-// repeated in both K halves.
+// A operand pairing with a [hi | lo] B operand: the row values repeated in
+// both K halves.
 __device__ __forceinline__ bf16x8 dup4(bf16x4 a) {
     bf16x8 r;
 #pragma unroll
@@ -382,30 +371,24 @@ __device__ __forceinline__ void prod_load(PIn<BF16, DK, DV> &in, const Cursor &c
     if (w == PROD_INV_WAVE) in.b = static_cast<const typename Elem<BF16>::T *>(a.beta_raw)[(tok0 + min(lane, last)) * H + h];
 }
 
-// hi/lo bf16 parts of 8 values (two groups of 4).
-struct HL8 {
-    bf16x4 hi0, lo0, hi1, lo1;
-};
-__device__ __forceinline__ HL8 split8(const float (&x)[8]) {
-    HL8 s;
-    hilo4(f32x4{x[0], x[1], x[2], x[3]}, s.hi0, s.lo0);
-    hilo4(f32x4{x[4], x[5], x[6], x[7]}, s.hi1, s.lo1);
-    return s;
+// 8 values as one bf16 MFMA operand (RNE).
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = static_cast<__bf16>(x[i]);
+    return r;
+}
+__device__ __forceinline__ bf16x4 pack4(f32x4 x) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = static_cast<__bf16>(x[i]);
+    return r;
 }
 __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
     bf16x8 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
     return r;
-}
-// acc += X Y^T over the 8 channels of each lane's unit (rows: the tokens of
-// the A-role lanes, columns: the tokens of the B-role lanes), to ~2^-16
-// relative: (Xhi + Xlo) Yhi + Xhi Ylo.
-__device__ __forceinline__ f32x4 contract8(const HL8 &X, const HL8 &Y, f32x4 acc) {
-    acc = mfma_bf16(cat4(X.hi0, X.lo0), cat4(Y.hi0, Y.hi0), acc);
-    acc = mfma_bf16(cat4(X.hi1, X.lo1), cat4(Y.hi1, Y.hi1), acc);
-    acc = mfma_bf16(cat4(X.hi0, X.hi1), cat4(Y.lo0, Y.lo1), acc);
-    return acc;
 }
 __device__ __forceinline__ f32x4 contract4(const float (&X)[4], const float (&Y)[4], f32x4 acc) {
 #pragma unroll
@@ -416,22 +399,11 @@ __device__ __forceinline__ f32x4 contract4(const float (&X)[4], const float (&Y)
 // 16x16x16 product in C layout without any data movement: given XT = C layout
 // of X^T (lane (lq, ln) element i = X[ln][4lq+i], which is the A operand's
 // element) and Y in C layout (the B operand's element), return X Y in C layout.
-template <bool BF16>
 __device__ __forceinline__ f32x4 prod16(f32x4 XT, f32x4 Y) {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF16) {
-        bf16x4 xh, xl, yh, yl;
-        hilo4(XT, xh, xl);
-        hilo4(Y, yh, yl);
-        const bf16x4 zero = {};
-        f32x4 acc = mfma_bf16(cat4(xh, xl), cat4(yh, yh), z);
-        return mfma_bf16(cat4(xh, xh), cat4(yl, zero), acc);
-    } else {
-        f32x4 acc = z;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = mfma_f32(XT[i], Y[i], acc);
-        return acc;
-    }
+    for (int i = 0; i < 4; ++i) acc = mfma_f32(XT[i], Y[i], acc);   // fp32 MFMA, K = 4 per step
+    return acc;
 }
 __device__ __forceinline__ f32x4 plus_eye(f32x4 X, int ln, int lq) {
 #pragma unroll
@@ -636,9 +608,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                         Rq[c] = qf[c] * f;
                     }
                     if constexpr (BF16) {
-                        const HL8 hR = split8(R), hRq = split8(Rq), hC = split8(kr);
-                        pL = contract8(hR, hC, pL);
-                        pMT = contract8(hC, hRq, pMT);
+                        // one MFMA over the wave's 32 channels (k slot e of lane (lq, ln) = channel e of unit lq)
+                        const bf16x8 bC = pack8(kr);
+                        pL = mfma_bf16(pack8(R), bC, pL);
+                        pMT = mfma_bf16(bC, pack8(Rq), pMT);
                     } else {
                         pL = contract4(R, kr, pL);
                         pMT = contract4(kr, Rq, pMT);
@@ -658,8 +631,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                         R[c] = kf[c] * f;
                         Rq[c] = qf[c] * f;
                     }
-                    [[maybe_unused]] HL8 hR, hRq;
-                    if constexpr (BF16) { hR = split8(R); hRq = split8(Rq); }
+                    [[maybe_unused]] bf16x8 bR, bRq;
+                    if constexpr (BF16) { bR = pack8(R); bRq = pack8(Rq); }
 #pragma unroll
                     for (int b = 0; b < 4; ++b) {
                         float C[UC];
@@ -671,9 +644,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                         f32x4 Lb, MTb;
                         if constexpr (BF16) {
-                            const HL8 hC = split8(C);
-                            Lb = contract8(hR, hC, z);
-                            MTb = contract8(hC, hRq, z);
+                            const bf16x8 bC = pack8(C);
+                            Lb = mfma_bf16(bR, bC, z);
+                            MTb = mfma_bf16(bC, bRq, z);
                         } else {
                             Lb = contract4(R, C, z);
                             MTb = contract4(C, Rq, z);
@@ -720,16 +693,16 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 }
                 // fp32 MFMA products: the C-layout operands feed 16x16x4 f32 MFMAs
                 // directly, with no bf16 splitting (the chain is latency bound)
-                const f32x4 L2 = prod16<false>(LT, L), L2T = prod16<false>(L, LT);
-                const f32x4 L4 = prod16<false>(L2T, L2), L4T = prod16<false>(L2, L2T);
-                const f32x4 L8 = prod16<false>(L4T, L4);
+                const f32x4 L2 = prod16(LT, L), L2T = prod16(L, LT);
+                const f32x4 L4 = prod16(L2T, L2), L4T = prod16(L2, L2T);
+                const f32x4 L8 = prod16(L4T, L4);
                 // A^T = ((I + L)(I + L^2))^T,  B = (I + L^4)(I + L^8),  INV^T = B^T A^T
-                const f32x4 AT = prod16<false>(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
-                const f32x4 Bm = prod16<false>(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
-                const f32x4 IT = prod16<false>(Bm, AT);
+                const f32x4 AT = prod16(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
+                const f32x4 Bm = prod16(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
+                const f32x4 IT = prod16(Bm, AT);
                 if constexpr (BF16) {
-                    *reinterpret_cast<bf16x8 *>(slot + P::INV + lane * 16) = split_hilo(IT);
-                    *reinterpret_cast<bf16x8 *>(slot + P::MQK + lane * 16) = split_hilo(MQ);
+                    *reinterpret_cast<bf16x4 *>(slot + P::INV + lane * 8) = pack4(IT);
+                    *reinterpret_cast<bf16x4 *>(slot + P::MQK + lane * 8) = pack4(MQ);
                 } else {
                     *reinterpret_cast<f32x4 *>(slot + P::INV + lane * 16) = IT;
                     *reinterpret_cast<f32x4 *>(slot + P::MQK + lane * 16) = MQ;
@@ -989,21 +962,18 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             // R3: U = INV u ; R4: O = Qs + Mqk U ; R5: S += k^r^T U
             f32x4 U = {0.f, 0.f, 0.f, 0.f}, O;
             if constexpr (BF16) {
-                // INV and Mqk arrive as [hi | lo]; the state-side operand carries
-                // the split instead: [x_hi | x_hi] then [x_lo | 0] gives
-                // (A_hi + A_lo) x_hi + A_hi x_lo.
-                const bf16x8 inv = *reinterpret_cast<const bf16x8 *>(pl + P::INV + lane * 16);
-                const bf16x8 mqk = *reinterpret_cast<const bf16x8 *>(pl + P::MQK + lane * 16);
-                const bf16x4 zero = {};
+                // INV, Mqk and k^r are single bf16 operands, duplicated over both K
+                // halves; u and U ride as [hi | lo], so each product is one MFMA
+                // with the state-side operand at ~2^-16 relative.
+                const bf16x4 inv = *reinterpret_cast<const bf16x4 *>(pl + P::INV + lane * 8);
+                const bf16x4 mqk = *reinterpret_cast<const bf16x4 *>(pl + P::MQK + lane * 8);
                 bf16x4 uh, ul;
                 hilo4(u, uh, ul);
-                U = mfma_bf16(inv, cat4(uh, uh), U);
-                U = mfma_bf16(inv, cat4(ul, zero), U);
+                U = mfma_bf16(dup4(inv), cat4(uh, ul), U);
                 bf16x4 Uh, Ul;
                 hilo4(U, Uh, Ul);
-                O = mfma_bf16(mqk, cat4(Uh, Uh), Qs);
-                O = mfma_bf16(mqk, cat4(Ul, zero), O);
                 const bf16x8 bU = cat4(Uh, Ul);
+                O = mfma_bf16(dup4(mqk), bU, Qs);
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
                     const bf16x4 kr4 = *reinterpret_cast<const bf16x4 *>(pl + P::KR + (mt * 64 + lane) * 8);
