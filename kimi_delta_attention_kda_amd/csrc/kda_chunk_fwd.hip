@@ -58,14 +58,17 @@
 // A chunk in which every channel's total decay is at most 100 in log2 units
 // ("mild") uses one reference at the chunk end:
 //   rows k_i 2^{g_C - g_i} (<= 2^100), columns k^r_j = k_j 2^{g_j - g_C} (<= 1).
-// Other chunks use four 4-token blocks: for rows in block b the reference is
-// the cumulative decay g' at the end of block b-1, with each token's decay
-// clipped at 24 (e^g floored at 2^-24):
-//   rows k_i 2^{g'_ref - g'_i} (<= 1),  columns k_j 2^{g'_j - g'_ref} (<= 2^72
-//   inside block b, <= 1 before it),
-// one MFMA pass per row block.  Pairs whose true decay gap exceeds 24 (log2)
-// are then computed as at most 2^-24 instead of their (smaller) true value,
-// an error below fp32 rounding of the O(1) entries; everything else is exact.
+// Other chunks use row blocks of BR tokens: for rows in block b the reference
+// is the cumulative decay g' at the end of block b-1, with each token's decay
+// clipped at CLIP (e^g floored at 2^-CLIP):
+//   rows k_i 2^{g'_ref - g'_i} (<= 1),  columns k_j 2^{g'_j - g'_ref}
+//   (<= 2^{BR CLIP} inside block b, <= 1 before it),
+// one MFMA pass per row block.  Pairs whose true decay gap exceeds CLIP
+// (log2) are then computed as at most 2^-CLIP instead of their (smaller) true
+// value; everything else is exact.  The fp32 build takes four 4-token blocks
+// with CLIP = 24 (an error below fp32 rounding of the O(1) entries); the bf16
+// build, whose L and Mqk operands are rounded to bf16 (2^-9 relative), takes
+// two 8-token blocks with CLIP = 12.
 // The state-side operands (k~, q~, k^r) and the state decay use the unclipped
 // gates; all their factors are <= 1, so underflow only drops negligible terms.
 #include <type_traits>
@@ -405,6 +408,13 @@ __device__ __forceinline__ f32x4 prod16(f32x4 XT, f32x4 Y) {
     for (int i = 0; i < 4; ++i) acc = mfma_f32(XT[i], Y[i], acc);   // fp32 MFMA, K = 4 per step
     return acc;
 }
+// The same product from single-bf16 operands (upper K half zero): one MFMA.
+__device__ __forceinline__ f32x4 prod16b(f32x4 XT, f32x4 Y) {
+    bf16x8 a = {}, b = {};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = static_cast<__bf16>(XT[i]); b[i] = static_cast<__bf16>(Y[i]); }
+    return mfma_bf16(a, b, f32x4{0.f, 0.f, 0.f, 0.f});
+}
 __device__ __forceinline__ f32x4 plus_eye(f32x4 X, int ln, int lq) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) X[i] += (4 * lq + i == ln) ? 1.f : 0.f;
@@ -454,14 +464,23 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     constexpr int NS = DV / BDV;
     constexpr int NCW = BDV / 16;          // compute waves of a consumer workgroup
     constexpr int MT = DK / 16;
-    constexpr int NP = KDA_PRODUCER_WGS;
+    constexpr int NP = producer_wgs(BDV);
     static_assert(NCW >= 1 && NCW <= 4, "consumer slab of 16..64 columns");
     static_assert(KDA_RING <= 32, "one lane per ring slot when polling; ready and used in their own lines");
 
-    // LDS: producers use their input buffers and scratch, consumers a 3-deep payload buffer.
+    // Consumers copy, per payload, the blocks (1 KiB each) up to v and then their
+    // slab's v blocks only, compactly into one of NBUF LDS buffers of CBUF bytes.
+    constexpr int FB = 64 * 4 * P::ES;            // bytes per v fragment
+    constexpr int VB0 = P::V / 1024;
+    constexpr int NSB = ((BDV / 16) * FB + 1023) / 1024;
+    constexpr int NCB = VB0 + NSB;
+    constexpr int CBUF = NCB * 1024;
+    constexpr int NBUF = 4;                      // compute q, copies of q+1 .. q+3 in flight
+    // LDS: producers use their input buffers and scratch; consumers the payload
+    // buffers, the helper-stored outputs and three 32-byte poll spots.
     constexpr int PROD_BYTES = PG<BF16, DK, DV>::BYTES;
-    constexpr int CONS_BYTES = 3 * ((P::BYTES + 16 * NTHR - 1) / (16 * NTHR)) * 16 * NTHR +
-                               (BDV < 64 ? 2 * (BDV / 16) * 64 * 16 : 0) + 16;   // helper-stored outputs, kshared
+    constexpr int OBUF_BYTES = BDV < 64 ? 2 * (BDV / 16) * 64 * 16 : 0;
+    constexpr int CONS_BYTES = NBUF * CBUF + OBUF_BYTES + 3 * 32;
     constexpr int LDS_BYTES = PROD_BYTES > CONS_BYTES ? PROD_BYTES : CONS_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
@@ -469,12 +488,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     if (role.team < 0) return;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int ln = lane & 15, lq = lane >> 4;
-    // Payload q is copied by all NTHR threads of a consumer, NFT 16-byte pieces
-    // each, into LDS buffer q % 3; a ring slot holds SLOT = PBUF bytes (the tail
-    // past the payload is copied but unused).
-    constexpr int NFT = (P::BYTES + 16 * NTHR - 1) / (16 * NTHR);
-    constexpr int PBUF = NFT * 16 * NTHR;
-    constexpr int SLOT = PBUF;
+    constexpr int SLOT = P::BYTES;               // ring slot (whole 1 KiB blocks)
     static_assert(SLOT <= KDA_RING_SLOT_BYTES, "slot larger than the workspace's");
     unsigned char *ring = args.ring + (size_t)role.team * KDA_RING * SLOT;
     int *ready = args.flags + (size_t)role.team * KDA_TEAM_FLAG_INTS;
@@ -617,16 +631,28 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                         pMT = contract4(kr, Rq, pMT);
                     }
                 } else {
-                    // strong: 4-token row blocks; per-token decay clipped at 2^-24; block b's
-                    // reference is the clipped cumulative decay at the end of block b-1
-                    float Gp[UC], B1[UC], B2[UC], B3[UC], R[UC], Rq[UC];
+                    // strong: row blocks of BR tokens, each token's decay clipped at 2^-CLIP, so that a
+                    // column factor inside its block stays <= 2^(BR CLIP) <= 2^96; block b's reference is
+                    // the clipped cumulative decay at the end of block b-1.  The bf16 build rounds the
+                    // entries to bf16 anyway, so it clips at 2^-12 (two 8-token blocks); fp32 clips at
+                    // 2^-24 (four 4-token blocks).
+                    constexpr int NB = BF16 ? 2 : 4, BR = CH / NB;
+                    constexpr float CLIP = BF16 ? 12.0f : 24.0f;
+                    float Gp[UC], Bf[NB][UC], R[UC], Rq[UC];
 #pragma unroll
                     for (int c = 0; c < UC; ++c) {
-                        Gp[c] = scan16(fmaxf(gv[c], -24.0f));
-                        B1[c] = row_bcast<3>(Gp[c]);
-                        B2[c] = row_bcast<7>(Gp[c]);
-                        B3[c] = row_bcast<11>(Gp[c]);
-                        const float ref = t < 4 ? 0.f : t < 8 ? B1[c] : t < 12 ? B2[c] : B3[c];
+                        Gp[c] = scan16(fmaxf(gv[c], -CLIP));
+                        Bf[0][c] = 0.f;
+                        if constexpr (NB == 2) {
+                            Bf[1][c] = row_bcast<7>(Gp[c]);
+                        } else {
+                            Bf[1][c] = row_bcast<3>(Gp[c]);
+                            Bf[2][c] = row_bcast<7>(Gp[c]);
+                            Bf[3][c] = row_bcast<11>(Gp[c]);
+                        }
+                        float ref = Bf[0][c];
+#pragma unroll
+                        for (int bb = 1; bb < NB; ++bb) ref = t >= BR * bb ? Bf[bb][c] : ref;
                         const float f = __builtin_amdgcn_exp2f(Gp[c] - ref);     // <= 1
                         R[c] = kf[c] * f;
                         Rq[c] = qf[c] * f;
@@ -634,13 +660,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                     [[maybe_unused]] bf16x8 bR, bRq;
                     if constexpr (BF16) { bR = pack8(R); bRq = pack8(Rq); }
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
+                    for (int bb = 0; bb < NB; ++bb) {
                         float C[UC];
 #pragma unroll
-                        for (int c = 0; c < UC; ++c) {
-                            const float ref = b == 0 ? 0.f : b == 1 ? B1[c] : b == 2 ? B2[c] : B3[c];
-                            C[c] = t < 4 * b + 4 ? kf[c] * __builtin_amdgcn_exp2f(ref - Gp[c]) : 0.f;   // <= 2^96
-                        }
+                        for (int c = 0; c < UC; ++c)
+                            C[c] = t < BR * (bb + 1) ? kf[c] * __builtin_amdgcn_exp2f(Bf[bb][c] - Gp[c]) : 0.f;
                         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                         f32x4 Lb, MTb;
                         if constexpr (BF16) {
@@ -651,9 +675,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                             Lb = contract4(R, C, z);
                             MTb = contract4(C, Rq, z);
                         }
-                        // keep the rows (of L and Mqk) that lie in block b
-                        if (r == b) pL = Lb;
-                        if ((t >> 2) == b) pMT = MTb;
+                        // keep the rows (of L and Mqk) that lie in block bb: C-layout rows 4r .. 4r+3
+                        // of L, column t of Mqk^T
+                        if ((4 * r) / BR == bb) pL = Lb;
+                        if (t / BR == bb) pMT = MTb;
                     }
                 }
                 f32x4 *pp = reinterpret_cast<f32x4 *>(lds + G::PART) + (wu * 2) * 64 + lane;
@@ -691,15 +716,17 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                     LT[i] = ln > row ? -bcol * LT[i] : 0.f;       // L[ln][row]
                     MQ[i] = ln >= row ? MQ[i] : 0.f;              // Mqk[ln][row], lower incl. diagonal
                 }
-                // fp32 MFMA products: the C-layout operands feed 16x16x4 f32 MFMAs
-                // directly, with no bf16 splitting (the chain is latency bound)
-                const f32x4 L2 = prod16(LT, L), L2T = prod16(L, LT);
-                const f32x4 L4 = prod16(L2T, L2), L4T = prod16(L2, L2T);
-                const f32x4 L8 = prod16(L4T, L4);
+                // C-layout operands feed the MFMAs directly: fp32 16x16x4 MFMAs for the
+                // fp32 build; single-bf16 products for the bf16 build, whose INV is
+                // rounded to bf16 for the payload anyway
+                auto pr = [](f32x4 XT, f32x4 Y) { return BF16 ? prod16b(XT, Y) : prod16(XT, Y); };
+                const f32x4 L2 = pr(LT, L), L2T = pr(L, LT);
+                const f32x4 L4 = pr(L2T, L2), L4T = pr(L2, L2T);
+                const f32x4 L8 = pr(L4T, L4);
                 // A^T = ((I + L)(I + L^2))^T,  B = (I + L^4)(I + L^8),  INV^T = B^T A^T
-                const f32x4 AT = prod16(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
-                const f32x4 Bm = prod16(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
-                const f32x4 IT = prod16(Bm, AT);
+                const f32x4 AT = pr(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
+                const f32x4 Bm = pr(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
+                const f32x4 IT = pr(Bm, AT);
                 if constexpr (BF16) {
                     *reinterpret_cast<bf16x4 *>(slot + P::INV + lane * 8) = pack4(IT);
                     *reinterpret_cast<bf16x4 *>(slot + P::MQK + lane * 8) = pack4(MQ);
@@ -743,69 +770,71 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     const int v0 = slab * BDV + 16 * (computes ? wu : 0);
     const int vt = v0 >> 4;
     // Helper waves (those beyond the slab's compute waves, if any) poll the
-    // ring, copy the payloads into LDS and store the outputs, so that the
-    // compute waves never wait on memory inside the loop.  Without helpers
-    // every wave does a share.
+    // ring, copy the payloads into LDS and store the outputs while the compute
+    // waves work, so the compute waves issue no memory instructions at all.
+    // (Giving the compute waves a share of the copy after their compute was
+    // measured slower: their memory instructions queue behind the helpers'.)
+    // Without helpers every wave does a share at the top of each step.
     constexpr int NH = 4 - NCW;                   // helper waves
     constexpr int CPW = NH > 0 ? NH : 4;          // copying waves
     const bool copier = NH > 0 ? wu >= NCW : true;
     const int cw = NH > 0 ? wu - NCW : wu;        // index among the copying waves
-    const bool poller = cw == 0;                  // the one wave that polls the ready flags
-    unsigned char *obuf = lds + 3 * PBUF;         // [2][NCW][64 lanes] f32x4 outputs (helpers store them)
-    volatile int *kshared = reinterpret_cast<volatile int *>(lds + 3 * PBUF +
-                                                             (NH > 0 ? 2 * NCW * 64 * 16 : 0));
-    // Copied blocks (1 KiB each): the payload up to v, then this slab's v blocks only.
-    constexpr int FB = 64 * 4 * P::ES;            // bytes per v fragment
-    constexpr int VB0 = P::V / 1024;
-    constexpr int NSB = ((BDV / 16) * FB + 1023) / 1024;
-    constexpr int NCB = VB0 + NSB;
-    const int SB0 = (P::V + slab * (BDV / 16) * FB) / 1024;
+    const int poller = NH > 0 ? NCW : 0;          // the wave that polls the ready flags
+    unsigned char *obuf = lds + NBUF * CBUF;      // [2][NCW][64 lanes] f32x4 outputs (helpers store them)
+    int *pollbuf = reinterpret_cast<int *>(lds + NBUF * CBUF + OBUF_BYTES);   // [3][8] ready flags
+    const int SB0 = (P::V + slab * (BDV / 16) * FB) / 1024;     // first copied v block (global)
     int q_total = 0;
     for (int chain = role.team; chain < n_chains; chain += args.n_teams)
         q_total += (chain_info(args, chain).len + CH - 1) / CH;
 
-    // Ready tracking (poller): chunks <= known are ready.  One poll loads all
-    // RING flags (one lane per slot) and extends `known` over the run of ready
-    // chunks; the poller publishes it in LDS for the other waves.
+    // Ready tracking: chunks <= known are ready (each copying wave keeps its
+    // own `known`).  Every step the first copying wave copies the RING ready
+    // flags into an LDS poll spot with the same LDS DMA as the payloads; the
+    // answer is read two steps later, after that wave's vmcnt wait and a
+    // barrier, from spot (step % 3), so the L2 round trip never stalls a step
+    // and the poll costs one memory instruction per workgroup.  (A
+    // compiler-visible load would also make the compiler wait for the younger
+    // payload copies.)  Only a chunk still not ready by then costs a blocking
+    // poll.  Flags only grow, so an old answer stays true.
     int known = -1;
-    auto ensure_ready = [&](int need) {
+    auto run_from = [&](int f, int need) {   // number of consecutive ready chunks from need
+        const int cj = need + lane;
+        const int fj = __shfl(f, cj % KDA_RING);
+        const unsigned long long ok = __ballot(lane < KDA_RING && fj >= cj + 1);
+        return (int)__builtin_ctzll(~ok);
+    };
+    static_assert(KDA_RING == 8, "the poll copies 8 flags with two lanes");
+    auto poll_issue = [&](int spot) {
+        if (wu == poller && lane < 2) lds_dma16(ready + 4 * lane, lds_addr(pollbuf + 8 * spot));
+    };
+    auto ensure_ready = [&](int need, int spot) {   // spot < 0: no poll answer to read
         if (need <= known) return;
+        if (spot >= 0) {
+            const int run = run_from(lane < KDA_RING ? pollbuf[8 * spot + lane] : 0, need);
+            if (run > 0) { known = need + run - 1; return; }
+        }
         for (long n = 0;; ++n) {
-            const int f = lane < KDA_RING ? ld_flag(&ready[lane]) : 0;
-            const int cj = need + lane;
-            const int fj = __shfl(f, cj % KDA_RING);
-            const unsigned long long ok = __ballot(lane < KDA_RING && fj >= cj + 1);
-            const int run = __builtin_ctzll(~ok);
+            const int run = run_from(lane < KDA_RING ? ld_flag(&ready[lane]) : 0, need);
             if (run > 0) { known = need + run - 1; return; }
             // not ready yet: give up if another wait already did, else wait a little
             if (ld_flag(err) || n > SPIN_LIMIT) { st_flag(err, 1); known = q_total; return; }
             __builtin_amdgcn_s_sleep(2);
         }
     };
-    // The non-polling waves read the published value (LDS; bounded wait).
-    auto await_ready = [&](int need) {
-        if (poller) {
-            ensure_ready(need);
-            if (lane == 0) *kshared = known;
-            return;
-        }
-        for (long n = 0; *kshared < need; ++n) {
-            __builtin_amdgcn_s_sleep(1);
-            if (n > SPIN_LIMIT) { st_flag(err, 1); return; }
-        }
-    };
-    // This wave's share of the copy of payload q into LDS buffer q % 3:
-    // copy blocks j = cw, cw + CPW, ... < NCB (lane i moves bytes 16 i .. 16 i + 15).
+    // This wave's share of the copy of payload q into LDS buffer q % NBUF:
+    // copy blocks j = cw, cw + CPW, ... < NCB (lane i moves bytes 16 i .. 16 i + 15);
+    // block j < VB0 is payload block j, the others this slab's v blocks.
     auto dma = [&](int q) {
         const unsigned char *src = ring + (size_t)(q % KDA_RING) * SLOT + lane * 16;
-        const unsigned dst = lds_addr(lds) + (unsigned)(q % 3) * PBUF;
+        const unsigned dst = lds_addr(lds) + (unsigned)(q % NBUF) * CBUF;
         for (int j = cw; j < NCB; j += CPW) {
             const int b = j < VB0 ? j : SB0 + (j - VB0);
-            lds_dma16(src + b * 1024, dst + b * 1024);
+            lds_dma16(src + b * 1024, dst + j * 1024);
         }
     };
-    // Wait until at most one copy share of this wave is in flight.
-    auto dma_wait_one = [&]() {
+    // Wait until this wave's payload copies of the previous step are the only
+    // vector-memory ops in flight (the number it issued is fixed per wave).
+    auto wait_prev_copies = [&]() {
         constexpr int N0 = (NCB + CPW - 1) / CPW;
         constexpr int N1 = CPW > 1 ? (NCB - 1 + CPW - 1) / CPW : 0;
         constexpr int N2 = CPW > 2 ? (NCB - 2 + CPW - 1) / CPW : 0;
@@ -850,19 +879,39 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     f32x4 Op = {0.f, 0.f, 0.f, 0.f};
     size_t op_tok = 0;
     int op_rem = 0, op_head = 0;
-    const size_t o_row = (size_t)args.H * DV;
     auto flush_o = [&](int q) {     // outputs of chunk q - 1
         if (op_rem > 0) {
             if constexpr (NH == 0) {
+                // 4x4 transpose inside each quad (two DPP butterflies): lane 4c + j then
+                // holds row 4lq + j, columns 4c .. 4c+3 of the tile, stored in one go
+                const int j = ln & 3;
+                f32x4 a, b;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (4 * lq + i < op_rem)
-                        store_act<BF16>(args.o, (op_tok * args.H + op_head) * DV + v0 + ln + (4 * lq + i) * o_row,
-                                        Op[i]);
+                for (int r = 0; r < 4; ++r) {
+                    const float x = dpp_f<0xB1>(Op[r ^ 1]);     // lane j ^ 1
+                    a[r] = ((r ^ j) & 1) == 0 ? Op[r] : x;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = dpp_f<0x4E>(a[r ^ 2]);      // lane j ^ 2
+                    b[r] = ((r ^ j) & 2) == 0 ? a[r] : x;
+                }
+                const int row = 4 * lq + j;
+                if (row < op_rem) {
+                    const size_t at = ((op_tok + row) * args.H + op_head) * DV + v0 + 4 * (ln >> 2);
+                    if constexpr (BF16) {
+                        uint2 v2;
+                        v2.x = pack_bf16x2(b[0], b[1]);
+                        v2.y = pack_bf16x2(b[2], b[3]);
+                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.o) + at) = v2;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = b;
+                    }
+                }
             } else if (!computes) {
                 // lane: row lane / 4 of the tile, columns 4 (lane % 4) .. + 3 (one contiguous store)
                 const int row = lane >> 2, c4 = 4 * (lane & 3);
-                for (int wc = cw; wc < NCW; wc += NH) {
+                for (int wc = wu - NCW; wc < NCW; wc += NH) {   // helper wu - NCW stores tiles wc
                     const float *ot = reinterpret_cast<const float *>(obuf) + (((q - 1) & 1) * NCW + wc) * 256;
                     float x[4];
 #pragma unroll
@@ -897,14 +946,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         }
         const size_t tok0 = ci.bos + (size_t)c * CH;
         const int rem = min(CH, ci.len - c * CH);
-        const bool ahead = q + 2 < q_total;
         if (copier) {
-            if (ahead) await_ready(q + 2);
-            flush_o(q);
-            if (ahead) dma(q + 2);
+            // this wave's share of payload q+1 has landed, and its last poll and output
+            // stores: only its copy of q+2 (issued one step ago, last) may still be in flight
+            if (q + 2 < q_total) wait_prev_copies();
+            else vm_wait<0>();
+            if (q + 3 < q_total) ensure_ready(q + 3, q % 3);   // poll of step q-2 (or the prologue)
+            if (q + 5 < q_total) poll_issue((q + 2) % 3);      // read at step q+2
+            flush_o(q);                   // outputs of chunk q-1
+            if (q + 3 < q_total) dma(q + 3);   // last, so the next step's wait leaves it in flight
         }
         if (computes) {
-            const unsigned char *pl = lds + (q % 3) * PBUF;
+            const unsigned char *pl = lds + (q % NBUF) * CBUF;
+            // v fragment vt of the payload sits in the copied slab blocks, which start at P::V
+            const int voff = P::V + P::V + vt * FB - SB0 * 1024;
             // all of this chunk's LDS operands first: their latency overlaps R1
             using FragK = typename std::conditional<BF16, bf16x8, f32x4>::type;
             constexpr int NF = P::NF;
@@ -920,11 +975,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             const f32x4 beta = *reinterpret_cast<const f32x4 *>(pl + P::BETA + lq * 16);
             f32x4 vv;
             if constexpr (BF16) {
-                const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(pl + P::V + (vt * 64 + lane) * 8);
+                const bf16x4 v4 = *reinterpret_cast<const bf16x4 *>(pl + voff + lane * 8);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) vv[i] = static_cast<float>(v4[i]);
             } else {
-                vv = *reinterpret_cast<const f32x4 *>(pl + P::V + (vt * 64 + lane) * 16);
+                vv = *reinterpret_cast<const f32x4 *>(pl + voff + lane * 16);
             }
             // R1: W = k~ S, Qs = q~ S ; then decay the state in place
             f32x4 W = {0.f, 0.f, 0.f, 0.f}, Qs = {0.f, 0.f, 0.f, 0.f};
@@ -1001,30 +1056,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         op_tok = tok0;
         op_head = ci.head;
         op_rem = rem;
-        if (copier) {
-            if (ahead) dma_wait_one();    // payload q+1 has landed (only q+2 may still fly)
-            else vm_wait<0>();
-        }
-        lds_barrier();
+        lds_barrier();                    // payload q+1 published; buffer q free
         if (q + 1 < q_total && tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[(q + 1) % KDA_RING], 1);
         ++c;
     };
 
     if (q_total > 0) {
-        if (poller) {
-            ensure_ready(0);
-            if (q_total > 1) ensure_ready(1);
-            if (lane == 0) *kshared = known;
-        }
-        lds_barrier();
         if (copier) {
-            dma(0);
-            if (q_total > 1) {
-                dma(1);
-                dma_wait_one();
-            } else {
-                vm_wait<0>();
+            for (int j = 0; j < 3 && j < q_total; ++j) {
+                ensure_ready(j, -1);
+                dma(j);
             }
+            if (q_total > 3) poll_issue(0);   // read at step 0
+            if (q_total > 4) poll_issue(1);   // read at step 1
+            vm_wait<0>();
         }
         lds_barrier();
         if (tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[0], 1);
@@ -1043,7 +1088,7 @@ template <bool BF16, int DK, int DV, int BDV>
 static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
 {
     constexpr int NS = DV / BDV;
-    constexpr int TS = NS + KDA_PRODUCER_WGS;
+    constexpr int TS = NS + producer_wgs(BDV);
     const int n_chains = a.n_seq * a.H;
     if (n_chains == 0) return hipSuccess;
     int dev = 0, n_cu = 0, occ = 0;
@@ -1079,7 +1124,8 @@ static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
 }
 
 // d_v slab width: enough consumer workgroups to cover the device, at most 64
-// columns (4 compute waves) and at least 16.
+// columns (4 compute waves) and at least 16.  Narrower slabs leave helper
+// waves that issue memory work while the compute waves compute.
 static int pick_bdv(int n_chains, int dv)
 {
     int bdv = dv < 64 ? dv : 64;

@@ -5,13 +5,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Chunk-forward team ring: slots per team, bytes per slot, producer
-// workgroups per team, and the largest number of teams one launch uses.
+// Chunk-forward team ring: slots per team, bytes per slot, and the largest
+// number of teams one launch uses.
 #ifndef KDA_RING
 #define KDA_RING 8
 #endif
 #define KDA_RING_SLOT_BYTES 24576   // largest slot; a launch uses its payload's copy size
-#define KDA_PRODUCER_WGS 4
 #define KDA_MAX_TEAMS 256
 // Per-team flag block (ints): ready[KDA_RING] at 0, used[KDA_RING] at 32, so
 // each array has a cache line to itself and no line is shared between teams
@@ -19,6 +18,12 @@
 #define KDA_TEAM_FLAG_INTS 64
 
 namespace kda {
+
+// Producer workgroups per team for a d_v slab of bdv columns.  A 64-column
+// slab has four computing waves per consumer and a team of two consumers for
+// d_v = 128; six producers then keep up with it and a team still fills four
+// compute units in pairs.  Narrower slabs (more consumers) take four.
+constexpr int producer_wgs(int bdv) { return bdv >= 64 ? 6 : 4; }
 
 hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
                          const float *A_log, const float *dt_bias, float *pool,
