@@ -477,10 +477,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     constexpr int CBUF = NCB * 1024;
     constexpr int NBUF = 4;                      // compute q, copies of q+1 .. q+3 in flight
     // LDS: producers use their input buffers and scratch; consumers the payload
-    // buffers, the helper-stored outputs and three 32-byte poll spots.
+    // buffers and three 32-byte poll spots.
     constexpr int PROD_BYTES = PG<BF16, DK, DV>::BYTES;
-    constexpr int OBUF_BYTES = BDV < 64 ? 2 * (BDV / 16) * 64 * 16 : 0;
-    constexpr int CONS_BYTES = NBUF * CBUF + OBUF_BYTES + 3 * 32;
+    constexpr int CONS_BYTES = NBUF * CBUF + 3 * 32;
     constexpr int LDS_BYTES = PROD_BYTES > CONS_BYTES ? PROD_BYTES : CONS_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
@@ -769,19 +768,19 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     const bool computes = wu < NCW;
     const int v0 = slab * BDV + 16 * (computes ? wu : 0);
     const int vt = v0 >> 4;
-    // Helper waves (those beyond the slab's compute waves, if any) poll the
-    // ring, copy the payloads into LDS and store the outputs while the compute
-    // waves work, so the compute waves issue no memory instructions at all.
-    // (Giving the compute waves a share of the copy after their compute was
-    // measured slower: their memory instructions queue behind the helpers'.)
-    // Without helpers every wave does a share at the top of each step.
+    // Helper waves (those beyond the slab's compute waves, if any) copy the
+    // payloads into LDS while the compute waves work; the compute waves store
+    // their own outputs right after their compute and wave 0 issues the ready
+    // poll, so the helpers' step is only the copy.  (Giving the compute waves
+    // a share of the copy as well was measured slower: their copies queue
+    // behind the helpers'.)  Without helpers every wave copies a share, polls
+    // (wave 0) and stores its previous outputs at the top of each step.
     constexpr int NH = 4 - NCW;                   // helper waves
     constexpr int CPW = NH > 0 ? NH : 4;          // copying waves
     const bool copier = NH > 0 ? wu >= NCW : true;
     const int cw = NH > 0 ? wu - NCW : wu;        // index among the copying waves
-    const int poller = NH > 0 ? NCW : 0;          // the wave that polls the ready flags
-    unsigned char *obuf = lds + NBUF * CBUF;      // [2][NCW][64 lanes] f32x4 outputs (helpers store them)
-    int *pollbuf = reinterpret_cast<int *>(lds + NBUF * CBUF + OBUF_BYTES);   // [3][8] ready flags
+    constexpr int poller = 0;                     // the wave that polls the ready flags
+    int *pollbuf = reinterpret_cast<int *>(lds + NBUF * CBUF);   // [3][8] ready flags
     const int SB0 = (P::V + slab * (BDV / 16) * FB) / 1024;     // first copied v block (global)
     int q_total = 0;
     for (int chain = role.team; chain < n_chains; chain += args.n_teams)
@@ -809,8 +808,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     };
     auto ensure_ready = [&](int need, int spot) {   // spot < 0: no poll answer to read
         if (need <= known) return;
-        if (spot >= 0) {
-            const int run = run_from(lane < KDA_RING ? pollbuf[8 * spot + lane] : 0, need);
+        if (spot >= 0) {          // lane i checks chunk need + i in its slot directly
+            const int cj = need + lane;
+            const int fj = lane < KDA_RING ? pollbuf[8 * spot + cj % KDA_RING] : 0;
+            const unsigned long long ok = __ballot(lane < KDA_RING && fj >= cj + 1);
+            const int run = (int)__builtin_ctzll(~ok);
             if (run > 0) { known = need + run - 1; return; }
         }
         for (long n = 0;; ++n) {
@@ -832,18 +834,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             lds_dma16(src + b * 1024, dst + j * 1024);
         }
     };
-    // Wait until this wave's payload copies of the previous step are the only
-    // vector-memory ops in flight (the number it issued is fixed per wave).
-    auto wait_prev_copies = [&]() {
+    // Wait until at most K steps' worth of this wave's payload copies (the
+    // last ones it issued) are in flight; the number a wave issues per step is
+    // fixed per wave.
+    auto wait_copies = [&](auto K) {
+        constexpr int k = decltype(K)::value;
         constexpr int N0 = (NCB + CPW - 1) / CPW;
         constexpr int N1 = CPW > 1 ? (NCB - 1 + CPW - 1) / CPW : 0;
         constexpr int N2 = CPW > 2 ? (NCB - 2 + CPW - 1) / CPW : 0;
         constexpr int N3 = CPW > 3 ? (NCB - 3 + CPW - 1) / CPW : 0;
         switch (cw) {
-        case 0: vm_wait<N0>(); break;
-        case 1: vm_wait<N1>(); break;
-        case 2: vm_wait<N2>(); break;
-        default: vm_wait<N3>(); break;
+        case 0: vm_wait<k * N0>(); break;
+        case 1: vm_wait<k * N1>(); break;
+        case 2: vm_wait<k * N2>(); break;
+        default: vm_wait<k * N3>(); break;
         }
     };
 
@@ -873,69 +877,48 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         vm_wait<0>();   // the state is never a pending load inside the chunk loop
     };
 
-    // Output rows of the previous chunk, stored one step late (older than the
-    // next copy, so they never delay the payload wait).  With helper waves the
-    // compute waves leave them in LDS and the helpers store them.
+    // A compute wave's output tile (Op, C layout, already scaled) for chunk
+    // rows op_tok .. op_tok + op_rem - 1: a 4x4 transpose inside each quad (two
+    // DPP butterflies) leaves lane 4c + j with row 4lq + j, columns 4c .. 4c+3,
+    // so the tile goes out in one store instruction.  Without helpers the
+    // store is deferred to the top of the next step (older than that step's
+    // copy, so it never delays a payload wait).
     f32x4 Op = {0.f, 0.f, 0.f, 0.f};
     size_t op_tok = 0;
     int op_rem = 0, op_head = 0;
-    auto flush_o = [&](int q) {     // outputs of chunk q - 1
-        if (op_rem > 0) {
-            if constexpr (NH == 0) {
-                // 4x4 transpose inside each quad (two DPP butterflies): lane 4c + j then
-                // holds row 4lq + j, columns 4c .. 4c+3 of the tile, stored in one go
-                const int j = ln & 3;
-                f32x4 a, b;
+    auto flush_o = [&]() {
+        if (op_rem > 0 && computes) {
+            const int j = ln & 3;
+            f32x4 a, b;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = dpp_f<0xB1>(Op[r ^ 1]);     // lane j ^ 1
-                    a[r] = ((r ^ j) & 1) == 0 ? Op[r] : x;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float x = dpp_f<0xB1>(Op[r ^ 1]);     // lane j ^ 1
+                a[r] = ((r ^ j) & 1) == 0 ? Op[r] : x;
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float x = dpp_f<0x4E>(a[r ^ 2]);      // lane j ^ 2
-                    b[r] = ((r ^ j) & 2) == 0 ? a[r] : x;
-                }
-                const int row = 4 * lq + j;
-                if (row < op_rem) {
-                    const size_t at = ((op_tok + row) * args.H + op_head) * DV + v0 + 4 * (ln >> 2);
-                    if constexpr (BF16) {
-                        uint2 v2;
-                        v2.x = pack_bf16x2(b[0], b[1]);
-                        v2.y = pack_bf16x2(b[2], b[3]);
-                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.o) + at) = v2;
-                    } else {
-                        *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = b;
-                    }
-                }
-            } else if (!computes) {
-                // lane: row lane / 4 of the tile, columns 4 (lane % 4) .. + 3 (one contiguous store)
-                const int row = lane >> 2, c4 = 4 * (lane & 3);
-                for (int wc = wu - NCW; wc < NCW; wc += NH) {   // helper wu - NCW stores tiles wc
-                    const float *ot = reinterpret_cast<const float *>(obuf) + (((q - 1) & 1) * NCW + wc) * 256;
-                    float x[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] = ot[(16 * (row >> 2) + c4 + j) * 4 + (row & 3)];
-                    if (row < op_rem) {
-                        const size_t at = ((op_tok + row) * args.H + op_head) * DV + slab * BDV + 16 * wc + c4;
-                        if constexpr (BF16) {
-                            uint2 v2;
-                            v2.x = pack_bf16x2(x[0], x[1]);
-                            v2.y = pack_bf16x2(x[2], x[3]);
-                            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.o) + at) = v2;
-                        } else {
-                            *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = f32x4{x[0], x[1], x[2], x[3]};
-                        }
-                    }
+            for (int r = 0; r < 4; ++r) {
+                const float x = dpp_f<0x4E>(a[r ^ 2]);      // lane j ^ 2
+                b[r] = ((r ^ j) & 2) == 0 ? a[r] : x;
+            }
+            const int row = 4 * lq + j;
+            if (row < op_rem) {
+                const size_t at = ((op_tok + row) * args.H + op_head) * DV + v0 + 4 * (ln >> 2);
+                if constexpr (BF16) {
+                    uint2 v2;
+                    v2.x = pack_bf16x2(b[0], b[1]);
+                    v2.y = pack_bf16x2(b[2], b[3]);
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.o) + at) = v2;
+                } else {
+                    *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = b;
                 }
             }
         }
         op_rem = 0;
     };
 
-    // One chunk q, computed from LDS buffer q % 3.  Payload q+2 is requested
-    // at the top; payload q+1 (requested one step earlier) is waited for at
-    // the bottom, before the barrier that publishes it.
+    // One chunk q, computed from LDS buffer q % NBUF.  The copying waves first
+    // wait for their share of payload q+1 (published by this step's closing
+    // barrier) and then request payload q+3.
     auto step = [&](int q) {
         // chain bookkeeping (zero-length chains: h_T = h0)
         while (!started || c >= nch) {
@@ -947,14 +930,24 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         const size_t tok0 = ci.bos + (size_t)c * CH;
         const int rem = min(CH, ci.len - c * CH);
         if (copier) {
-            // this wave's share of payload q+1 has landed, and its last poll and output
-            // stores: only its copy of q+2 (issued one step ago, last) may still be in flight
-            if (q + 2 < q_total) wait_prev_copies();
-            else vm_wait<0>();
+            // Request payload q+3, then wait until this wave's share of payload q+1
+            // (and anything older: its last poll and output stores) has landed;
+            // only its copies of q+2 (one step ago) and q+3 may stay in flight.
             if (q + 3 < q_total) ensure_ready(q + 3, q % 3);   // poll of step q-2 (or the prologue)
-            if (q + 5 < q_total) poll_issue((q + 2) % 3);      // read at step q+2
-            flush_o(q);                   // outputs of chunk q-1
-            if (q + 3 < q_total) dma(q + 3);   // last, so the next step's wait leaves it in flight
+            if constexpr (NH == 0) {
+                if (q + 5 < q_total) poll_issue((q + 2) % 3);  // read at step q+2
+                flush_o();                // outputs of chunk q-1
+            }
+            if (q + 3 < q_total) {
+                dma(q + 3);
+                wait_copies(std::integral_constant<int, 2>());
+            } else if (q + 2 < q_total) {
+                wait_copies(std::integral_constant<int, 1>());
+            } else {
+                vm_wait<0>();
+            }
+        } else {
+            vm_wait<0>();                 // this wave's output store and poll of the last step
         }
         if (computes) {
             const unsigned char *pl = lds + (q % NBUF) * CBUF;
@@ -1051,11 +1044,14 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) Op[i] = args.scale * O[i];
-            if constexpr (NH > 0) reinterpret_cast<f32x4 *>(obuf)[((q & 1) * NCW + wu) * 64 + lane] = Op;
         }
         op_tok = tok0;
         op_head = ci.head;
         op_rem = rem;
+        if constexpr (NH > 0) {
+            flush_o();                    // this chunk's outputs, at once
+            if (q + 5 < q_total) poll_issue((q + 2) % 3);      // read at step q+2
+        }
         lds_barrier();                    // payload q+1 published; buffer q free
         if (q + 1 < q_total && tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[(q + 1) % KDA_RING], 1);
         ++c;
@@ -1067,15 +1063,15 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 ensure_ready(j, -1);
                 dma(j);
             }
-            if (q_total > 3) poll_issue(0);   // read at step 0
-            if (q_total > 4) poll_issue(1);   // read at step 1
-            vm_wait<0>();
         }
+        if (q_total > 3) poll_issue(0);   // read at step 0
+        if (q_total > 4) poll_issue(1);   // read at step 1
+        vm_wait<0>();
         lds_barrier();
         if (tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[0], 1);
     }
     for (int q = 0; q < q_total; ++q) step(q);
-    if (copier) flush_o(q_total);
+    if constexpr (NH == 0) flush_o();    // deferred outputs of the last chunk
     // final state of the last open chain, then any trailing zero-length chains
     if (started) store_hT();
     for (chain = started ? chain + args.n_teams : role.team; chain < n_chains; chain += args.n_teams) {
