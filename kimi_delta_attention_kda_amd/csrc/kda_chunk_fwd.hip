@@ -477,9 +477,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     constexpr int CBUF = NCB * 1024;
     constexpr int NBUF = 4;                      // compute q, copies of q+1 .. q+3 in flight
     // LDS: producers use their input buffers and scratch; consumers the payload
-    // buffers and three 32-byte poll spots.
+    // buffers, the compute waves' output tiles (for the helpers to store) and
+    // three 32-byte poll spots.
     constexpr int PROD_BYTES = PG<BF16, DK, DV>::BYTES;
-    constexpr int CONS_BYTES = NBUF * CBUF + 3 * 32;
+    constexpr int OBUF_BYTES = BDV < 64 ? 2 * (BDV / 16) * 64 * 16 : 0;
+    constexpr int CONS_BYTES = NBUF * CBUF + OBUF_BYTES + 3 * 32;
     constexpr int LDS_BYTES = PROD_BYTES > CONS_BYTES ? PROD_BYTES : CONS_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
@@ -768,19 +770,20 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     const bool computes = wu < NCW;
     const int v0 = slab * BDV + 16 * (computes ? wu : 0);
     const int vt = v0 >> 4;
-    // Helper waves (those beyond the slab's compute waves, if any) copy the
-    // payloads into LDS while the compute waves work; the compute waves store
-    // their own outputs right after their compute and wave 0 issues the ready
-    // poll, so the helpers' step is only the copy.  (Giving the compute waves
-    // a share of the copy as well was measured slower: their copies queue
-    // behind the helpers'.)  Without helpers every wave copies a share, polls
-    // (wave 0) and stores its previous outputs at the top of each step.
+    // Helper waves (those beyond the slab's compute waves, if any) poll the
+    // ring, copy the payloads into LDS and store the outputs (left in LDS by
+    // the compute waves) while the compute waves work, so the compute waves
+    // issue no memory instructions at all.  (Giving the compute waves a share
+    // of the copy, or their own output stores, was measured slower.)  Without
+    // helpers every wave copies a share, polls (wave 0) and stores its
+    // previous outputs at the top of each step.
     constexpr int NH = 4 - NCW;                   // helper waves
     constexpr int CPW = NH > 0 ? NH : 4;          // copying waves
     const bool copier = NH > 0 ? wu >= NCW : true;
     const int cw = NH > 0 ? wu - NCW : wu;        // index among the copying waves
-    constexpr int poller = 0;                     // the wave that polls the ready flags
-    int *pollbuf = reinterpret_cast<int *>(lds + NBUF * CBUF);   // [3][8] ready flags
+    const int poller = NH > 0 ? NCW : 0;          // the wave that polls the ready flags
+    float *obuf = reinterpret_cast<float *>(lds + NBUF * CBUF);   // [2][NCW][64 lanes][4] output tiles
+    int *pollbuf = reinterpret_cast<int *>(lds + NBUF * CBUF + OBUF_BYTES);   // [3][8] ready flags
     const int SB0 = (P::V + slab * (BDV / 16) * FB) / 1024;     // first copied v block (global)
     int q_total = 0;
     for (int chain = role.team; chain < n_chains; chain += args.n_teams)
@@ -878,16 +881,41 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     };
 
     // A compute wave's output tile (Op, C layout, already scaled) for chunk
-    // rows op_tok .. op_tok + op_rem - 1: a 4x4 transpose inside each quad (two
-    // DPP butterflies) leaves lane 4c + j with row 4lq + j, columns 4c .. 4c+3,
-    // so the tile goes out in one store instruction.  Without helpers the
-    // store is deferred to the top of the next step (older than that step's
-    // copy, so it never delays a payload wait).
+    // rows op_tok .. op_tok + op_rem - 1 goes out in one store instruction per
+    // tile, one step late (older than that step's copy, so it never delays a
+    // payload wait): with helpers, a helper reads it from LDS transposed;
+    // without, a 4x4 transpose inside each quad (two DPP butterflies) leaves
+    // lane 4c + j with row 4lq + j, columns 4c .. 4c+3.
     f32x4 Op = {0.f, 0.f, 0.f, 0.f};
     size_t op_tok = 0;
     int op_rem = 0, op_head = 0;
-    auto flush_o = [&]() {
-        if (op_rem > 0 && computes) {
+    auto store_tile = [&](size_t at_col0, int row, const f32x4 &b) {   // 4 columns of one row
+        const size_t at = ((op_tok + row) * args.H + op_head) * DV + at_col0;
+        if constexpr (BF16) {
+            uint2 v2;
+            v2.x = pack_bf16x2(b[0], b[1]);
+            v2.y = pack_bf16x2(b[2], b[3]);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.o) + at) = v2;
+        } else {
+            *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = b;
+        }
+    };
+    auto flush_o = [&](int q) {   // outputs of chunk q - 1
+        if constexpr (NH > 0) {
+            // helper: tile wc of chunk q-1 from LDS, read transposed (lane: row lane/4,
+            // columns 4 (lane % 4) .. + 3) and stored with one instruction
+            const int row = lane >> 2, c4 = 4 * (lane & 3);
+            for (int wc = cw; wc < NCW && op_rem > 0; wc += NH) {
+                const float *ot = obuf + (((q - 1) & 1) * NCW + wc) * 256;
+                f32x4 x;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) x[j] = ot[(16 * (row >> 2) + c4 + j) * 4 + (row & 3)];
+                if (row < op_rem) store_tile(slab * BDV + 16 * wc + c4, row, x);
+            }
+            op_rem = 0;
+            return;
+        }
+        if (op_rem > 0) {
             const int j = ln & 3;
             f32x4 a, b;
 #pragma unroll
@@ -901,17 +929,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 b[r] = ((r ^ j) & 2) == 0 ? a[r] : x;
             }
             const int row = 4 * lq + j;
-            if (row < op_rem) {
-                const size_t at = ((op_tok + row) * args.H + op_head) * DV + v0 + 4 * (ln >> 2);
-                if constexpr (BF16) {
-                    uint2 v2;
-                    v2.x = pack_bf16x2(b[0], b[1]);
-                    v2.y = pack_bf16x2(b[2], b[3]);
-                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(args.o) + at) = v2;
-                } else {
-                    *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = b;
-                }
-            }
+            if (row < op_rem) store_tile(v0 + 4 * (ln >> 2), row, b);
         }
         op_rem = 0;
     };
@@ -934,10 +952,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             // (and anything older: its last poll and output stores) has landed;
             // only its copies of q+2 (one step ago) and q+3 may stay in flight.
             if (q + 3 < q_total) ensure_ready(q + 3, q % 3);   // poll of step q-2 (or the prologue)
-            if constexpr (NH == 0) {
-                if (q + 5 < q_total) poll_issue((q + 2) % 3);  // read at step q+2
-                flush_o();                // outputs of chunk q-1
-            }
+            if (q + 5 < q_total) poll_issue((q + 2) % 3);      // read at step q+2
+            flush_o(q);                   // outputs of chunk q-1
             if (q + 3 < q_total) {
                 dma(q + 3);
                 wait_copies(std::integral_constant<int, 2>());
@@ -946,8 +962,6 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             } else {
                 vm_wait<0>();
             }
-        } else {
-            vm_wait<0>();                 // this wave's output store and poll of the last step
         }
         if (computes) {
             const unsigned char *pl = lds + (q % NBUF) * CBUF;
@@ -1044,14 +1058,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) Op[i] = args.scale * O[i];
+            if constexpr (NH > 0) reinterpret_cast<f32x4 *>(obuf)[((q & 1) * NCW + wu) * 64 + lane] = Op;
         }
         op_tok = tok0;
         op_head = ci.head;
         op_rem = rem;
-        if constexpr (NH > 0) {
-            flush_o();                    // this chunk's outputs, at once
-            if (q + 5 < q_total) poll_issue((q + 2) % 3);      // read at step q+2
-        }
         lds_barrier();                    // payload q+1 published; buffer q free
         if (q + 1 < q_total && tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[(q + 1) % KDA_RING], 1);
         ++c;
@@ -1071,7 +1082,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         if (tid == (NH > 0 ? 64 * NCW : 0)) add_flag(&used[0], 1);
     }
     for (int q = 0; q < q_total; ++q) step(q);
-    if constexpr (NH == 0) flush_o();    // deferred outputs of the last chunk
+    if (copier) flush_o(q_total);        // deferred outputs of the last chunk
     // final state of the last open chain, then any trailing zero-length chains
     if (started) store_hT();
     for (chain = started ? chain + args.n_teams : role.team; chain < n_chains; chain += args.n_teams) {
