@@ -199,6 +199,22 @@ __device__ __forceinline__ bf16x8 dup4(bf16x4 a) {
     for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = a[i]; }
     return r;
 }
+// 4x4 transpose inside each quad of lanes (two DPP butterflies): lane j of the
+// quad gets element j of each quad lane, i.e. out[r] = lane r's x[j].
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int j) {
+    f32x4 a, b;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float y = dpp_f<0xB1>(x[r ^ 1]);     // lane j ^ 1
+        a[r] = ((r ^ j) & 1) == 0 ? x[r] : y;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const float y = dpp_f<0x4E>(a[r ^ 2]);     // lane j ^ 2
+        b[r] = ((r ^ j) & 2) == 0 ? a[r] : y;
+    }
+    return b;
+}
 __device__ __forceinline__ void hilo4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -902,32 +918,41 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     };
     auto flush_o = [&](int q) {   // outputs of chunk q - 1
         if constexpr (NH > 0) {
-            // helper: tile wc of chunk q-1 from LDS, read transposed (lane: row lane/4,
-            // columns 4 (lane % 4) .. + 3) and stored with one instruction
-            const int row = lane >> 2, c4 = 4 * (lane & 3);
-            for (int wc = cw; wc < NCW && op_rem > 0; wc += NH) {
-                const float *ot = obuf + (((q - 1) & 1) * NCW + wc) * 256;
-                f32x4 x;
+            // the last helper stores the slab's block of chunk q-1: lane l writes row l / 4,
+            // slab columns 4 NCW (l % 4) .. + 4 NCW - 1 (one store of 16 rows x BDV columns)
+            if (cw == NH - 1 && op_rem > 0) {
+                const int row = lane >> 2;
+                const f32x4 *ot = reinterpret_cast<const f32x4 *>(obuf) + ((q - 1) & 1) * NCW * 64;
+                f32x4 x[NCW];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x[j] = ot[(16 * (row >> 2) + c4 + j) * 4 + (row & 3)];
-                if (row < op_rem) store_tile(slab * BDV + 16 * wc + c4, row, x);
+                for (int m = 0; m < NCW; ++m) {
+                    const int g = NCW * (lane & 3) + m;          // 4-column group of the slab
+                    x[m] = ot[(g >> 2) * 64 + 4 * row + (g & 3)];
+                }
+                if (row < op_rem) {
+                    const size_t at = ((op_tok + row) * args.H + op_head) * DV + slab * BDV + 4 * NCW * (lane & 3);
+                    if constexpr (BF16) {
+                        uint32_t w[2 * NCW];
+#pragma unroll
+                        for (int m = 0; m < NCW; ++m) {
+                            w[2 * m] = pack_bf16x2(x[m][0], x[m][1]);
+                            w[2 * m + 1] = pack_bf16x2(x[m][2], x[m][3]);
+                        }
+                        uint16_t *dst = static_cast<uint16_t *>(args.o) + at;
+                        if constexpr (NCW == 2) *reinterpret_cast<uint4 *>(dst) = uint4{w[0], w[1], w[2], w[3]};
+                        else *reinterpret_cast<uint2 *>(dst) = uint2{w[0], w[1]};
+                    } else {
+#pragma unroll
+                        for (int m = 0; m < NCW; ++m) reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at)[m] = x[m];
+                    }
+                }
             }
             op_rem = 0;
             return;
         }
         if (op_rem > 0) {
             const int j = ln & 3;
-            f32x4 a, b;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float x = dpp_f<0xB1>(Op[r ^ 1]);     // lane j ^ 1
-                a[r] = ((r ^ j) & 1) == 0 ? Op[r] : x;
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float x = dpp_f<0x4E>(a[r ^ 2]);      // lane j ^ 2
-                b[r] = ((r ^ j) & 2) == 0 ? a[r] : x;
-            }
+            const f32x4 b = quad_transpose(Op, j);
             const int row = 4 * lq + j;
             if (row < op_rem) store_tile(v0 + 4 * (ln >> 2), row, b);
         }
@@ -1058,7 +1083,13 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) Op[i] = args.scale * O[i];
-            if constexpr (NH > 0) reinterpret_cast<f32x4 *>(obuf)[((q & 1) * NCW + wu) * 64 + lane] = Op;
+            if constexpr (NH > 0) {
+                // tile in row-major 4-column groups: entry 4 R + k holds row R, columns
+                // 4k .. 4k+3 (after the quad transpose lane 4c + j holds row 4lq + j,
+                // columns 4c .. 4c+3), so the storing helper reads it without conflicts
+                const f32x4 b = quad_transpose(Op, ln & 3);
+                reinterpret_cast<f32x4 *>(obuf)[((q & 1) * NCW + wu) * 64 + 16 * lq + 4 * (ln & 3) + (ln >> 2)] = b;
+            }
         }
         op_tok = tok0;
         op_head = ci.head;
