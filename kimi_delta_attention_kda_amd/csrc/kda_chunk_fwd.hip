@@ -755,21 +755,31 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             } else {
                 // ---- k^r fragments (from the staging area) and v fragments (from the inputs)
                 constexpr int NKR = (DK / 16) * 64, NVF = (DV / 16) * 64;
+                constexpr int PER = BF16 ? 2 : 1;       // fragment lanes per thread: 16-byte stores
                 const int ft = wu < PROD_INV_WAVE ? tid : tid - 64;   // threads of the other three waves
-                for (int idx = ft; idx < NKR + NVF; idx += NTHR - 64) {
-                    const int l2 = idx & 63, lq2 = l2 >> 4, ln2 = l2 & 15;
-                    int src, dst;   // 4 tokens of one channel / column: 4 * ES contiguous bytes
-                    if (idx < NKR) {
-                        const int mt = idx >> 6;
-                        src = G::KRT + tile_chan<BF16>(mt, ln2 >> 2, ln2 & 3) * G::TP + 4 * lq2 * G::ES;
-                        dst = P::KR + (mt * 64 + l2) * P::KRB;
-                    } else {
-                        const int vt = (idx - NKR) >> 6;
-                        src = G::VT + (16 * vt + ln2) * G::TP + 4 * lq2 * G::ES;
-                        dst = P::V + (vt * 64 + l2) * 4 * G::ES;
+                for (int idx0 = ft * PER; idx0 < NKR + NVF; idx0 += (NTHR - 64) * PER) {
+                    using Piece = typename std::conditional<BF16, uint2, f32x4>::type;
+                    Piece v[PER];
+                    int dst = 0;
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) {
+                        const int idx = idx0 + e;
+                        const int l2 = idx & 63, lq2 = l2 >> 4, ln2 = l2 & 15;
+                        int src;   // 4 tokens of one channel / column: 4 * ES contiguous bytes
+                        if (idx < NKR) {
+                            const int mt = idx >> 6;
+                            src = G::KRT + tile_chan<BF16>(mt, ln2 >> 2, ln2 & 3) * G::TP + 4 * lq2 * G::ES;
+                            if (e == 0) dst = P::KR + (mt * 64 + l2) * P::KRB;
+                        } else {
+                            const int vt = (idx - NKR) >> 6;
+                            src = G::VT + (16 * vt + ln2) * G::TP + 4 * lq2 * G::ES;
+                            if (e == 0) dst = P::V + (vt * 64 + l2) * 4 * G::ES;
+                        }
+                        v[e] = *reinterpret_cast<const Piece *>(lds + src);
                     }
-                    if constexpr (BF16) *reinterpret_cast<uint2 *>(slot + dst) = *reinterpret_cast<const uint2 *>(lds + src);
-                    else *reinterpret_cast<f32x4 *>(slot + dst) = *reinterpret_cast<const f32x4 *>(lds + src);
+                    // consecutive fragment lanes are consecutive in the payload (NKR is even)
+                    if constexpr (BF16) *reinterpret_cast<uint4 *>(slot + dst) = uint4{v[0].x, v[0].y, v[1].x, v[1].y};
+                    else *reinterpret_cast<f32x4 *>(slot + dst) = v[0];
                 }
             }
             stores_done();
