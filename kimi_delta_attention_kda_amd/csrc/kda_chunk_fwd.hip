@@ -496,7 +496,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     // buffers, the compute waves' output tiles (for the helpers to store) and
     // three 32-byte poll spots.
     constexpr int PROD_BYTES = PG<BF16, DK, DV>::BYTES;
-    constexpr int OBUF_BYTES = BDV < 64 ? 2 * (BDV / 16) * 64 * 16 : 0;
+    constexpr int OBUF_BYTES = BDV < 64 ? 2 * 2 * (BDV / 16) * 64 * 16 : 0;   // [step parity][2 chunks][tiles]
     constexpr int CONS_BYTES = NBUF * CBUF + OBUF_BYTES + 3 * 32;
     constexpr int LDS_BYTES = PROD_BYTES > CONS_BYTES ? PROD_BYTES : CONS_BYTES;
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
@@ -808,7 +808,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     const bool copier = NH > 0 ? wu >= NCW : true;
     const int cw = NH > 0 ? wu - NCW : wu;        // index among the copying waves
     const int poller = NH > 0 ? NCW : 0;          // the wave that polls the ready flags
-    float *obuf = reinterpret_cast<float *>(lds + NBUF * CBUF);   // [2][NCW][64 lanes][4] output tiles
+    float *obuf = reinterpret_cast<float *>(lds + NBUF * CBUF);   // [2][2][NCW][64 lanes][4] output tiles
     int *pollbuf = reinterpret_cast<int *>(lds + NBUF * CBUF + OBUF_BYTES);   // [3][8] ready flags
     const int SB0 = (P::V + slab * (BDV / 16) * FB) / 1024;     // first copied v block (global)
     int q_total = 0;
@@ -926,6 +926,37 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             *reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at) = b;
         }
     };
+    // (with helpers) the last helper stores the slab's block of one chunk from LDS
+    // output slot oslot: lane l writes row l / 4, slab columns 4 NCW (l % 4) .. + 4 NCW - 1
+    // (one store of 16 rows x BDV columns)
+    auto store_slot = [&](int oslot, size_t tok, int head, int rem) {
+        if (cw != NH - 1 || rem <= 0) return;
+        const int row = lane >> 2;
+        const f32x4 *ot = reinterpret_cast<const f32x4 *>(obuf) + oslot * NCW * 64;
+        f32x4 x[NCW];
+#pragma unroll
+        for (int m = 0; m < NCW; ++m) {
+            const int g = NCW * (lane & 3) + m;          // 4-column group of the slab
+            x[m] = ot[(g >> 2) * 64 + 4 * row + (g & 3)];
+        }
+        if (row < rem) {
+            const size_t at = ((tok + row) * args.H + head) * DV + slab * BDV + 4 * NCW * (lane & 3);
+            if constexpr (BF16) {
+                uint32_t wv[2 * NCW];
+#pragma unroll
+                for (int m = 0; m < NCW; ++m) {
+                    wv[2 * m] = pack_bf16x2(x[m][0], x[m][1]);
+                    wv[2 * m + 1] = pack_bf16x2(x[m][2], x[m][3]);
+                }
+                uint16_t *dst = static_cast<uint16_t *>(args.o) + at;
+                if constexpr (NCW == 2) *reinterpret_cast<uint4 *>(dst) = uint4{wv[0], wv[1], wv[2], wv[3]};
+                else *reinterpret_cast<uint2 *>(dst) = uint2{wv[0], wv[1]};
+            } else {
+#pragma unroll
+                for (int m = 0; m < NCW; ++m) reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at)[m] = x[m];
+            }
+        }
+    };
     auto flush_o = [&](int q) {   // outputs of chunk q - 1
         if constexpr (NH > 0) {
             // the last helper stores the slab's block of chunk q-1: lane l writes row l / 4,
@@ -969,36 +1000,9 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         op_rem = 0;
     };
 
-    // One chunk q, computed from LDS buffer q % NBUF.  The copying waves first
-    // wait for their share of payload q+1 (published by this step's closing
-    // barrier) and then request payload q+3.
-    auto step = [&](int q) {
-        // chain bookkeeping (zero-length chains: h_T = h0)
-        while (!started || c >= nch) {
-            if (started) { store_hT(); chain += args.n_teams; }
-            started = true;
-            open_chain();
-            if (nch == 0) c = 1;
-        }
-        const size_t tok0 = ci.bos + (size_t)c * CH;
-        const int rem = min(CH, ci.len - c * CH);
-        if (copier) {
-            // Request payload q+3, then wait until this wave's share of payload q+1
-            // (and anything older: its last poll and output stores) has landed;
-            // only its copies of q+2 (one step ago) and q+3 may stay in flight.
-            if (q + 3 < q_total) ensure_ready(q + 3, q % 3);   // poll of step q-2 (or the prologue)
-            if (q + 5 < q_total) poll_issue((q + 2) % 3);      // read at step q+2
-            flush_o(q);                   // outputs of chunk q-1
-            if (q + 3 < q_total) {
-                dma(q + 3);
-                wait_copies(std::integral_constant<int, 2>());
-            } else if (q + 2 < q_total) {
-                wait_copies(std::integral_constant<int, 1>());
-            } else {
-                vm_wait<0>();
-            }
-        }
-        if (computes) {
+    // This compute wave's share of chunk q from its LDS buffer; the output tile
+    // goes to Op (and, with helpers, to LDS output slot oslot).
+    auto compute_chunk = [&](int q, int oslot) {
             const unsigned char *pl = lds + (q % NBUF) * CBUF;
             // v fragment vt of the payload sits in the copied slab blocks, which start at P::V
             const int voff = P::V + P::V + vt * FB - SB0 * 1024;
@@ -1098,9 +1102,86 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 // 4k .. 4k+3 (after the quad transpose lane 4c + j holds row 4lq + j,
                 // columns 4c .. 4c+3), so the storing helper reads it without conflicts
                 const f32x4 b = quad_transpose(Op, ln & 3);
-                reinterpret_cast<f32x4 *>(obuf)[((q & 1) * NCW + wu) * 64 + 16 * lq + 4 * (ln & 3) + (ln >> 2)] = b;
+                reinterpret_cast<f32x4 *>(obuf)[(oslot * NCW + wu) * 64 + 16 * lq + 4 * (ln & 3) + (ln >> 2)] = b;
+            }
+    };
+
+    auto next_chunk = [&]() {   // chain bookkeeping (zero-length chains: h_T = h0)
+        while (!started || c >= nch) {
+            if (started) { store_hT(); chain += args.n_teams; }
+            started = true;
+            open_chain();
+            if (nch == 0) c = 1;
+        }
+    };
+
+    // With helper waves: two chunks per step (one barrier per two chunks).  At
+    // the top of step st the helpers check chunks 2st+2, 2st+3 ready (from the
+    // poll of the previous step), poll, store the previous step's two output
+    // blocks and copy payloads 2st+2, 2st+3 into the buffers of the previous
+    // step's chunks; they wait for the copies before the barrier, while the
+    // compute waves work through chunks 2st, 2st+1.
+    size_t otok[2] = {0, 0};
+    int ohead[2] = {0, 0}, orem[2] = {0, 0};
+    auto step2 = [&](int st) {
+        const int q0 = 2 * st;
+        if (copier) {
+            const int spot = st >= 1 ? ((st - 1) & 1) : -1;
+            for (int e = 0; e < 2; ++e)
+                if (q0 + 2 + e < q_total) ensure_ready(q0 + 2 + e, spot);
+            if (cw == 0 && q0 + 4 < q_total) poll_issue(st & 1);
+            for (int e = 0; e < 2; ++e) store_slot(((st - 1) & 1) * 2 + e, otok[e], ohead[e], orem[e]);
+            for (int e = 0; e < 2; ++e)
+                if (q0 + 2 + e < q_total) dma(q0 + 2 + e);
+            vm_wait<0>();                 // both copies (and the poll and the stores) have landed
+        }
+        for (int e = 0; e < 2; ++e) {
+            orem[e] = 0;
+            if (q0 + e >= q_total) continue;
+            next_chunk();
+            if (computes) compute_chunk(q0 + e, (st & 1) * 2 + e);
+            otok[e] = ci.bos + (size_t)c * CH;
+            ohead[e] = ci.head;
+            orem[e] = min(CH, ci.len - c * CH);
+            ++c;
+        }
+        lds_barrier();                    // payloads 2st+2, 2st+3 published; buffers of 2st, 2st+1 free
+        if (tid == 64 * NCW) {
+            for (int e = 0; e < 2; ++e)
+                if (q0 + 2 + e < q_total) add_flag(&used[(q0 + 2 + e) % KDA_RING], 1);
+        }
+    };
+
+    // One chunk q, computed from LDS buffer q % NBUF.  The copying waves first
+    // wait for their share of payload q+1 (published by this step's closing
+    // barrier) and then request payload q+3.
+    auto step = [&](int q) {
+        // chain bookkeeping (zero-length chains: h_T = h0)
+        while (!started || c >= nch) {
+            if (started) { store_hT(); chain += args.n_teams; }
+            started = true;
+            open_chain();
+            if (nch == 0) c = 1;
+        }
+        const size_t tok0 = ci.bos + (size_t)c * CH;
+        const int rem = min(CH, ci.len - c * CH);
+        if (copier) {
+            // Request payload q+3, then wait until this wave's share of payload q+1
+            // (and anything older: its last poll and output stores) has landed;
+            // only its copies of q+2 (one step ago) and q+3 may stay in flight.
+            if (q + 3 < q_total) ensure_ready(q + 3, q % 3);   // poll of step q-2 (or the prologue)
+            if (q + 5 < q_total) poll_issue((q + 2) % 3);      // read at step q+2
+            flush_o(q);                   // outputs of chunk q-1
+            if (q + 3 < q_total) {
+                dma(q + 3);
+                wait_copies(std::integral_constant<int, 2>());
+            } else if (q + 2 < q_total) {
+                wait_copies(std::integral_constant<int, 1>());
+            } else {
+                vm_wait<0>();
             }
         }
+        if (computes) compute_chunk(q, 0);
         op_tok = tok0;
         op_head = ci.head;
         op_rem = rem;
@@ -1109,6 +1190,25 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         ++c;
     };
 
+    if constexpr (NH > 0) {
+        if (q_total > 0) {
+            if (copier) {
+                for (int j = 0; j < 2 && j < q_total; ++j) {
+                    ensure_ready(j, -1);
+                    dma(j);
+                }
+                vm_wait<0>();
+            }
+            lds_barrier();
+            if (tid == 64 * NCW) {
+                for (int j = 0; j < 2 && j < q_total; ++j) add_flag(&used[j], 1);
+            }
+        }
+        const int nsteps = (q_total + 1) / 2;
+        for (int st = 0; st < nsteps; ++st) step2(st);
+        if (copier && nsteps > 0)
+            for (int e = 0; e < 2; ++e) store_slot(((nsteps - 1) & 1) * 2 + e, otok[e], ohead[e], orem[e]);
+    } else {
     if (q_total > 0) {
         if (copier) {
             for (int j = 0; j < 3 && j < q_total; ++j) {
@@ -1124,6 +1224,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     }
     for (int q = 0; q < q_total; ++q) step(q);
     if (copier) flush_o(q_total);        // deferred outputs of the last chunk
+    }
     // final state of the last open chain, then any trailing zero-length chains
     if (started) store_hT();
     for (chain = started ? chain + args.n_teams : role.team; chain < n_chains; chain += args.n_teams) {
