@@ -128,6 +128,16 @@ __device__ __forceinline__ void vm_wait() {       // at most N vector-memory ops
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
     asm volatile("" ::: "memory");
 }
+// At most n (wave-uniform, 0 .. 4) vector-memory ops of this wave in flight.
+__device__ __forceinline__ void vm_wait_le(int n) {
+    switch (n) {
+    case 4: vm_wait<4>(); break;
+    case 3: vm_wait<3>(); break;
+    case 2: vm_wait<2>(); break;
+    case 1: vm_wait<1>(); break;
+    default: vm_wait<0>(); break;
+    }
+}
 __device__ __forceinline__ unsigned lds_addr(const void *p) {
     return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
@@ -929,8 +939,8 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     // (with helpers) the last helper stores the slab's block of one chunk from LDS
     // output slot oslot: lane l writes row l / 4, slab columns 4 NCW (l % 4) .. + 4 NCW - 1
     // (one store of 16 rows x BDV columns)
-    auto store_slot = [&](int oslot, size_t tok, int head, int rem) {
-        if (cw != NH - 1 || rem <= 0) return;
+    auto store_slot = [&](int oslot, size_t tok, int head, int rem) -> int {   // store instructions issued
+        if (cw != NH - 1 || rem <= 0) return 0;
         const int row = lane >> 2;
         const f32x4 *ot = reinterpret_cast<const f32x4 *>(obuf) + oslot * NCW * 64;
         f32x4 x[NCW];
@@ -956,6 +966,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 for (int m = 0; m < NCW; ++m) reinterpret_cast<f32x4 *>(static_cast<float *>(args.o) + at)[m] = x[m];
             }
         }
+        return BF16 ? 1 : NCW;
     };
     auto flush_o = [&](int q) {   // outputs of chunk q - 1
         if constexpr (NH > 0) {
@@ -1130,10 +1141,12 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
             for (int e = 0; e < 2; ++e)
                 if (q0 + 2 + e < q_total) ensure_ready(q0 + 2 + e, spot);
             if (cw == 0 && q0 + 4 < q_total) poll_issue(st & 1);
-            for (int e = 0; e < 2; ++e) store_slot(((st - 1) & 1) * 2 + e, otok[e], ohead[e], orem[e]);
             for (int e = 0; e < 2; ++e)
                 if (q0 + 2 + e < q_total) dma(q0 + 2 + e);
-            vm_wait<0>();                 // both copies (and the poll and the stores) have landed
+            // the previous step's outputs go last: only they may stay in flight past the wait
+            int nst = 0;
+            for (int e = 0; e < 2; ++e) nst += store_slot(((st - 1) & 1) * 2 + e, otok[e], ohead[e], orem[e]);
+            vm_wait_le(nst);              // both copies and the poll have landed
         }
         for (int e = 0; e < 2; ++e) {
             orem[e] = 0;
