@@ -1,11 +1,13 @@
 /*
  * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
  *
- * Two entry points, both hand-written HIP for CDNA4:
+ * Entry points, all hand-written HIP for CDNA4:
  *
- *   kda_chunk_fwd    chunkwise prefill over dense or packed variable-length
- *                    sequences, returning the outputs and the final states;
- *   kda_decode_step  one fused T=1 decode step over a pool of states.
+ *   kda_chunk_fwd       chunkwise prefill over dense or packed variable-length
+ *                       sequences, returning the outputs and the final states;
+ *   kda_chunk_fwd_pool  the same prefill with the states in a decode state
+ *                       pool (read and updated in place through slot indices);
+ *   kda_decode_step     one fused T=1 decode step over a pool of states.
  *
  * The method ([TL-KDA] section 1): per (sequence, head), with the state S
  * stored as (d_v, d_k),
@@ -30,7 +32,7 @@
  *   - The calls enqueue work on `stream` and return without synchronising;
  *     results are ready once the caller synchronises the stream.  A kernel
  *     fault surfaces at that synchronisation.
- *   - kda_decode_step allocates nothing.  kda_chunk_fwd uses a device
+ *   - kda_decode_step allocates nothing.  kda_chunk_fwd(_pool) uses a device
  *     workspace (ring buffers and flags for its producer/consumer teams,
  *     about 64 MiB) that the library allocates on the first call on each
  *     device and keeps until the process exits; calls that overlap in time
@@ -110,6 +112,35 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v,
                   void *o, float *h_T,
                   int B, int T, int H, int dk, int dv, int n_seq,
                   float scale, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_pool -- the prefill of kda_chunk_fwd with the states kept in a
+ * decode state pool instead of dense h0 / h_T arrays, so that a prefill (or an
+ * extend of a running sequence) and the decode steps of kda_decode_step share
+ * one state store ([SGL-PR]: the packed decode addresses its states through
+ * the pool indices, a negative index marking a pad slot).
+ *
+ * Sequence s starts from state_pool[state_idx[s]] and its final state is
+ * written back to that slot in place; state_idx[s] < 0 starts from the zero
+ * state and keeps no final state.  Everything else (layouts, chunk, head
+ * dims, dtype, cu_seqlens, scale) is as for kda_chunk_fwd.
+ *
+ *   state_pool : [P, H, dv, dk] float32 -- the layout of kda_decode_step's
+ *                pool with HV = H, V = dv, K = dk; read and updated in place.
+ *   state_idx  : [n_seq] int32 slot per sequence (device memory).  Live
+ *                entries must be distinct and < P (duplicates race; not
+ *                checked on the host because the indices live in device
+ *                memory).
+ * Returns KDA_OK or a negative kda_status (KDA_ERR_SHAPE for P <= 0,
+ * KDA_ERR_NULL for a missing pool or index array).
+ */
+int kda_chunk_fwd_pool(const void *q, const void *k, const void *v,
+                       const void *g_raw, const void *beta_raw,
+                       const float *A_log, const float *dt_bias,
+                       float *state_pool, const int32_t *state_idx,
+                       const int32_t *cu_seqlens, int chunk, void *o,
+                       int B, int T, int H, int dk, int dv, int n_seq, int P,
+                       float scale, kda_dtype dtype, hipStream_t stream);
 
 /*
  * kda_decode_step -- fused T=1 KDA decode over a state pool ([SGL-PR],

@@ -19,7 +19,8 @@ _lib = None
 KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_check", "kda_decode_step", "kda_status_str")
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_check", "kda_decode_step",
+           "kda_status_str")
 
 
 class KDAError(RuntimeError):
@@ -38,6 +39,8 @@ def load_library(path: str = LIB_PATH):
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, F, I, P]
     lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd_pool.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P]
+    lib.kda_chunk_fwd_pool.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.kda_decode_step.restype = I
     lib.kda_chunk_fwd_check.argtypes = [P]
@@ -107,6 +110,49 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None
         _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), B, T, H, dk, dv, n_seq,
         float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
     return o, h_T
+
+
+def chunk_fwd_pool(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_idx,
+                   cu_seqlens=None, chunk: int = 16, scale=None, o=None, stream=None):
+    """Chunkwise KDA prefill with the states in a decode state pool.
+
+    As chunk_fwd, but sequence s starts from state_pool[state_idx[s]] and its
+    final state is written back there in place (state_idx[s] < 0: zero start,
+    final state dropped).  state_pool: [P, H, dv, dk] float32 (the layout of
+    decode_step's pool); state_idx: [N] int32 with distinct live entries.
+    Returns o [B, T, H, dv]."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    act = q.dtype
+    if act not in (torch.float32, torch.bfloat16):
+        raise KDAError("activations must be float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw)):
+        _dev(name, t, act)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("state_pool", state_pool)):
+        _dev(name, t, torch.float32)
+    _dev("state_idx", state_idx, torch.int32)
+    _dev("cu_seqlens", cu_seqlens, torch.int32)
+    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or tuple(beta_raw.shape) != (B, T, H):
+        raise KDAError("inconsistent activation shapes")
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, dv, dk):
+        raise KDAError("state_pool must be [P, H, dv, dk]")
+    if state_idx.numel() != n_seq:
+        raise KDAError("state_idx must hold one slot per sequence")
+    if scale is None:
+        scale = dk ** -0.5
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=act, device=q.device)
+    _dev("o", o, act)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(load_library().kda_chunk_fwd_pool(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
+        _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), chunk, _ptr(o), B, T, H, dk, dv, n_seq,
+        state_pool.shape[0], float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32,
+        ctypes.c_void_p(stream)))
+    return o
 
 
 def chunk_fwd_check(stream=None):

@@ -51,11 +51,13 @@ const char *kda_status_str(int status)
     }
 }
 
-int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw,
-                  const void *beta_raw, const float *A_log, const float *dt_bias,
-                  const float *h0, const int32_t *cu_seqlens, int chunk, void *o, float *h_T,
-                  int B, int T, int H, int dk, int dv, int n_seq, float scale,
-                  kda_dtype dtype, hipStream_t stream)
+// Shared body of kda_chunk_fwd and kda_chunk_fwd_pool (state_idx: NULL for the
+// dense-state form; then h0 / h_T rows are sequences).
+static int chunk_fwd_impl(const void *q, const void *k, const void *v, const void *g_raw,
+                          const void *beta_raw, const float *A_log, const float *dt_bias,
+                          const float *h0, const int32_t *state_idx, const int32_t *cu_seqlens,
+                          int chunk, void *o, float *h_T, int B, int T, int H, int dk, int dv,
+                          int n_seq, float scale, kda_dtype dtype, hipStream_t stream)
 {
     if (chunk != 16) return KDA_ERR_UNSUPPORTED;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -72,7 +74,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw
     if ((long long)n_seq * H * 2 > 0x7fffffffLL) return KDA_ERR_SHAPE;
     if (!A_log || !dt_bias) return KDA_ERR_NULL;
     if (n_seq > 0 && tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !o)) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, cu_seqlens};
+    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, cu_seqlens, state_idx};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
     if (n_seq == 0) return KDA_OK;
@@ -85,11 +87,36 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw
     a.err = a.flags + (size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS;
     a.n_teams = 0;
     a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
-    a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.cu_seqlens = cu_seqlens;
+    a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.state_idx = state_idx; a.cu_seqlens = cu_seqlens;
     a.o = o; a.h_T = h_T; a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
     const hipError_t e = kda::launch_chunk_fwd(a, dtype == KDA_BF16 ? 1 : 0, dk, dv, stream);
     if (e == hipErrorInvalidValue) return KDA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw,
+                  const void *beta_raw, const float *A_log, const float *dt_bias,
+                  const float *h0, const int32_t *cu_seqlens, int chunk, void *o, float *h_T,
+                  int B, int T, int H, int dk, int dv, int n_seq, float scale,
+                  kda_dtype dtype, hipStream_t stream)
+{
+    return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
+                          h_T, B, T, H, dk, dv, n_seq, scale, dtype, stream);
+}
+
+int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *g_raw,
+                       const void *beta_raw, const float *A_log, const float *dt_bias,
+                       float *state_pool, const int32_t *state_idx, const int32_t *cu_seqlens,
+                       int chunk, void *o, int B, int T, int H, int dk, int dv, int n_seq, int P,
+                       float scale, kda_dtype dtype, hipStream_t stream)
+{
+    if (P <= 0) return KDA_ERR_SHAPE;
+    if (n_seq > 0 && (!state_pool || !state_idx)) return KDA_ERR_NULL;
+    if ((long long)P * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    // the slots double as h0 (read when a sequence starts) and h_T (written when it
+    // ends); each (sequence, head, slab) is read and written by the same workgroup
+    return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_idx, cu_seqlens,
+                          chunk, o, state_pool, B, T, H, dk, dv, n_seq, scale, dtype, stream);
 }
 
 int kda_chunk_fwd_check(hipStream_t stream)

@@ -894,9 +894,10 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     ChainInfo ci{};
     f32x4 S[MT];
     size_t hbase = 0;
+    int hrow = 0;
     bool started = false;
     auto store_hT = [&]() {
-        if (computes && args.h_T) {
+        if (computes && args.h_T && hrow >= 0) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
                 *reinterpret_cast<f32x4 *>(args.h_T + hbase + tile_chan<BF16>(mt, lq, 0)) = S[mt];
@@ -906,10 +907,13 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         ci = chain_info(args, chain);
         nch = (ci.len + CH - 1) / CH;
         c = 0;
-        hbase = (((size_t)ci.seq * args.H + ci.head) * DV + v0 + ln) * DK;
+        // state row of this sequence: its index, or (pool-addressed) its slot; a
+        // negative slot starts from zero and keeps no final state
+        hrow = args.state_idx ? args.state_idx[ci.seq] : ci.seq;
+        hbase = (((size_t)(hrow < 0 ? 0 : hrow) * args.H + ci.head) * DV + v0 + ln) * DK;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            if (args.h0 && computes)
+            if (args.h0 && computes && hrow >= 0)
                 S[mt] = *reinterpret_cast<const f32x4 *>(args.h0 + hbase + tile_chan<BF16>(mt, lq, 0));
             else S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }

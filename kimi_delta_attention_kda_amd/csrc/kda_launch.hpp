@@ -33,6 +33,7 @@ hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t 
 struct ChunkArgs {
     const void *q, *k, *v, *g_raw, *beta_raw;
     const float *A_log, *dt_bias, *h0;
+    const int32_t *state_idx;   // NULL: h0 / h_T row = sequence; else row = state_idx[sequence] (< 0: none)
     const int32_t *cu_seqlens;
     void *o;
     float *h_T;

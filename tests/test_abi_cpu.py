@@ -68,6 +68,27 @@ def test_chunk_validation(lib):
     assert chunk(lib, n_seq=0, B=0) == 0            # nothing to do, no launch
 
 
+def chunk_pool(lib, **kw):
+    args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, pool=A, idx=B, cu=None, chunk=16, o=A,
+                B=1, T=16, H=1, dk=128, dv=128, n_seq=1, P=4, scale=0.1, dtype=1)
+    args.update(kw)
+    return lib.kda_chunk_fwd_pool(args["q"], args["k"], args["v"], args["g"], args["b"],
+                                  args["A_log"], args["dt"], args["pool"], args["idx"], args["cu"],
+                                  args["chunk"], args["o"], args["B"], args["T"], args["H"],
+                                  args["dk"], args["dv"], args["n_seq"], args["P"], args["scale"],
+                                  args["dtype"], None)
+
+
+def test_chunk_pool_validation(lib):
+    assert chunk_pool(lib, P=0) == -2
+    assert chunk_pool(lib, pool=None) == -1
+    assert chunk_pool(lib, idx=None) == -1
+    assert chunk_pool(lib, idx=MIS) == -4
+    assert chunk_pool(lib, chunk=8) == -3
+    assert chunk_pool(lib, n_seq=2) == -2            # dense input needs n_seq == B
+    assert chunk_pool(lib, n_seq=0, B=0) == 0        # nothing to do, no launch
+
+
 def decode(lib, **kw):
     args = dict(qkv=A, a=A, b=A, A_log=B, dt=B, pool=A, idx=A, o=A, B=4, H=2, HV=4, K=128,
                 V=128, P=8, scale=0.1, flags=1)
