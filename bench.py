@@ -211,26 +211,50 @@ def main():
         decode_call()
     torch.cuda.synchronize()
 
-    # ---------------- timed region: K steps, events on the launch stream
+    # ---------------- timed region: K steps, events on the launch stream.  The K
+    # prefills run back to back, then the K decode steps (a decode loop, as in
+    # serving); each step is one prefill plus one decode step.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    evp_ = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    evd_ = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     host_dec = 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    evp_[0].record()
     for s in range(K):
-        ev[s][0].record()
         prefill_call()
-        ev[s][1].record()
+        evp_[s + 1].record()
+    evd_[0].record()
+    for s in range(K):
         th = time.perf_counter()
         decode_call()
         host_dec += time.perf_counter() - th
-        ev[s][2].record()
+        evd_[s + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]
-    dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]
+    pre_ms = [evp_[s].elapsed_time(evp_[s + 1]) for s in range(K)]
+    dec_ms = [evd_[s].elapsed_time(evd_[s + 1]) for s in range(K)]
     pre_avg = float(np.mean(pre_ms)) * 1e-3
     dec_avg = float(np.mean(dec_ms)) * 1e-3
+
+    # the pool-addressed prefill on the same workload (states in a pool of 2 N slots,
+    # sequence s in slot 2 s), timed the same way outside the step
+    ppool = torch.zeros((2 * p.n_seq, p.H, p.dv, p.dk), dtype=torch.float32, device=dev)
+    pidx = torch.arange(0, 2 * p.n_seq, 2, dtype=torch.int32, device=dev)
+    pin_pool = {k_: v_ for k_, v_ in pin.items() if k_ != "h0"}
+
+    def prefill_pool_call():
+        kda.chunk_fwd_pool(**pin_pool, state_pool=ppool, state_idx=pidx, scale=p.scale, o=o)
+
+    for _ in range(2):
+        prefill_pool_call()
+    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    for s_ in range(K):
+        evp[s_][0].record()
+        prefill_pool_call()
+        evp[s_][1].record()
+    torch.cuda.synchronize()
+    pool_avg = float(np.mean([evp[s_][0].elapsed_time(evp[s_][1]) for s_ in range(K)])) * 1e-3
 
     tokheads = p.tokens * p.H
     flops = tokheads * prefill_flops_per_tokhead(p.dk, p.dv)
@@ -279,6 +303,7 @@ def main():
         "prefill_us": round(pre_avg * 1e6, 2),
         "prefill_tflops": round(flops / pre_avg / 1e12, 2),
         "prefill_mfma_frac": round(flops / pre_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "prefill_pool_us": round(pool_avg * 1e6, 2),
         "decode_us": round(dec_avg * 1e6, 2),
         "decode_host_us_per_call": round(host_dec / K * 1e6, 2),
         "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
