@@ -13,7 +13,9 @@ reported next to it.  Device times come from HIP events recorded on the
 stream the kernels run on.  `roofline` describes the prefill kernel against
 MI355X's HBM peak, `roofline_decode` the decode kernel.  `cpu_baseline` is the
 fp64 oracle (plain C, OpenMP over chains) timed on the host cores on the same
-prefill workload.
+prefill workload.  Outside the step, the pool-addressed prefill (same
+workload) and kda_decode_extend with T = 4 tokens per row (decode workload's
+rows, heads and pool) are timed the same way and reported as extra fields.
 """
 from __future__ import annotations
 
@@ -55,6 +57,20 @@ def decode_bytes(d):
     out = 2 * d.B * d.HV * d.V
     par = 4 * d.HV + 4 * d.HV * d.K + 4 * d.B
     return state + act + out + par
+
+
+def extend_bytes(d, T):
+    """decode_bytes with T tokens' activations and outputs per row (the state
+    is still read and written once)."""
+    live = int((d.state_idx >= 0).sum())
+    state = 2 * 4 * d.V * d.K * live * d.HV
+    act = T * (2 * d.B * (2 * d.H * d.K + d.HV * d.V) + 2 * d.B * d.HV * d.K + 2 * d.B * d.HV)
+    out = T * 2 * d.B * d.HV * d.V
+    par = 4 * d.HV + 4 * d.HV * d.K + 4 * d.B
+    return state + act + out + par
+
+
+EXTEND_T = 4
 
 
 def source_hash(files):
@@ -256,6 +272,32 @@ def main():
     torch.cuda.synchronize()
     pool_avg = float(np.mean([evp[s_][0].elapsed_time(evp[s_][1]) for s_ in range(K)])) * 1e-3
 
+    # T = 4 tokens per row through kda_decode_extend (speculative-verify shape) on
+    # the decode workload's rows, heads and pool, timed the same way
+    de = synth.extend(4, T=EXTEND_T, **{k_: v_ for k_, v_ in synth.DECODE_WORKLOAD.items() if k_ != "name"})
+    dein = dict(qkv=bf16(de.qkv), a=bf16(de.a), b=bf16(de.b), A_log=torch.from_numpy(de.A_log).to(dev),
+                dt_bias=torch.from_numpy(de.dt_bias).to(dev))
+    epool = torch.from_numpy(de.pool).to(dev)
+    eidx = torch.from_numpy(de.state_idx).to(dev)
+    oe = torch.empty((de.B, EXTEND_T, de.HV, de.V), dtype=torch.bfloat16, device=dev)
+
+    def extend_call():
+        kda.decode_extend(**dein, state_pool=epool, state_idx=eidx, num_heads=de.H,
+                          num_v_heads=de.HV, scale=de.scale, o=oe)
+
+    for _ in range(2):
+        extend_call()
+    eve = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    eve[0].record()
+    for s_ in range(K):
+        extend_call()
+        eve[s_ + 1].record()
+    torch.cuda.synchronize()
+    ext_avg = float(np.mean([eve[s_].elapsed_time(eve[s_ + 1]) for s_ in range(K)])) * 1e-3
+    ext_gbs = extend_bytes(de, EXTEND_T) / ext_avg / 1e9
+    del epool
+
     tokheads = p.tokens * p.H
     flops = tokheads * prefill_flops_per_tokhead(p.dk, p.dv)
     pbytes = prefill_bytes(p)
@@ -306,6 +348,10 @@ def main():
         "prefill_pool_us": round(pool_avg * 1e6, 2),
         "decode_us": round(dec_avg * 1e6, 2),
         "decode_host_us_per_call": round(host_dec / K * 1e6, 2),
+        "extend_T": EXTEND_T,
+        "extend_us": round(ext_avg * 1e6, 2),
+        "extend_gbs": round(ext_gbs, 1),
+        "extend_hbm_frac": round(ext_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "chunk_fwd_kernel<bf16,128,128>",

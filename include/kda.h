@@ -7,7 +7,9 @@
  *                       sequences, returning the outputs and the final states;
  *   kda_chunk_fwd_pool  the same prefill with the states in a decode state
  *                       pool (read and updated in place through slot indices);
- *   kda_decode_step     one fused T=1 decode step over a pool of states.
+ *   kda_decode_step     one fused T=1 decode step over a pool of states;
+ *   kda_decode_extend   T tokens per row applied to the pool states in one
+ *                       launch (short extends, speculative verification).
  *
  * The method ([TL-KDA] section 1): per (sequence, head), with the state S
  * stored as (d_v, d_k),
@@ -32,7 +34,7 @@
  *   - The calls enqueue work on `stream` and return without synchronising;
  *     results are ready once the caller synchronises the stream.  A kernel
  *     fault surfaces at that synchronisation.
- *   - kda_decode_step allocates nothing.  kda_chunk_fwd(_pool) uses a device
+ *   - kda_decode_step and kda_decode_extend allocate nothing.  kda_chunk_fwd(_pool) uses a device
  *     workspace (ring buffers and flags for its producer/consumer teams,
  *     about 64 MiB) that the library allocates on the first call on each
  *     device and keeps until the process exits; calls that overlap in time
@@ -174,6 +176,35 @@ int kda_decode_step(const void *qkv, const void *a, const void *b,
                     float scale, int flags, hipStream_t stream);
 
 #define KDA_DECODE_L2NORM 1
+
+/*
+ * kda_decode_extend -- T tokens per row through the same update as
+ * kda_decode_step, in token order, in one launch: the fused recurrent form
+ * with a token loop that [SGL-PR] (section "实现拆解" and the review notes)
+ * gives for extends and speculative (EAGLE) verification, which do not go
+ * through the T=1 packed decode.  Each live slot is read once, carried
+ * through the T tokens and written once, holding the state after token T-1.
+ * With T = 1 the results are bitwise those of kda_decode_step.
+ *
+ * Layout (token t of row n is entry n*T + t of the token axis):
+ *   qkv        : [B, T, 2*H*K + HV*V] bf16
+ *   a          : [B, T, HV*K] bf16      b : [B, T, HV] bf16
+ *   A_log      : [HV] float32           dt_bias : [HV*K] float32
+ *   state_pool : [P, HV, V, K] float32, updated in place
+ *   state_idx  : [B] int32 slot per row; < 0 marks a pad row (all T outputs
+ *                zero, no state access).  Live entries must be distinct and
+ *                < P (not checked on the host: device memory).
+ *   o          : [B, T, HV, V] bf16; o[n, t] is read from the state after
+ *                token t.
+ *   K, V       : 128 each.  HV % H == 0.  T >= 0 (T == 0 launches nothing).
+ *   flags      : bit 0 set = L2-normalise q and k in the kernel.
+ * Returns KDA_OK or a negative kda_status.
+ */
+int kda_decode_extend(const void *qkv, const void *a, const void *b,
+                      const float *A_log, const float *dt_bias,
+                      float *state_pool, const int32_t *state_idx, void *o,
+                      int B, int T, int H, int HV, int K, int V, int P,
+                      float scale, int flags, hipStream_t stream);
 
 /*
  * kda_chunk_fwd_check -- synchronise `stream` and report whether the last

@@ -20,7 +20,7 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_check", "kda_decode_step",
-           "kda_status_str")
+           "kda_decode_extend", "kda_status_str")
 
 
 class KDAError(RuntimeError):
@@ -43,6 +43,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_pool.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.kda_decode_step.restype = I
+    lib.kda_decode_extend.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.kda_decode_extend.restype = I
     lib.kda_chunk_fwd_check.argtypes = [P]
     lib.kda_chunk_fwd_check.restype = I
     lib.kda_status_str.argtypes = [I]
@@ -178,17 +180,57 @@ def decode_step(qkv, a, b, A_log, dt_bias, state_pool, state_idx, num_heads: int
         _dev(name, t, torch.float32)
     _dev("state_idx", state_idx, torch.int32)
     if qkv.shape[-1] != 2 * H * K + HV * V or a.numel() != B * HV * K or b.numel() != B * HV \
-            or tuple(state_pool.shape[1:]) != (HV, V, K) or state_idx.numel() != B:
+            or tuple(state_pool.shape[1:]) != (HV, V, K) or state_idx.numel() != B \
+            or A_log.numel() != HV or dt_bias.numel() != HV * K:
         raise KDAError("inconsistent decode shapes")
     if scale is None:
         scale = K ** -0.5
     if o is None:
         o = torch.empty((B, HV, V), dtype=torch.bfloat16, device=qkv.device)
     _dev("o", o, torch.bfloat16)
+    if o.numel() != B * HV * V:
+        raise KDAError("o must hold [B, HV, V] elements")
     if stream is None:
         stream = torch.cuda.current_stream(qkv.device).cuda_stream
     _check(load_library().kda_decode_step(
         _ptr(qkv), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool),
         _ptr(state_idx), _ptr(o), B, H, HV, K, V, state_pool.shape[0], float(scale),
+        KDA_DECODE_L2NORM if l2norm else 0, ctypes.c_void_p(stream)))
+    return o
+
+
+def decode_extend(qkv, a, b, A_log, dt_bias, state_pool, state_idx, num_heads: int,
+                  num_v_heads: int, head_k_dim: int = 128, head_v_dim: int = 128, scale=None,
+                  l2norm: bool = True, o=None, stream=None):
+    """T tokens per row through the decode update in one launch; `state_pool`
+    [P, HV, V, K] float32 is updated in place and ends holding each live row's
+    state after its last token.  qkv: [B, T, 2*H*K + HV*V] bf16; a: [B, T, HV*K]
+    bf16; b: [B, T, HV] bf16; A_log: [HV] f32; dt_bias: [HV*K] f32; state_idx:
+    [B] int32 (< 0 = pad).  Returns o [B, T, HV, V] bf16."""
+    if qkv.dim() != 3:
+        raise KDAError("qkv must be [B, T, 2*H*K + HV*V]")
+    B, T = qkv.shape[0], qkv.shape[1]
+    H, HV, K, V = num_heads, num_v_heads, head_k_dim, head_v_dim
+    for name, t in (("qkv", qkv), ("a", a), ("b", b)):
+        _dev(name, t, torch.bfloat16)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("state_pool", state_pool)):
+        _dev(name, t, torch.float32)
+    _dev("state_idx", state_idx, torch.int32)
+    if qkv.shape[-1] != 2 * H * K + HV * V or a.numel() != B * T * HV * K or b.numel() != B * T * HV \
+            or tuple(state_pool.shape[1:]) != (HV, V, K) or state_idx.numel() != B \
+            or A_log.numel() != HV or dt_bias.numel() != HV * K:
+        raise KDAError("inconsistent decode-extend shapes")
+    if scale is None:
+        scale = K ** -0.5
+    if o is None:
+        o = torch.empty((B, T, HV, V), dtype=torch.bfloat16, device=qkv.device)
+    _dev("o", o, torch.bfloat16)
+    if o.numel() != B * T * HV * V:
+        raise KDAError("o must hold [B, T, HV, V] elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(qkv.device).cuda_stream
+    _check(load_library().kda_decode_extend(
+        _ptr(qkv), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool),
+        _ptr(state_idx), _ptr(o), B, T, H, HV, K, V, state_pool.shape[0], float(scale),
         KDA_DECODE_L2NORM if l2norm else 0, ctypes.c_void_p(stream)))
     return o

@@ -152,4 +152,25 @@ int kda_decode_step(const void *qkv, const void *a, const void *b, const float *
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_decode_extend(const void *qkv, const void *a, const void *b, const float *A_log,
+                      const float *dt_bias, float *state_pool, const int32_t *state_idx, void *o,
+                      int B, int T, int H, int HV, int K, int V, int P, float scale, int flags,
+                      hipStream_t stream)
+{
+    if (K != 128 || V != 128) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || HV % H != 0 || P < 0) return KDA_ERR_SHAPE;
+    if ((long long)B * HV > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if ((long long)B * T * (2LL * H * K + (long long)HV * V) > 0x7fffffffLL * 8) return KDA_ERR_SHAPE;
+    if (B == 0 || T == 0) return KDA_OK;
+    if (!qkv || !a || !b || !A_log || !dt_bias || !state_pool || !state_idx || !o) return KDA_ERR_NULL;
+    const void *ptrs[] = {qkv, a, b, A_log, dt_bias, state_pool, state_idx, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_extend(
+        static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(a),
+        static_cast<const uint16_t *>(b), A_log, dt_bias, state_pool, state_idx,
+        static_cast<uint16_t *>(o), B, T, H, HV, scale, flags & KDA_DECODE_L2NORM, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -32,70 +32,51 @@
 
 namespace kda {
 
-template <int K_, int V_>
-__global__ __launch_bounds__(512) void decode_kernel(
-    const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
-    const uint16_t *__restrict__ b, const float *__restrict__ A_log,
-    const float *__restrict__ dt_bias, float *__restrict__ pool,
-    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV,
-    float scale, int l2norm)
-{
-    static_assert(K_ == 128 && V_ == 128, "decode kernel is built for K = V = 128");
-    constexpr int ROWS = V_ / 32;  // rows per thread
-    const int n = blockIdx.x / HV;
-    const int hv = blockIdx.x - n * HV;
-    const int tid = threadIdx.x & 255;
-    const int r0 = (threadIdx.x >> 8) * (V_ / 2);  // first state row of this half
-    const int j = tid & 15;
-    const int g = tid >> 4;
-
-    // Activation loads go out before the state loads: vmcnt retires in issue
-    // order, so the gate arithmetic then overlaps the state's latency instead
-    // of waiting behind it.  v is loaded here too, so no load follows the
-    // first state store (vmcnt counts stores as well).
-    const int hq = hv / (HV / H);
-    const size_t D = 2 * (size_t)H * K_ + (size_t)HV * V_;
-    const uint16_t *x = qkv + (size_t)n * D;
-    const int cols[2] = {4 * j, 64 + 4 * j};
+// One token's activations for one (row, value head), as a thread of the
+// 512-thread workgroup loads them: its 8 q, k and a channels (bf16 pairs at
+// columns 4j and 64+4j), the v values of its state rows and b.
+template <int V_>
+struct TokenRaw {
     uint2 qb[2], kb[2], ab[2];
-    f32x4 dt[2];
+    uint16_t vraw[V_ / 32];
+    uint16_t braw;
+};
+
+// x: the token's packed qkv row; arow: its a row; bp: its b entry.
+template <int K_, int V_>
+__device__ __forceinline__ void load_token(TokenRaw<V_> &t, const uint16_t *x, const uint16_t *arow,
+                                           const uint16_t *bp, int H, int hq, int hv, int j, int g,
+                                           int r0)
+{
+    const int cols[2] = {4 * j, 64 + 4 * j};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        qb[h] = *reinterpret_cast<const uint2 *>(x + (size_t)hq * K_ + cols[h]);
-        kb[h] = *reinterpret_cast<const uint2 *>(x + (size_t)H * K_ + (size_t)hq * K_ + cols[h]);
-        ab[h] = *reinterpret_cast<const uint2 *>(a + ((size_t)n * HV + hv) * K_ + cols[h]);
-        dt[h] = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + cols[h]);
+        t.qb[h] = *reinterpret_cast<const uint2 *>(x + (size_t)hq * K_ + cols[h]);
+        t.kb[h] = *reinterpret_cast<const uint2 *>(x + (size_t)H * K_ + (size_t)hq * K_ + cols[h]);
+        t.ab[h] = *reinterpret_cast<const uint2 *>(arow + cols[h]);
     }
     const uint16_t *vrow = x + 2 * (size_t)H * K_ + (size_t)hv * V_ + r0;
-    uint16_t vraw[ROWS];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) vraw[r] = vrow[g + 16 * r];
-    const uint16_t braw = b[(size_t)n * HV + hv];
-    const float A_l = A_log[hv];
+    for (int r = 0; r < V_ / 32; ++r) t.vraw[r] = vrow[g + 16 * r];
+    t.braw = *bp;
+}
 
-    uint16_t *orow = o + ((size_t)n * HV + hv) * V_;
-    const int idx = state_idx[n];
-    if (idx < 0) {  // pad slot: zero output, no state access
-        if (threadIdx.x < V_) orow[threadIdx.x] = 0;
-        return;
-    }
-
-    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the state loads
-    float *S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_) + (size_t)r0 * K_;
-    // state rows g + 16 r of this half, two float4 per row
-    f32x4 s[ROWS][2];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-        const float *row = S + (size_t)(g + 16 * r) * K_;
-        s[r][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * j));
-        s[r][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * j));
-    }
-
+// One token of [SGL-PR]'s update on the thread's state registers s (rows
+// g + 16 r of its half, columns 4j.. and 64+4j..): gate, optional L2 norm,
+// q scale, beta, then per row S' = S Diag(e^g), u = beta (v - S'k),
+// S = S' + u k^T and o = S'q + u (k.q).  row_done(r, o_r) runs once row r is
+// final, so a caller can store it at once.
+template <int V_, typename RowFn>
+__device__ __forceinline__ void token_update(f32x4 (&s)[V_ / 32][2], const TokenRaw<V_> &t,
+                                             const f32x4 (&dt)[2], float A, float scale, int l2norm,
+                                             RowFn &&row_done)
+{
+    constexpr int ROWS = V_ / 32;
     float qv[8], kv[8], eg[8];
-    const float A = __builtin_amdgcn_exp2f(A_l * kLog2e);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint32_t qw[2] = {qb[h].x, qb[h].y}, kw[2] = {kb[h].x, kb[h].y}, aw[2] = {ab[h].x, ab[h].y};
+        const uint32_t qw[2] = {t.qb[h].x, t.qb[h].y}, kw[2] = {t.kb[h].x, t.kb[h].y},
+                       aw[2] = {t.ab[h].x, t.ab[h].y};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint16_t qe = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
@@ -120,7 +101,7 @@ __global__ __launch_bounds__(512) void decode_kernel(
 #pragma unroll
     for (int c = 0; c < 8; ++c) { qv[c] *= scale; kq += kv[c] * qv[c]; }
     kq = row16_sum(kq);
-    const float beta = sigmoid_f(bf16_to_f32(braw));
+    const float beta = sigmoid_f(bf16_to_f32(t.braw));
 
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
@@ -136,16 +117,142 @@ __global__ __launch_bounds__(512) void decode_kernel(
             }
         pk = row16_sum(pk);
         pq = row16_sum(pq);
-        const int row = g + 16 * r;
-        const float u = beta * (bf16_to_f32(vraw[r]) - pk);
+        const float u = beta * (bf16_to_f32(t.vraw[r]) - pk);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[r][h][e] += u * kv[4 * h + e];
+        row_done(r, pq + u * kq);
+    }
+}
+
+template <int K_, int V_>
+__global__ __launch_bounds__(512) void decode_kernel(
+    const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
+    const uint16_t *__restrict__ b, const float *__restrict__ A_log,
+    const float *__restrict__ dt_bias, float *__restrict__ pool,
+    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV,
+    float scale, int l2norm)
+{
+    static_assert(K_ == 128 && V_ == 128, "decode kernel is built for K = V = 128");
+    constexpr int ROWS = V_ / 32;  // rows per thread
+    const int n = blockIdx.x / HV;
+    const int hv = blockIdx.x - n * HV;
+    const int tid = threadIdx.x & 255;
+    const int r0 = (threadIdx.x >> 8) * (V_ / 2);  // first state row of this half
+    const int j = tid & 15;
+    const int g = tid >> 4;
+
+    // Activation loads go out before the state loads: vmcnt retires in issue
+    // order, so the gate arithmetic then overlaps the state's latency instead
+    // of waiting behind it.  v is loaded here too, so no load follows the
+    // first state store (vmcnt counts stores as well).
+    const int hq = hv / (HV / H);
+    const size_t D = 2 * (size_t)H * K_ + (size_t)HV * V_;
+    TokenRaw<V_> tk;
+    load_token<K_, V_>(tk, qkv + (size_t)n * D, a + ((size_t)n * HV + hv) * K_, b + (size_t)n * HV + hv,
+                       H, hq, hv, j, g, r0);
+    f32x4 dt[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        dt[h] = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + 4 * j + 64 * h);
+    const float A_l = A_log[hv];
+
+    uint16_t *orow = o + ((size_t)n * HV + hv) * V_;
+    const int idx = state_idx[n];
+    if (idx < 0) {  // pad slot: zero output, no state access
+        if (threadIdx.x < V_) orow[threadIdx.x] = 0;
+        return;
+    }
+
+    __builtin_amdgcn_sched_barrier(0);  // keep the activation loads ahead of the state loads
+    float *S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_) + (size_t)r0 * K_;
+    // state rows g + 16 r of this half, two float4 per row
+    f32x4 s[ROWS][2];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const float *row = S + (size_t)(g + 16 * r) * K_;
+        s[r][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * j));
+        s[r][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * j));
+    }
+
+    const float A = __builtin_amdgcn_exp2f(A_l * kLog2e);
+    token_update<V_>(s, tk, dt, A, scale, l2norm, [&](int r, float ov) {
+        const int row = g + 16 * r;
         float *dst = S + (size_t)row * K_;
         __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
         __builtin_nontemporal_store(s[r][1], reinterpret_cast<f32x4 *>(dst + 64 + 4 * j));
-        if (j == 0) orow[r0 + row] = f32_to_bf16(pq + u * kq);
+        if (j == 0) orow[r0 + row] = f32_to_bf16(ov);
+    });
+}
+
+// T tokens per row applied in order to the row's slot (the fused recurrent
+// form with a token loop that [SGL-PR] names for extend and speculative
+// verification): the slot is read once, kept in registers for all T tokens
+// and written once; each token's activations are loaded while the previous
+// token is computed.  Token t of row n: qkv[(n T + t) D ..], a[(n T + t) HV K
+// ..], b[(n T + t) HV ..], o[((n T + t) HV + hv) V ..].
+template <int K_, int V_>
+__global__ __launch_bounds__(512) void extend_kernel(
+    const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
+    const uint16_t *__restrict__ b, const float *__restrict__ A_log,
+    const float *__restrict__ dt_bias, float *__restrict__ pool,
+    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int T, int H, int HV,
+    float scale, int l2norm)
+{
+    static_assert(K_ == 128 && V_ == 128, "extend kernel is built for K = V = 128");
+    constexpr int ROWS = V_ / 32;
+    const int n = blockIdx.x / HV;
+    const int hv = blockIdx.x - n * HV;
+    const int tid = threadIdx.x & 255;
+    const int r0 = (threadIdx.x >> 8) * (V_ / 2);
+    const int j = tid & 15;
+    const int g = tid >> 4;
+    const int hq = hv / (HV / H);
+    const size_t D = 2 * (size_t)H * K_ + (size_t)HV * V_;
+    const size_t tok0 = (size_t)n * T;
+
+    const int idx = state_idx[n];
+    if (idx < 0) {  // pad row: zero outputs, no state access
+        for (int t = 0; t < T; ++t)
+            if (threadIdx.x < V_) o[((tok0 + t) * HV + hv) * V_ + threadIdx.x] = 0;
+        return;
+    }
+    auto load = [&](TokenRaw<V_> &tk, int t) {
+        const size_t tok = tok0 + t;
+        load_token<K_, V_>(tk, qkv + tok * D, a + (tok * HV + hv) * K_, b + tok * HV + hv, H, hq, hv, j,
+                           g, r0);
+    };
+    TokenRaw<V_> cur, nxt;
+    load(cur, 0);
+    f32x4 dt[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        dt[h] = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + 4 * j + 64 * h);
+    const float A = __builtin_amdgcn_exp2f(A_log[hv] * kLog2e);
+
+    __builtin_amdgcn_sched_barrier(0);  // token 0's activations ahead of the state loads
+    float *S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_) + (size_t)r0 * K_;
+    f32x4 s[ROWS][2];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const float *row = S + (size_t)(g + 16 * r) * K_;
+        s[r][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * j));
+        s[r][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * j));
+    }
+    for (int t = 0; t < T; ++t) {
+        if (t + 1 < T) load(nxt, t + 1);
+        uint16_t *orow = o + ((tok0 + t) * HV + hv) * V_ + r0;
+        token_update<V_>(s, cur, dt, A, scale, l2norm, [&](int r, float ov) {
+            if (j == 0) orow[g + 16 * r] = f32_to_bf16(ov);
+        });
+        if (t + 1 < T) cur = nxt;
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        float *dst = S + (size_t)(g + 16 * r) * K_;
+        __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
+        __builtin_nontemporal_store(s[r][1], reinterpret_cast<f32x4 *>(dst + 64 + 4 * j));
     }
 }
 
@@ -156,6 +263,16 @@ hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t 
 {
     hipLaunchKernelGGL((decode_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(512), 0, stream,
                        qkv, a, b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+    return hipGetLastError();
+}
+
+hipError_t launch_extend(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
+                         const float *A_log, const float *dt_bias, float *pool,
+                         const int32_t *state_idx, uint16_t *o, int B, int T, int H, int HV,
+                         float scale, int l2norm, hipStream_t stream)
+{
+    hipLaunchKernelGGL((extend_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(512), 0, stream,
+                       qkv, a, b, A_log, dt_bias, pool, state_idx, o, T, H, HV, scale, l2norm);
     return hipGetLastError();
 }
 

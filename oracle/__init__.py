@@ -4,7 +4,7 @@ Only `tests/`, `__graft_entry__.smoke()` and the benchmark's `cpu_baseline`
 leg may import this package.  The product library never loads it and shares
 no code with it.
 
-`fwd` and `decode` call the plain-C token recurrence in `kda_oracle.c`
+`fwd`, `decode` and `extend` call the plain-C token recurrence in `kda_oracle.c`
 (OpenMP over independent (sequence, head) chains); `oracle.ref` holds the
 numpy twins and the chunkwise / level-1 references used to pin it.
 """
@@ -49,6 +49,11 @@ def _load():
                                           ctypes.c_int64, ctypes.c_double, ctypes.c_int, P,
                                           ctypes.c_int]
         lib.kda_oracle_decode.restype = ctypes.c_int
+        lib.kda_oracle_extend.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int64, ctypes.c_double, ctypes.c_int, P,
+                                          ctypes.c_int]
+        lib.kda_oracle_extend.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -115,4 +120,25 @@ def decode(qkv, a, b, A_log, dt_bias, pool, state_idx, H, HV, K, V, scale=None,
                                    int(n_threads or default_threads()))
     if rc != 0:
         raise ValueError("kda_oracle_decode rejected its arguments")
+    return o, pool
+
+
+def extend(qkv, a, b, A_log, dt_bias, pool, state_idx, H, HV, K, V, scale=None,
+           l2norm=True, n_threads=None):
+    """T decode steps per row in token order.  qkv: [B, T, 2HK + HV V];
+    a: [B, T, HV K]; b: [B, T, HV].  Returns (o [B,T,HV,V], new pool) in fp64;
+    the input pool is not modified."""
+    qkv = _f64(qkv)
+    B, T = qkv.shape[0], qkv.shape[1]
+    if scale is None:
+        scale = K ** -0.5
+    pool = np.array(pool, np.float64, copy=True, order="C")
+    idx = np.ascontiguousarray(state_idx, np.int64)
+    o = np.zeros((B, T, HV, V))
+    rc = _load().kda_oracle_extend(_ptr(qkv), _ptr(_f64(a)), _ptr(_f64(b)), _ptr(_f64(A_log)),
+                                   _ptr(_f64(dt_bias)), _ptr(pool), _ptr(idx), B, T, H, HV, K, V,
+                                   pool.shape[0], float(scale), int(bool(l2norm)), _ptr(o),
+                                   int(n_threads or default_threads()))
+    if rc != 0:
+        raise ValueError("kda_oracle_extend rejected its arguments")
     return o, pool

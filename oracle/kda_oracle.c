@@ -131,6 +131,85 @@ int kda_oracle_fwd(const double *q, const double *k, const double *v,
 }
 
 /*
+ * T tokens per row over a state pool, each token one step of [SGL-PR]'s
+ * decode update, in token order (the fused recurrent form with a token loop
+ * that the page gives for extend and speculative verification):
+ *   qkv  : [B, T, 2*H*K + HV*V]  (q heads, then k heads, then v heads)
+ *   a    : [B, T, HV*K]   b : [B, T, HV]   A_log : [HV]   dt_bias : [HV*K]
+ *   pool : [P, HV, V, K] updated in place for the referenced slots
+ *   state_idx : [B]; a negative entry is a pad: zero outputs, no state write.
+ *   o    : [B, T, HV, V]
+ * Value head hv reads q/k head hv / (HV / H).  T = 1 is the decode step.
+ */
+int kda_oracle_extend(const double *qkv, const double *a, const double *b,
+                      const double *A_log, const double *dt_bias, double *pool,
+                      const int64_t *state_idx, int B, int T, int H, int HV, int K, int V,
+                      int64_t P, double scale, int l2norm, double *o, int n_threads)
+{
+    if (!qkv || !a || !b || !A_log || !dt_bias || !pool || !state_idx || !o) return -1;
+    if (B < 0 || T < 0 || H <= 0 || HV <= 0 || HV % H != 0 || K <= 0 || V <= 0) return -1;
+    const int64_t row = 2 * (int64_t)H * K + (int64_t)HV * V;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : err)
+#endif
+    for (int i = 0; i < B * HV; ++i) {
+        const int n = i / HV, hv = i % HV, hq = hv / (HV / H);
+        const int64_t idx = state_idx[n];
+        if (idx < 0) {
+            for (int t = 0; t < T; ++t) {
+                double *on = o + (((int64_t)n * T + t) * HV + hv) * V;
+                for (int r = 0; r < V; ++r) on[r] = 0.0;
+            }
+            continue;
+        }
+        if (idx >= P) { err |= 1; continue; }
+        double *buf = (double *)malloc(sizeof(double) * (3 * (size_t)K + V));
+        if (!buf) { err |= 1; continue; }
+        double *qv = buf, *kv = buf + K, *eg = buf + 2 * K, *u = buf + 3 * K;
+        double *S = pool + (idx * HV + hv) * (int64_t)V * K;
+        const double A_exp = exp(A_log[hv]);
+        for (int t = 0; t < T; ++t) {
+            const int64_t tok = (int64_t)n * T + t;
+            const double *x = qkv + tok * row;
+            double *on = o + (tok * HV + hv) * V;
+            for (int c = 0; c < K; ++c) {
+                qv[c] = x[(int64_t)hq * K + c];
+                kv[c] = x[(int64_t)H * K + (int64_t)hq * K + c];
+            }
+            if (l2norm) {
+                double sq = 0.0, sk = 0.0;
+                for (int c = 0; c < K; ++c) { sq += qv[c] * qv[c]; sk += kv[c] * kv[c]; }
+                const double nq = sqrt(sq + 1e-6), nk = sqrt(sk + 1e-6);
+                for (int c = 0; c < K; ++c) { qv[c] /= nq; kv[c] /= nk; }
+            }
+            for (int c = 0; c < K; ++c) qv[c] *= scale;
+            for (int c = 0; c < K; ++c)
+                eg[c] = exp(-A_exp * softplus_exact(a[tok * HV * K + (int64_t)hv * K + c] +
+                                                    dt_bias[(int64_t)hv * K + c]));
+            const double beta = sigmoid(b[tok * HV + hv]);
+            const double *vv = x + 2 * (int64_t)H * K + (int64_t)hv * V;
+            for (int r = 0; r < V; ++r) {
+                double *Sr = S + (int64_t)r * K;
+                double w = 0.0;
+                for (int c = 0; c < K; ++c) { Sr[c] *= eg[c]; w += Sr[c] * kv[c]; }
+                u[r] = beta * (vv[r] - w);
+            }
+            for (int r = 0; r < V; ++r) {
+                double *Sr = S + (int64_t)r * K;
+                double acc = 0.0;
+                for (int c = 0; c < K; ++c) { Sr[c] += u[r] * kv[c]; acc += Sr[c] * qv[c]; }
+                on[r] = acc;
+            }
+        }
+        free(buf);
+    }
+    (void)n_threads;
+    return err ? -1 : 0;
+}
+
+/*
  * One T=1 decode step over a state pool, as in [SGL-PR]:
  *   qkv  : [B, 2*H*K + HV*V]  (q heads, then k heads, then v heads)
  *   a    : [B, HV*K]   b : [B, HV]   A_log : [HV]   dt_bias : [HV*K]
@@ -144,59 +223,6 @@ int kda_oracle_decode(const double *qkv, const double *a, const double *b,
                       const int64_t *state_idx, int B, int H, int HV, int K, int V,
                       int64_t P, double scale, int l2norm, double *o, int n_threads)
 {
-    if (!qkv || !a || !b || !A_log || !dt_bias || !pool || !state_idx || !o) return -1;
-    if (B < 0 || H <= 0 || HV <= 0 || HV % H != 0 || K <= 0 || V <= 0) return -1;
-    const int64_t row = 2 * (int64_t)H * K + (int64_t)HV * V;
-    int err = 0;
-#ifdef _OPENMP
-    if (n_threads > 0) omp_set_num_threads(n_threads);
-#pragma omp parallel for schedule(dynamic, 4) reduction(| : err)
-#endif
-    for (int i = 0; i < B * HV; ++i) {
-        const int n = i / HV, hv = i % HV, hq = hv / (HV / H);
-        double *on = o + ((int64_t)n * HV + hv) * V;
-        const int64_t idx = state_idx[n];
-        if (idx < 0) {
-            for (int r = 0; r < V; ++r) on[r] = 0.0;
-            continue;
-        }
-        if (idx >= P) { err |= 1; continue; }
-        double *buf = (double *)malloc(sizeof(double) * (3 * (size_t)K + V));
-        if (!buf) { err |= 1; continue; }
-        double *qv = buf, *kv = buf + K, *eg = buf + 2 * K, *u = buf + 3 * K;
-        const double *x = qkv + (int64_t)n * row;
-        for (int c = 0; c < K; ++c) {
-            qv[c] = x[(int64_t)hq * K + c];
-            kv[c] = x[(int64_t)H * K + (int64_t)hq * K + c];
-        }
-        if (l2norm) {
-            double sq = 0.0, sk = 0.0;
-            for (int c = 0; c < K; ++c) { sq += qv[c] * qv[c]; sk += kv[c] * kv[c]; }
-            const double nq = sqrt(sq + 1e-6), nk = sqrt(sk + 1e-6);
-            for (int c = 0; c < K; ++c) { qv[c] /= nq; kv[c] /= nk; }
-        }
-        for (int c = 0; c < K; ++c) qv[c] *= scale;
-        const double A_exp = exp(A_log[hv]);
-        for (int c = 0; c < K; ++c)
-            eg[c] = exp(-A_exp * softplus_exact(a[(int64_t)n * HV * K + (int64_t)hv * K + c] +
-                                                dt_bias[(int64_t)hv * K + c]));
-        const double beta = sigmoid(b[(int64_t)n * HV + hv]);
-        const double *vv = x + 2 * (int64_t)H * K + (int64_t)hv * V;
-        double *S = pool + (idx * HV + hv) * (int64_t)V * K;
-        for (int r = 0; r < V; ++r) {
-            double *Sr = S + (int64_t)r * K;
-            double w = 0.0;
-            for (int c = 0; c < K; ++c) { Sr[c] *= eg[c]; w += Sr[c] * kv[c]; }
-            u[r] = beta * (vv[r] - w);
-        }
-        for (int r = 0; r < V; ++r) {
-            double *Sr = S + (int64_t)r * K;
-            double acc = 0.0;
-            for (int c = 0; c < K; ++c) { Sr[c] += u[r] * kv[c]; acc += Sr[c] * qv[c]; }
-            on[r] = acc;
-        }
-        free(buf);
-    }
-    (void)n_threads;
-    return err ? -1 : 0;
+    return kda_oracle_extend(qkv, a, b, A_log, dt_bias, pool, state_idx, B, 1, H, HV, K, V, P,
+                             scale, l2norm, o, n_threads);
 }

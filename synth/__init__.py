@@ -275,15 +275,24 @@ class Decode:
                     A_log=self.A_log.astype(np.float64), dt_bias=self.dt_bias.astype(np.float64))
 
 
+def _unit_qk(qkv, H, K):
+    """L2-normalise the q and k heads of packed rows (last axis), float32."""
+    qk = _l2norm_f32(qkv[..., :2 * H * K].reshape(-1, K))
+    qkv[..., :2 * H * K] = qk.reshape(qkv[..., :2 * H * K].shape)
+
+
 def decode(seed: int, B: int, H: int, HV: int, K: int, V: int, P: int, n_pad: int, *,
-           name: str = "custom", gate_stress: float = 0.0) -> Decode:
+           name: str = "custom", gate_stress: float = 0.0, unit_qk: bool = False) -> Decode:
     """Draw a decode workload: distinct slots (first B of a permutation of P),
-    then `n_pad` random rows set to -1."""
+    then `n_pad` random rows set to -1.  `unit_qk`: q and k heads drawn as unit
+    vectors (for calls without the in-kernel norm)."""
     assert P >= B and HV % H == 0
     rng = np.random.default_rng(seed)
     st = _Streams(seed)
     D = 2 * H * K + HV * V
     qkv = st.normal((B, D))
+    if unit_qk:
+        _unit_qk(qkv, H, K)
     a = st.normal((B, HV * K))
     b = st.normal((B, HV))
     dt_bias = rng.uniform(-1.0, 1.0, size=HV * K).astype(np.float32)
@@ -298,6 +307,33 @@ def decode(seed: int, B: int, H: int, HV: int, K: int, V: int, P: int, n_pad: in
     return Decode(name=name, B=B, H=H, HV=HV, K=K, V=V, P=P, qkv=bf16_bits(qkv), a=bf16_bits(a),
                   b=bf16_bits(b), A_log=A_log, dt_bias=dt_bias, pool=pool, state_idx=idx,
                   meta=dict(seed=seed))
+
+
+def extend(seed: int, B: int, T: int, H: int, HV: int, K: int, V: int, P: int, n_pad: int, *,
+           name: str = "custom", gate_stress: float = 0.0, unit_qk: bool = False) -> Decode:
+    """Draw a T-token-per-row decode workload (extend / speculative verify):
+    as `decode`, with qkv [B, T, D], a [B, T, HV*K] and b [B, T, HV]."""
+    assert P >= B and HV % H == 0
+    rng = np.random.default_rng(seed)
+    st = _Streams(seed)
+    D = 2 * H * K + HV * V
+    qkv = st.normal((B, T, D))
+    if unit_qk:
+        _unit_qk(qkv, H, K)
+    a = st.normal((B, T, HV * K))
+    b = st.normal((B, T, HV))
+    dt_bias = rng.uniform(-1.0, 1.0, size=HV * K).astype(np.float32)
+    A_log = rng.uniform(0.0, LOG16, size=HV).astype(np.float32)
+    pool = st.normal((P, HV, V, K), 0.02)
+    idx = rng.permutation(P)[:B].astype(np.int32)
+    if n_pad:
+        idx[rng.choice(B, size=n_pad, replace=False)] = -1
+    if gate_stress > 0:
+        hit = rng.random(size=a.shape) < gate_stress
+        a[hit] = np.float32(30.0)
+    return Decode(name=name, B=B, H=H, HV=HV, K=K, V=V, P=P, qkv=bf16_bits(qkv), a=bf16_bits(a),
+                  b=bf16_bits(b), A_log=A_log, dt_bias=dt_bias, pool=pool, state_idx=idx,
+                  meta=dict(seed=seed, T=T))
 
 
 DECODE_WORKLOAD = dict(name="decode-bf16 B256 H32 HV32 K128 V128 pool512 pad8",

@@ -107,6 +107,26 @@ def test_decode_validation(lib):
     assert decode(lib, B=0) == 0
 
 
+def extend(lib, **kw):
+    args = dict(qkv=A, a=A, b=A, A_log=B, dt=B, pool=A, idx=A, o=A, B=4, T=3, H=2, HV=4, K=128,
+                V=128, P=8, scale=0.1, flags=1)
+    args.update(kw)
+    return lib.kda_decode_extend(args["qkv"], args["a"], args["b"], args["A_log"], args["dt"],
+                                 args["pool"], args["idx"], args["o"], args["B"], args["T"],
+                                 args["H"], args["HV"], args["K"], args["V"], args["P"],
+                                 args["scale"], args["flags"], None)
+
+
+def test_decode_extend_validation(lib):
+    assert extend(lib, V=64) == -3
+    assert extend(lib, T=-1) == -2
+    assert extend(lib, HV=6, H=4) == -2              # HV % H != 0
+    assert extend(lib, o=None) == -1
+    assert extend(lib, qkv=MIS) == -4
+    assert extend(lib, T=0) == 0                     # nothing to do, no launch
+    assert extend(lib, B=0) == 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 16, 1, 64)

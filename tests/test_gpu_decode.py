@@ -69,7 +69,7 @@ def test_decode_small(B, H, HV, pads):
 def test_decode_without_l2norm_and_gate_stress():
     d = synth.decode(61, B=8, H=2, HV=4, K=128, V=128, P=12, n_pad=1, gate_stress=0.05)
     # without the in-kernel norm feed unit vectors so magnitudes stay O(1)
-    d2 = synth.decode(62, B=8, H=2, HV=4, K=128, V=128, P=12, n_pad=1)
+    d2 = synth.decode(62, B=8, H=2, HV=4, K=128, V=128, P=12, n_pad=1, unit_qk=True)
     check_decode(d, what="decode gate-stress")
     check_decode(d2, l2norm=False, what="decode no-l2norm")
 

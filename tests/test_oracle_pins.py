@@ -356,6 +356,65 @@ def test_decode_c_matches_numpy():
 
 
 # ----------------------------------------------------------------------------
+# extend (I14): T decode steps per row in one call are the forward recurrence
+# over those T tokens from the slot's state (matrix form, numpy), on
+# L2-normalised q, k; pads give zero outputs and leave every slot alone.
+# ----------------------------------------------------------------------------
+def _extend_inputs(seed, B=5, T=7, H=2, HV=4, K=8, V=5, P=9):
+    r = RNG(seed)
+    d = dict(qkv=r.standard_normal((B, T, 2 * H * K + HV * V)), a=r.standard_normal((B, T, HV * K)),
+             b=r.standard_normal((B, T, HV)), A_log=r.uniform(0, math.log(16), HV),
+             dt_bias=r.uniform(-1, 1, HV * K))
+    pool = 0.3 * r.standard_normal((P, HV, V, K))
+    idx = r.permutation(P)[:B]
+    idx[2] = -1
+    return d, pool, idx
+
+
+def test_extend_is_a_forward_chain():
+    B, T, H, HV, K, V, P = 5, 7, 2, 4, 8, 5, 9
+    d, pool, idx = _extend_inputs(61)
+    o, newpool = oracle.extend(**d, pool=pool, state_idx=idx, H=H, HV=HV, K=K, V=V, n_threads=2)
+    assert o.shape == (B, T, HV, V)
+    for n in range(B):
+        if idx[n] < 0:
+            assert not o[n].any()
+            continue
+        for hv in range(HV):
+            hq = hv // (HV // H)
+            x = d["qkv"][n]
+            q = x[:, hq * K:(hq + 1) * K]
+            k = x[:, H * K + hq * K:H * K + (hq + 1) * K]
+            q = q / np.sqrt((q * q).sum(-1, keepdims=True) + 1e-6)
+            k = k / np.sqrt((k * k).sum(-1, keepdims=True) + 1e-6)
+            v = x[:, 2 * H * K + hv * V:2 * H * K + (hv + 1) * V]
+            chain = dict(q=q[:, None], k=k[:, None], v=v[:, None], a=d["a"][n][:, None, hv * K:(hv + 1) * K],
+                         b=d["b"][n][:, hv:hv + 1], A_log=d["A_log"][hv:hv + 1],
+                         dt_bias=d["dt_bias"][hv * K:(hv + 1) * K][None], h0=pool[idx[n], hv][None, None],
+                         cu_seqlens=None, scale=K ** -0.5)
+            oo, hh = ref.recurrent_matrix_form(**chain)
+            assert close(o[n, :, hv], oo[:, 0], 1e-12)
+            assert close(newpool[idx[n], hv], hh[0, 0], 1e-12)
+    untouched = np.setdiff1d(np.arange(P), idx[idx >= 0])
+    assert np.array_equal(newpool[untouched], pool[untouched])
+
+
+def test_extend_equals_successive_decode_steps():
+    B, T, H, HV, K, V = 5, 7, 2, 4, 8, 5
+    d, pool, idx = _extend_inputs(62)
+    o, newpool = oracle.extend(**d, pool=pool, state_idx=idx, H=H, HV=HV, K=K, V=V, n_threads=2)
+    p = pool
+    for t in range(T):
+        ot, p = oracle.decode(d["qkv"][:, t], d["a"][:, t], d["b"][:, t], d["A_log"], d["dt_bias"], p, idx,
+                              H=H, HV=HV, K=K, V=V, n_threads=2)
+        assert np.array_equal(o[:, t], ot)
+    assert np.array_equal(newpool, p)
+    o0, p0 = oracle.extend(d["qkv"][:, :0], d["a"][:, :0], d["b"][:, :0], d["A_log"], d["dt_bias"], pool, idx,
+                           H=H, HV=HV, K=K, V=V, n_threads=2)
+    assert o0.shape == (B, 0, HV, V) and np.array_equal(p0, pool)
+
+
+# ----------------------------------------------------------------------------
 # level-1 references of the TileLang page (I11): they agree to fp64 rounding
 # (the page reports 1e-15-level max-abs and 1e-16-level rel-L2), and the two
 # deliberate structural bugs give O(1) errors.
