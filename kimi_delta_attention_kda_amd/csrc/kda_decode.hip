@@ -61,18 +61,19 @@ __device__ __forceinline__ void load_token(TokenRaw<V_> &t, const uint16_t *x, c
     t.braw = *bp;
 }
 
-// One token of [SGL-PR]'s update on the thread's state registers s (rows
-// g + 16 r of its half, columns 4j.. and 64+4j..): gate, optional L2 norm,
-// q scale, beta, then per row S' = S Diag(e^g), u = beta (v - S'k),
-// S = S' + u k^T and o = S'q + u (k.q).  row_done(r, o_r) runs once row r is
-// final, so a caller can store it at once.
-template <int V_, typename RowFn>
-__device__ __forceinline__ void token_update(f32x4 (&s)[V_ / 32][2], const TokenRaw<V_> &t,
-                                             const f32x4 (&dt)[2], float A, float scale, int l2norm,
-                                             RowFn &&row_done)
-{
-    constexpr int ROWS = V_ / 32;
+// Per-token values of [SGL-PR]'s update for the thread's 8 channels (columns
+// 4j.. and 64+4j..): decay e^g, q (L2-normalised if asked, times scale) and k
+// (L2-normalised if asked), the 16-lane sums k.q, and beta.  Every 16-lane row
+// group computes the same values.
+struct TokenPrep {
     float qv[8], kv[8], eg[8];
+    float kq, beta;
+};
+
+template <int V_>
+__device__ __forceinline__ void token_prep(TokenPrep &p, const TokenRaw<V_> &t, const f32x4 (&dt)[2],
+                                           float A, float scale, int l2norm)
+{
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t qw[2] = {t.qb[h].x, t.qb[h].y}, kw[2] = {t.kb[h].x, t.kb[h].y},
@@ -82,27 +83,37 @@ __device__ __forceinline__ void token_update(f32x4 (&s)[V_ / 32][2], const Token
             const uint16_t qe = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
             const uint16_t ke = (uint16_t)(kw[e >> 1] >> (16 * (e & 1)));
             const uint16_t ae = (uint16_t)(aw[e >> 1] >> (16 * (e & 1)));
-            qv[4 * h + e] = bf16_to_f32(qe);
-            kv[4 * h + e] = bf16_to_f32(ke);
-            eg[4 * h + e] = gate_decay(bf16_to_f32(ae) + dt[h][e], A);
+            p.qv[4 * h + e] = bf16_to_f32(qe);
+            p.kv[4 * h + e] = bf16_to_f32(ke);
+            p.eg[4 * h + e] = gate_decay(bf16_to_f32(ae) + dt[h][e], A);
         }
     }
     if (l2norm) {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) { sq += qv[c] * qv[c]; sk += kv[c] * kv[c]; }
+        for (int c = 0; c < 8; ++c) { sq += p.qv[c] * p.qv[c]; sk += p.kv[c] * p.kv[c]; }
         sq = row16_sum(sq);
         sk = row16_sum(sk);
         const float iq = 1.0f / sqrtf(sq + 1e-6f), ik = 1.0f / sqrtf(sk + 1e-6f);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) { qv[c] *= iq; kv[c] *= ik; }
+        for (int c = 0; c < 8; ++c) { p.qv[c] *= iq; p.kv[c] *= ik; }
     }
     float kq = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) { qv[c] *= scale; kq += kv[c] * qv[c]; }
-    kq = row16_sum(kq);
-    const float beta = sigmoid_f(bf16_to_f32(t.braw));
+    for (int c = 0; c < 8; ++c) { p.qv[c] *= scale; kq += p.kv[c] * p.qv[c]; }
+    p.kq = row16_sum(kq);
+    p.beta = sigmoid_f(bf16_to_f32(t.braw));
+}
 
+// The state rows of one token on the thread's registers s (rows g + 16 r of
+// its half): S' = S Diag(e^g), u = beta (v - S'k), S = S' + u k^T and
+// o = S'q + u (k.q).  row_done(r, o_r) runs once row r is final, so a caller
+// can store it at once.
+template <int V_, typename RowFn>
+__device__ __forceinline__ void token_rows(f32x4 (&s)[V_ / 32][2], const TokenPrep &p,
+                                           const uint16_t (&vraw)[V_ / 32], RowFn &&row_done)
+{
+    constexpr int ROWS = V_ / 32;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
         float pk = 0.f, pq = 0.f;
@@ -110,19 +121,19 @@ __device__ __forceinline__ void token_update(f32x4 (&s)[V_ / 32][2], const Token
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float sv = s[r][h][e] * eg[4 * h + e];
+                const float sv = s[r][h][e] * p.eg[4 * h + e];
                 s[r][h][e] = sv;
-                pk += sv * kv[4 * h + e];
-                pq += sv * qv[4 * h + e];
+                pk += sv * p.kv[4 * h + e];
+                pq += sv * p.qv[4 * h + e];
             }
         pk = row16_sum(pk);
         pq = row16_sum(pq);
-        const float u = beta * (bf16_to_f32(t.vraw[r]) - pk);
+        const float u = p.beta * (bf16_to_f32(vraw[r]) - pk);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[r][h][e] += u * kv[4 * h + e];
-        row_done(r, pq + u * kq);
+            for (int e = 0; e < 4; ++e) s[r][h][e] += u * p.kv[4 * h + e];
+        row_done(r, pq + u * p.kq);
     }
 }
 
@@ -177,7 +188,9 @@ __global__ __launch_bounds__(512) void decode_kernel(
     }
 
     const float A = __builtin_amdgcn_exp2f(A_l * kLog2e);
-    token_update<V_>(s, tk, dt, A, scale, l2norm, [&](int r, float ov) {
+    TokenPrep pr;
+    token_prep<V_>(pr, tk, dt, A, scale, l2norm);
+    token_rows<V_>(s, pr, tk.vraw, [&](int r, float ov) {
         const int row = g + 16 * r;
         float *dst = S + (size_t)row * K_;
         __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
@@ -189,9 +202,18 @@ __global__ __launch_bounds__(512) void decode_kernel(
 // T tokens per row applied in order to the row's slot (the fused recurrent
 // form with a token loop that [SGL-PR] names for extend and speculative
 // verification): the slot is read once, kept in registers for all T tokens
-// and written once; each token's activations are loaded while the previous
-// token is computed.  Token t of row n: qkv[(n T + t) D ..], a[(n T + t) HV K
-// ..], b[(n T + t) HV ..], o[((n T + t) HV + hv) V ..].
+// and written once.  Tokens go in windows of TW = 16:
+//   * the workgroup loads a window's q, k, a and v rows (1 KiB per token) into
+//     LDS, one 16-byte load per thread per 8 tokens, issued ahead of the state
+//     loads for the first window: one memory latency per window;
+//   * 16-lane row group tt then computes token tt's per-channel values (gate,
+//     normalised q and k, k.q, beta; the lane layout and summation order of
+//     the T = 1 kernel, so the results are bitwise the same) into LDS, once
+//     per token instead of once per row group;
+//   * the token loop reads them back and does only the row work;
+//   * the window's outputs are gathered in LDS and stored as 256-byte rows.
+// Token t of row n: qkv[(n T + t) D ..], a[(n T + t) HV K ..],
+// b[(n T + t) HV ..], o[((n T + t) HV + hv) V ..].
 template <int K_, int V_>
 __global__ __launch_bounds__(512) void extend_kernel(
     const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
@@ -202,6 +224,15 @@ __global__ __launch_bounds__(512) void extend_kernel(
 {
     static_assert(K_ == 128 && V_ == 128, "extend kernel is built for K = V = 128");
     constexpr int ROWS = V_ / 32;
+    constexpr int TW = 16;                   // tokens per window (one per 16-lane row group of a half)
+    constexpr int UNITS = (3 * K_ + V_) / 8; // 16-byte units per token: q, k, a, v
+    constexpr int PER = TW * UNITS / 512;    // units each thread loads per window
+    __shared__ uint4 stage[TW * UNITS];      // [token][q | k | a | v] bf16
+    __shared__ uint16_t bstage[TW];
+    __shared__ f32x4 prep[TW][3][K_ / 4];    // [token][q | k | e^g][channel] fp32
+    __shared__ float2 prep_s[TW];            // [token](k.q, beta)
+    __shared__ uint4 ostage[TW * V_ / 8];    // [token][V] bf16
+
     const int n = blockIdx.x / HV;
     const int hv = blockIdx.x - n * HV;
     const int tid = threadIdx.x & 255;
@@ -214,24 +245,86 @@ __global__ __launch_bounds__(512) void extend_kernel(
 
     const int idx = state_idx[n];
     if (idx < 0) {  // pad row: zero outputs, no state access
-        for (int t = 0; t < T; ++t)
-            if (threadIdx.x < V_) o[((tok0 + t) * HV + hv) * V_ + threadIdx.x] = 0;
+        for (int i = threadIdx.x; i < T * (V_ / 8); i += 512)
+            *reinterpret_cast<uint4 *>(o + ((tok0 + i / (V_ / 8)) * HV + hv) * V_ + 8 * (i % (V_ / 8))) =
+                make_uint4(0, 0, 0, 0);
         return;
     }
-    auto load = [&](TokenRaw<V_> &tk, int t) {
-        const size_t tok = tok0 + t;
-        load_token<K_, V_>(tk, qkv + tok * D, a + (tok * HV + hv) * K_, b + tok * HV + hv, H, hq, hv, j,
-                           g, r0);
+
+    // Window loads: lane unit lu = threadIdx % 64 of the token rows
+    // threadIdx / 64 and threadIdx / 64 + 8 (512 is a multiple of 64, so each
+    // lane always loads the same unit: q, k, a or v, 16 bytes).
+    const int lu = threadIdx.x & 63;
+    const int ltok = threadIdx.x >> 6;
+    const uint16_t *lbase;
+    size_t lstride;
+    if (lu < 32) {
+        lbase = qkv + (lu < 16 ? (size_t)hq * K_ + 8 * lu : (size_t)H * K_ + (size_t)hq * K_ + 8 * (lu - 16));
+        lstride = D;
+    } else if (lu < 48) {
+        lbase = a + (size_t)hv * K_ + 8 * (lu - 32);
+        lstride = (size_t)HV * K_;
+    } else {
+        lbase = qkv + 2 * (size_t)H * K_ + (size_t)hv * V_ + 8 * (lu - 48);
+        lstride = D;
+    }
+    struct Win {
+        uint4 v[PER];
+        uint16_t b;
     };
-    TokenRaw<V_> cur, nxt;
-    load(cur, 0);
+    auto load_window = [&](int t0, int nt) {
+        Win w;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int tt = ltok + 8 * e;
+            w.v[e] = tt < nt ? *reinterpret_cast<const uint4 *>(lbase + (tok0 + t0 + tt) * lstride)
+                             : make_uint4(0, 0, 0, 0);
+        }
+        w.b = threadIdx.x < nt ? b[(tok0 + t0 + threadIdx.x) * HV + hv] : (uint16_t)0;
+        return w;
+    };
+    const uint2 *st2 = reinterpret_cast<const uint2 *>(stage);
+    const uint16_t *st16 = reinterpret_cast<const uint16_t *>(stage);
     f32x4 dt[2];
+    float A = 0.f;
+    // raw window -> LDS, then row group g < nt (first half) preps token g
+    auto publish_window = [&](const Win &w, int nt) {
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            if (ltok + 8 * e < nt) stage[threadIdx.x + 512 * e] = w.v[e];
+        if (threadIdx.x < nt) bstage[threadIdx.x] = w.b;
+        __syncthreads();
+        if (threadIdx.x < 256 && g < nt) {
+            TokenRaw<V_> tk;
+            const uint2 *u2 = st2 + g * (UNITS * 2);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                tk.qb[h] = u2[j + 16 * h];
+                tk.kb[h] = u2[32 + j + 16 * h];
+                tk.ab[h] = u2[64 + j + 16 * h];
+            }
+            tk.braw = bstage[g];
+            TokenPrep pr;
+            token_prep<V_>(pr, tk, dt, A, scale, l2norm);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                prep[g][0][j + 16 * h] = f32x4{pr.qv[4 * h], pr.qv[4 * h + 1], pr.qv[4 * h + 2], pr.qv[4 * h + 3]};
+                prep[g][1][j + 16 * h] = f32x4{pr.kv[4 * h], pr.kv[4 * h + 1], pr.kv[4 * h + 2], pr.kv[4 * h + 3]};
+                prep[g][2][j + 16 * h] = f32x4{pr.eg[4 * h], pr.eg[4 * h + 1], pr.eg[4 * h + 2], pr.eg[4 * h + 3]};
+            }
+            if (j == 0) prep_s[g] = make_float2(pr.kq, pr.beta);
+        }
+        __syncthreads();
+    };
+
+    const int nt0 = T < TW ? T : TW;
+    const Win w0 = load_window(0, nt0);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
         dt[h] = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + 4 * j + 64 * h);
-    const float A = __builtin_amdgcn_exp2f(A_log[hv] * kLog2e);
+    A = __builtin_amdgcn_exp2f(A_log[hv] * kLog2e);
 
-    __builtin_amdgcn_sched_barrier(0);  // token 0's activations ahead of the state loads
+    __builtin_amdgcn_sched_barrier(0);  // the first window's loads ahead of the state loads
     float *S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_) + (size_t)r0 * K_;
     f32x4 s[ROWS][2];
 #pragma unroll
@@ -240,13 +333,42 @@ __global__ __launch_bounds__(512) void extend_kernel(
         s[r][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * j));
         s[r][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * j));
     }
-    for (int t = 0; t < T; ++t) {
-        if (t + 1 < T) load(nxt, t + 1);
-        uint16_t *orow = o + ((tok0 + t) * HV + hv) * V_ + r0;
-        token_update<V_>(s, cur, dt, A, scale, l2norm, [&](int r, float ov) {
-            if (j == 0) orow[g + 16 * r] = f32_to_bf16(ov);
-        });
-        if (t + 1 < T) cur = nxt;
+    publish_window(w0, nt0);
+
+    uint16_t *os16 = reinterpret_cast<uint16_t *>(ostage);
+    for (int t0 = 0; t0 < T; t0 += TW) {
+        const int nt = T - t0 < TW ? T - t0 : TW;
+        if (t0 > 0) {
+            publish_window(load_window(t0, nt), nt);
+        }
+        for (int tt = 0; tt < nt; ++tt) {
+            TokenPrep pr;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const f32x4 q4 = prep[tt][0][j + 16 * h], k4 = prep[tt][1][j + 16 * h],
+                            e4 = prep[tt][2][j + 16 * h];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    pr.qv[4 * h + e] = q4[e];
+                    pr.kv[4 * h + e] = k4[e];
+                    pr.eg[4 * h + e] = e4[e];
+                }
+            }
+            const float2 ks = prep_s[tt];
+            pr.kq = ks.x;
+            pr.beta = ks.y;
+            uint16_t vraw[ROWS];
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) vraw[r] = st16[tt * (UNITS * 8) + 3 * K_ + r0 + g + 16 * r];
+            token_rows<V_>(s, pr, vraw, [&](int r, float ov) {
+                if (j == 0) os16[tt * V_ + r0 + g + 16 * r] = f32_to_bf16(ov);
+            });
+        }
+        __syncthreads();  // window outputs gathered; stage and prep free for the next window
+        for (int i = threadIdx.x; i < nt * (V_ / 8); i += 512)
+            *reinterpret_cast<uint4 *>(o + ((tok0 + t0 + i / (V_ / 8)) * HV + hv) * V_ + 8 * (i % (V_ / 8))) =
+                ostage[i];
+        __syncthreads();  // ostage read before the next window writes it
     }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
