@@ -5,6 +5,7 @@ leg may import this package.  The product library never loads it and shares
 no code with it.
 
 `fwd`, `decode` and `extend` call the plain-C token recurrence in `kda_oracle.c`
+and `conv_update` its short causal convolution
 (OpenMP over independent (sequence, head) chains); `oracle.ref` holds the
 numpy twins and the chunkwise / level-1 references used to pin it.
 """
@@ -54,6 +55,9 @@ def _load():
                                           ctypes.c_int64, ctypes.c_double, ctypes.c_int, P,
                                           ctypes.c_int]
         lib.kda_oracle_extend.restype = ctypes.c_int
+        lib.kda_oracle_conv_update.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int64, P]
+        lib.kda_oracle_conv_update.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -142,3 +146,36 @@ def extend(qkv, a, b, A_log, dt_bias, pool, state_idx, H, HV, K, V, scale=None,
     if rc != 0:
         raise ValueError("kda_oracle_extend rejected its arguments")
     return o, pool
+
+
+def conv_update(x, conv_state, weight, bias, state_idx):
+    """One causal-conv update per row (silu).  x: [B, D]; conv_state:
+    [P, W-1, D]; weight: [D, W]; bias: [D] or None.  Returns (y [B, D], new
+    conv_state) in fp64; the input state is not modified."""
+    x = _f64(x)
+    B, D = x.shape
+    weight = _f64(weight).reshape(D, -1)
+    W = weight.shape[1]
+    idx = np.ascontiguousarray(state_idx, np.int64)
+    if W > 1:
+        cs = np.array(conv_state, np.float64, copy=True, order="C").reshape(-1, W - 1, D)
+        P = cs.shape[0]
+    else:   # width 1: no state
+        cs, P = None, np.iinfo(np.int64).max
+    y = np.zeros((B, D))
+    rc = _load().kda_oracle_conv_update(_ptr(x), _ptr(cs), _ptr(weight),
+                                        _ptr(None if bias is None else _f64(bias)), _ptr(idx),
+                                        B, D, W, P, _ptr(y))
+    if rc != 0:
+        raise ValueError("kda_oracle_conv_update rejected its arguments")
+    return y, cs
+
+
+def conv_decode(mixed_qkv, conv_state, conv_weight, conv_bias, a, b, A_log, dt_bias, pool,
+                state_idx, H, HV, K, V, scale=None, l2norm=True, n_threads=None):
+    """The short convolution, then one decode step on its output (both slots
+    addressed by state_idx).  Returns (o [B,HV,V], new pool, new conv_state)."""
+    y, cs = conv_update(mixed_qkv, conv_state, conv_weight, conv_bias, state_idx)
+    o, newpool = decode(y, a, b, A_log, dt_bias, pool, state_idx, H, HV, K, V, scale=scale,
+                        l2norm=l2norm, n_threads=n_threads)
+    return o, newpool, cs

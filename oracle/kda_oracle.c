@@ -226,3 +226,48 @@ int kda_oracle_decode(const double *qkv, const double *a, const double *b,
     return kda_oracle_extend(qkv, a, b, A_log, dt_bias, pool, state_idx, B, 1, H, HV, K, V, P,
                              scale, l2norm, o, n_threads);
 }
+
+/*
+ * Short causal convolution before decode, one new input per row ([SGL-PR],
+ * backend integration: causal_conv1d_update on the packed projections with
+ * activation "silu" and per-row conv-state slots given by the same cache
+ * indices as the recurrent state).  The page names the call without defining
+ * it; this is the plain depthwise causal convolution of width W whose state
+ * holds each channel's last W-1 inputs.  Per channel c of row n with slot
+ * idx = state_idx[n] >= 0:
+ *   window = (cs[idx, 0, c], ..., cs[idx, W-2, c], x[n, c])    oldest first
+ *   y[n, c] = silu(bias[c] + sum_w weight[c, w] * window[w]),  silu(z) = z / (1 + e^-z)
+ *   cs[idx, :, c] <- window[1 .. W-1]
+ * A pad row (idx < 0) gives y = 0 and writes no state.
+ *   x [B, D]   conv_state [P, W-1, D]   weight [D, W]   bias [D] or NULL   y [B, D]
+ */
+int kda_oracle_conv_update(const double *x, double *conv_state, const double *weight,
+                           const double *bias, const int64_t *state_idx, int B, int D, int W,
+                           int64_t P, double *y)
+{
+    if (!x || !weight || !state_idx || !y || (W > 1 && !conv_state)) return -1;
+    if (B < 0 || D <= 0 || W < 1) return -1;
+    double *win = (double *)malloc(sizeof(double) * (size_t)W);
+    if (!win) return -1;
+    int err = 0;
+    for (int n = 0; n < B; ++n) {
+        const int64_t idx = state_idx[n];
+        double *yn = y + (int64_t)n * D;
+        if (idx < 0) {
+            for (int c = 0; c < D; ++c) yn[c] = 0.0;
+            continue;
+        }
+        if (idx >= P) { err = 1; continue; }
+        double *cs = conv_state ? conv_state + idx * (int64_t)(W - 1) * D : NULL;
+        for (int c = 0; c < D; ++c) {
+            for (int w = 0; w < W - 1; ++w) win[w] = cs[(int64_t)w * D + c];
+            win[W - 1] = x[(int64_t)n * D + c];
+            double z = bias ? bias[c] : 0.0;
+            for (int w = 0; w < W; ++w) z += weight[(int64_t)c * W + w] * win[w];
+            yn[c] = z / (1.0 + exp(-z));
+            for (int w = 0; w < W - 1; ++w) cs[(int64_t)w * D + c] = win[w + 1];
+        }
+    }
+    free(win);
+    return err ? -1 : 0;
+}

@@ -415,6 +415,71 @@ def test_extend_equals_successive_decode_steps():
 
 
 # ----------------------------------------------------------------------------
+# short convolution before decode (I15): width 1 is silu of an affine map;
+# T updates from a zero state are the causal convolution of the whole input
+# sequence (numpy's convolve), and the state ends holding the last W-1 inputs;
+# pads give zero and leave their slots alone.
+# ----------------------------------------------------------------------------
+def test_conv_update_width1_is_silu():
+    from scipy.special import expit
+    r = RNG(71)
+    B, D = 5, 12
+    x, w, bias = r.standard_normal((B, D)), r.standard_normal((D, 1)), r.standard_normal(D)
+    idx = np.arange(B)
+    idx[3] = -1
+    y, _ = oracle.conv_update(x, None, w, bias, idx)
+    z = w[:, 0] * x + bias
+    want = z * expit(z)
+    want[3] = 0.0
+    assert close(y, want, 1e-15)
+
+
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_conv_updates_are_a_causal_convolution(W):
+    r = RNG(72 + W)
+    B, D, T, P = 4, 10, 9, 7
+    xs = r.standard_normal((T, B, D))
+    w, bias = r.standard_normal((D, W)), r.standard_normal(D)
+    idx = np.array([5, -1, 0, 3])
+    cs0 = r.standard_normal((P, W - 1, D))
+    cs0[idx[idx >= 0]] = 0.0                      # live slots start empty
+    cs = cs0
+    ys = []
+    for t in range(T):
+        y, cs = oracle.conv_update(xs[t], cs, w, bias, idx)
+        ys.append(y)
+    ys = np.stack(ys)                             # [T, B, D]
+    for n in range(B):
+        if idx[n] < 0:
+            assert not ys[:, n].any()
+            continue
+        for c in range(D):
+            z = bias[c] + np.convolve(xs[:, n, c], w[c, ::-1])[:T]
+            assert close(ys[:, n, c], z / (1 + np.exp(-z)), 1e-13)
+        assert np.array_equal(cs[idx[n]], xs[T - W + 1:, n, :])
+    others = np.setdiff1d(np.arange(P), idx[idx >= 0])
+    assert np.array_equal(cs[others], cs0[others])
+
+
+def test_conv_decode_composes():
+    r = RNG(75)
+    B, H, HV, K, V, P, W = 3, 1, 2, 8, 4, 5, 4
+    D = 2 * H * K + HV * V
+    x = r.standard_normal((B, D))
+    cs = r.standard_normal((P, W - 1, D))
+    w, bias = r.standard_normal((D, W)), r.standard_normal(D)
+    d = dict(a=r.standard_normal((B, HV * K)), b=r.standard_normal((B, HV)),
+             A_log=r.uniform(0, 1, HV), dt_bias=r.uniform(-1, 1, HV * K))
+    pool = 0.3 * r.standard_normal((P, HV, V, K))
+    idx = np.array([4, -1, 1])
+    o, newpool, newcs = oracle.conv_decode(x, cs, w, bias, **d, pool=pool, state_idx=idx, H=H, HV=HV,
+                                           K=K, V=V, n_threads=1)
+    y, cs2 = oracle.conv_update(x, cs, w, bias, idx)
+    o2, p2 = oracle.decode(y, **d, pool=pool, state_idx=idx, H=H, HV=HV, K=K, V=V, n_threads=1)
+    assert np.array_equal(o, o2) and np.array_equal(newpool, p2) and np.array_equal(newcs, cs2)
+
+
+# ----------------------------------------------------------------------------
 # level-1 references of the TileLang page (I11): they agree to fp64 rounding
 # (the page reports 1e-15-level max-abs and 1e-16-level rel-L2), and the two
 # deliberate structural bugs give O(1) errors.
