@@ -15,7 +15,8 @@ MI355X's HBM peak, `roofline_decode` the decode kernel.  `cpu_baseline` is the
 fp64 oracle (plain C, OpenMP over chains) timed on the host cores on the same
 prefill workload.  Outside the step, the pool-addressed prefill (same
 workload) and kda_decode_extend with T = 4 tokens per row (decode workload's
-rows, heads and pool) are timed the same way and reported as extra fields.
+rows, heads and pool) are timed the same way and reported as extra fields,
+as is kda_conv_decode_step (width-4 convolution fused with the decode step).
 """
 from __future__ import annotations
 
@@ -71,6 +72,15 @@ def extend_bytes(d, T):
 
 
 EXTEND_T = 4
+CONV_W = 4
+
+
+def conv_decode_bytes(d):
+    """decode_bytes plus the conv state read and written per live row and the
+    conv weights and bias read once."""
+    live = int((d.state_idx >= 0).sum())
+    D = 2 * d.H * d.K + d.HV * d.V
+    return decode_bytes(d) + 2 * 2 * (d.W - 1) * D * live + 2 * D * d.W + 2 * D
 
 
 def source_hash(files):
@@ -298,6 +308,32 @@ def main():
     ext_gbs = extend_bytes(de, EXTEND_T) / ext_avg / 1e9
     del epool
 
+    # the short convolution fused with the decode step (width 4) on the decode
+    # workload's rows, heads and pool, timed the same way
+    dc = synth.conv_decode(4, W=CONV_W, **{k_: v_ for k_, v_ in synth.DECODE_WORKLOAD.items() if k_ != "name"})
+    dcin = dict(mixed_qkv=bf16(dc.qkv), conv_state=bf16(dc.conv_state), conv_weight=bf16(dc.conv_weight),
+                conv_bias=bf16(dc.conv_bias), a=bf16(dc.a), b=bf16(dc.b),
+                A_log=torch.from_numpy(dc.A_log).to(dev), dt_bias=torch.from_numpy(dc.dt_bias).to(dev))
+    cpool = torch.from_numpy(dc.pool).to(dev)
+    cidx = torch.from_numpy(dc.state_idx).to(dev)
+
+    def conv_decode_call():
+        kda.conv_decode_step(**dcin, state_pool=cpool, state_idx=cidx, num_heads=dc.H,
+                             num_v_heads=dc.HV, scale=dc.scale, o=od)
+
+    for _ in range(2):
+        conv_decode_call()
+    evc = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evc[0].record()
+    for s_ in range(K):
+        conv_decode_call()
+        evc[s_ + 1].record()
+    torch.cuda.synchronize()
+    conv_avg = float(np.mean([evc[s_].elapsed_time(evc[s_ + 1]) for s_ in range(K)])) * 1e-3
+    conv_gbs = conv_decode_bytes(dc) / conv_avg / 1e9
+    del cpool, dcin
+
     tokheads = p.tokens * p.H
     flops = tokheads * prefill_flops_per_tokhead(p.dk, p.dv)
     pbytes = prefill_bytes(p)
@@ -352,6 +388,10 @@ def main():
         "extend_us": round(ext_avg * 1e6, 2),
         "extend_gbs": round(ext_gbs, 1),
         "extend_hbm_frac": round(ext_gbs / HBM_PEAK_GBS, 4),
+        "conv_decode_W": CONV_W,
+        "conv_decode_us": round(conv_avg * 1e6, 2),
+        "conv_decode_gbs": round(conv_gbs, 1),
+        "conv_decode_hbm_frac": round(conv_gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "chunk_fwd_kernel<bf16,128,128>",

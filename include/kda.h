@@ -9,7 +9,9 @@
  *                       pool (read and updated in place through slot indices);
  *   kda_decode_step     one fused T=1 decode step over a pool of states;
  *   kda_decode_extend   T tokens per row applied to the pool states in one
- *                       launch (short extends, speculative verification).
+ *                       launch (short extends, speculative verification);
+ *   kda_conv_decode_step  the short causal convolution before decode fused
+ *                       with the decode step.
  *
  * The method ([TL-KDA] section 1): per (sequence, head), with the state S
  * stored as (d_v, d_k),
@@ -34,7 +36,8 @@
  *   - The calls enqueue work on `stream` and return without synchronising;
  *     results are ready once the caller synchronises the stream.  A kernel
  *     fault surfaces at that synchronisation.
- *   - kda_decode_step and kda_decode_extend allocate nothing.  kda_chunk_fwd(_pool) uses a device
+ *   - kda_decode_step, kda_decode_extend and kda_conv_decode_step allocate
+ *     nothing.  kda_chunk_fwd(_pool) uses a device
  *     workspace (ring buffers and flags for its producer/consumer teams,
  *     about 64 MiB) that the library allocates on the first call on each
  *     device and keeps until the process exits; calls that overlap in time
@@ -205,6 +208,39 @@ int kda_decode_extend(const void *qkv, const void *a, const void *b,
                       float *state_pool, const int32_t *state_idx, void *o,
                       int B, int T, int H, int HV, int K, int V, int P,
                       float scale, int flags, hipStream_t stream);
+
+/*
+ * kda_conv_decode_step -- the short causal convolution that produces the
+ * packed q/k/v row, fused with one decode step ([SGL-PR], backend
+ * integration: causal_conv1d_update with activation silu on mixed_qkv, its
+ * conv-state slots addressed by the same cache indices as the recurrent
+ * state, then the packed decode; there they are two launches).
+ *
+ * For every live row n (slot idx = state_idx[n]) and channel c of the packed
+ * row (D = 2*H*K + HV*V channels):
+ *   window = (conv_state[idx, 0, c], ..., conv_state[idx, W-2, c], mixed_qkv[n, c])
+ *   y[c]   = silu(conv_bias[c] + sum_w conv_weight[c, w] * window[w]),
+ *   conv_state[idx, :, c] <- window[1 .. W-1],
+ * computed in fp32, and y (not rounded) is the qkv row of kda_decode_step's
+ * update, which then updates state_pool[idx] and writes o[n].  A pad row
+ * (idx < 0) gets zero outputs and touches neither state.
+ *
+ * Layout:
+ *   mixed_qkv   : [B, D] bf16 (q heads, k heads, v heads, before the conv)
+ *   conv_state  : [P, W-1, D] bf16, updated in place (oldest input first)
+ *   conv_weight : [D, W] bf16       conv_bias : [D] bf16, or NULL for none
+ *   a, b, A_log, dt_bias, state_pool, state_idx, o, scale, flags: as in
+ *                 kda_decode_step (P slots for both states).
+ *   K, V        : 128 each.  W: 2, 3 or 4.  HV % H == 0 and HV/H <= 126.
+ * Returns KDA_OK or a negative kda_status.
+ */
+int kda_conv_decode_step(const void *mixed_qkv, void *conv_state,
+                         const void *conv_weight, const void *conv_bias,
+                         const void *a, const void *b,
+                         const float *A_log, const float *dt_bias,
+                         float *state_pool, const int32_t *state_idx, void *o,
+                         int B, int H, int HV, int K, int V, int W, int P,
+                         float scale, int flags, hipStream_t stream);
 
 /*
  * kda_chunk_fwd_check -- synchronise `stream` and report whether the last

@@ -20,7 +20,7 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_check", "kda_decode_step",
-           "kda_decode_extend", "kda_status_str")
+           "kda_decode_extend", "kda_conv_decode_step", "kda_status_str")
 
 
 class KDAError(RuntimeError):
@@ -45,6 +45,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_step.restype = I
     lib.kda_decode_extend.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.kda_decode_extend.restype = I
+    lib.kda_conv_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.kda_conv_decode_step.restype = I
     lib.kda_chunk_fwd_check.argtypes = [P]
     lib.kda_chunk_fwd_check.restype = I
     lib.kda_status_str.argtypes = [I]
@@ -233,4 +235,47 @@ def decode_extend(qkv, a, b, A_log, dt_bias, state_pool, state_idx, num_heads: i
         _ptr(qkv), _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state_pool),
         _ptr(state_idx), _ptr(o), B, T, H, HV, K, V, state_pool.shape[0], float(scale),
         KDA_DECODE_L2NORM if l2norm else 0, ctypes.c_void_p(stream)))
+    return o
+
+
+def conv_decode_step(mixed_qkv, conv_state, conv_weight, conv_bias, a, b, A_log, dt_bias,
+                     state_pool, state_idx, num_heads: int, num_v_heads: int, head_k_dim: int = 128,
+                     head_v_dim: int = 128, scale=None, l2norm: bool = True, o=None, stream=None):
+    """The short causal convolution (silu) fused with one decode step; both
+    `conv_state` [P, W-1, D] bf16 and `state_pool` [P, HV, V, K] float32 are
+    updated in place for the live rows.  mixed_qkv: [B, D] bf16 before the
+    conv; conv_weight: [D, W] bf16; conv_bias: [D] bf16 or None; the other
+    arguments as in decode_step.  Returns o [B, HV, V] bf16."""
+    B = mixed_qkv.shape[0]
+    H, HV, K, V = num_heads, num_v_heads, head_k_dim, head_v_dim
+    D = 2 * H * K + HV * V
+    for name, t in (("mixed_qkv", mixed_qkv), ("conv_state", conv_state), ("conv_weight", conv_weight),
+                    ("conv_bias", conv_bias), ("a", a), ("b", b)):
+        _dev(name, t, torch.bfloat16)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("state_pool", state_pool)):
+        _dev(name, t, torch.float32)
+    _dev("state_idx", state_idx, torch.int32)
+    if conv_weight.dim() != 2 or conv_weight.shape[0] != D:
+        raise KDAError("conv_weight must be [D, W]")
+    W = conv_weight.shape[1]
+    P = state_pool.shape[0]
+    if mixed_qkv.shape[-1] != D or mixed_qkv.numel() != B * D or a.numel() != B * HV * K \
+            or b.numel() != B * HV or tuple(state_pool.shape[1:]) != (HV, V, K) \
+            or state_idx.numel() != B or A_log.numel() != HV or dt_bias.numel() != HV * K \
+            or tuple(conv_state.shape) != (P, W - 1, D) \
+            or (conv_bias is not None and conv_bias.numel() != D):
+        raise KDAError("inconsistent conv-decode shapes")
+    if scale is None:
+        scale = K ** -0.5
+    if o is None:
+        o = torch.empty((B, HV, V), dtype=torch.bfloat16, device=mixed_qkv.device)
+    _dev("o", o, torch.bfloat16)
+    if o.numel() != B * HV * V:
+        raise KDAError("o must hold [B, HV, V] elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(mixed_qkv.device).cuda_stream
+    _check(load_library().kda_conv_decode_step(
+        _ptr(mixed_qkv), _ptr(conv_state), _ptr(conv_weight), _ptr(conv_bias), _ptr(a), _ptr(b),
+        _ptr(A_log), _ptr(dt_bias), _ptr(state_pool), _ptr(state_idx), _ptr(o), B, H, HV, K, V, W, P,
+        float(scale), KDA_DECODE_L2NORM if l2norm else 0, ctypes.c_void_p(stream)))
     return o

@@ -173,4 +173,31 @@ int kda_decode_extend(const void *qkv, const void *a, const void *b, const float
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+int kda_conv_decode_step(const void *mixed_qkv, void *conv_state, const void *conv_weight,
+                         const void *conv_bias, const void *a, const void *b, const float *A_log,
+                         const float *dt_bias, float *state_pool, const int32_t *state_idx, void *o,
+                         int B, int H, int HV, int K, int V, int W, int P, float scale, int flags,
+                         hipStream_t stream)
+{
+    if (K != 128 || V != 128 || W < 2 || W > 4) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || H <= 0 || HV <= 0 || HV % H != 0 || P < 0) return KDA_ERR_SHAPE;
+    if ((long long)B * HV > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    // the conv outputs of one workgroup (q, k and HV/H value heads, fp32) sit in LDS
+    if (sizeof(float) * (2LL * K + (long long)(HV / H) * V) > 65536) return KDA_ERR_UNSUPPORTED;
+    if (B == 0) return KDA_OK;
+    if (!mixed_qkv || !conv_state || !conv_weight || !a || !b || !A_log || !dt_bias || !state_pool ||
+        !state_idx || !o)
+        return KDA_ERR_NULL;
+    const void *ptrs[] = {mixed_qkv, conv_state, conv_weight, conv_bias, a, b, A_log, dt_bias,
+                          state_pool, state_idx, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    const hipError_t e = kda::launch_conv_decode(
+        static_cast<const uint16_t *>(mixed_qkv), static_cast<uint16_t *>(conv_state),
+        static_cast<const uint16_t *>(conv_weight), static_cast<const uint16_t *>(conv_bias),
+        static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), A_log, dt_bias, state_pool,
+        state_idx, static_cast<uint16_t *>(o), B, H, HV, W, scale, flags & KDA_DECODE_L2NORM, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

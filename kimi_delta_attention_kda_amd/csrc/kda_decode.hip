@@ -70,21 +70,18 @@ struct TokenPrep {
     float kq, beta;
 };
 
-template <int V_>
-__device__ __forceinline__ void token_prep(TokenPrep &p, const TokenRaw<V_> &t, const f32x4 (&dt)[2],
-                                           float A, float scale, int l2norm)
+// The rest of the per-token values once p.qv and p.kv hold the raw q and k
+// channels: the decay from the thread's a channels (bf16 pairs) and dt_bias,
+// the optional L2 norm, the q scale, k.q and beta.
+__device__ __forceinline__ void prep_core(TokenPrep &p, const uint2 (&ab)[2], uint16_t braw,
+                                          const f32x4 (&dt)[2], float A, float scale, int l2norm)
 {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint32_t qw[2] = {t.qb[h].x, t.qb[h].y}, kw[2] = {t.kb[h].x, t.kb[h].y},
-                       aw[2] = {t.ab[h].x, t.ab[h].y};
+        const uint32_t aw[2] = {ab[h].x, ab[h].y};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const uint16_t qe = (uint16_t)(qw[e >> 1] >> (16 * (e & 1)));
-            const uint16_t ke = (uint16_t)(kw[e >> 1] >> (16 * (e & 1)));
             const uint16_t ae = (uint16_t)(aw[e >> 1] >> (16 * (e & 1)));
-            p.qv[4 * h + e] = bf16_to_f32(qe);
-            p.kv[4 * h + e] = bf16_to_f32(ke);
             p.eg[4 * h + e] = gate_decay(bf16_to_f32(ae) + dt[h][e], A);
         }
     }
@@ -102,7 +99,23 @@ __device__ __forceinline__ void token_prep(TokenPrep &p, const TokenRaw<V_> &t, 
 #pragma unroll
     for (int c = 0; c < 8; ++c) { p.qv[c] *= scale; kq += p.kv[c] * p.qv[c]; }
     p.kq = row16_sum(kq);
-    p.beta = sigmoid_f(bf16_to_f32(t.braw));
+    p.beta = sigmoid_f(bf16_to_f32(braw));
+}
+
+template <int V_>
+__device__ __forceinline__ void token_prep(TokenPrep &p, const TokenRaw<V_> &t, const f32x4 (&dt)[2],
+                                           float A, float scale, int l2norm)
+{
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t qw[2] = {t.qb[h].x, t.qb[h].y}, kw[2] = {t.kb[h].x, t.kb[h].y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p.qv[4 * h + e] = bf16_to_f32((uint16_t)(qw[e >> 1] >> (16 * (e & 1))));
+            p.kv[4 * h + e] = bf16_to_f32((uint16_t)(kw[e >> 1] >> (16 * (e & 1))));
+        }
+    }
+    prep_core(p, t.ab, t.braw, dt, A, scale, l2norm);
 }
 
 // The state rows of one token on the thread's registers s (rows g + 16 r of
@@ -111,7 +124,7 @@ __device__ __forceinline__ void token_prep(TokenPrep &p, const TokenRaw<V_> &t, 
 // can store it at once.
 template <int V_, typename RowFn>
 __device__ __forceinline__ void token_rows(f32x4 (&s)[V_ / 32][2], const TokenPrep &p,
-                                           const uint16_t (&vraw)[V_ / 32], RowFn &&row_done)
+                                           const float (&v)[V_ / 32], RowFn &&row_done)
 {
     constexpr int ROWS = V_ / 32;
 #pragma unroll
@@ -128,7 +141,7 @@ __device__ __forceinline__ void token_rows(f32x4 (&s)[V_ / 32][2], const TokenPr
             }
         pk = row16_sum(pk);
         pq = row16_sum(pq);
-        const float u = p.beta * (bf16_to_f32(vraw[r]) - pk);
+        const float u = p.beta * (v[r] - pk);
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -190,7 +203,10 @@ __global__ __launch_bounds__(512) void decode_kernel(
     const float A = __builtin_amdgcn_exp2f(A_l * kLog2e);
     TokenPrep pr;
     token_prep<V_>(pr, tk, dt, A, scale, l2norm);
-    token_rows<V_>(s, pr, tk.vraw, [&](int r, float ov) {
+    float vf[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) vf[r] = bf16_to_f32(tk.vraw[r]);
+    token_rows<V_>(s, pr, vf, [&](int r, float ov) {
         const int row = g + 16 * r;
         float *dst = S + (size_t)row * K_;
         __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
@@ -357,10 +373,10 @@ __global__ __launch_bounds__(512) void extend_kernel(
             const float2 ks = prep_s[tt];
             pr.kq = ks.x;
             pr.beta = ks.y;
-            uint16_t vraw[ROWS];
+            float vf[ROWS];
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) vraw[r] = st16[tt * (UNITS * 8) + 3 * K_ + r0 + g + 16 * r];
-            token_rows<V_>(s, pr, vraw, [&](int r, float ov) {
+            for (int r = 0; r < ROWS; ++r) vf[r] = bf16_to_f32(st16[tt * (UNITS * 8) + 3 * K_ + r0 + g + 16 * r]);
+            token_rows<V_>(s, pr, vf, [&](int r, float ov) {
                 if (j == 0) os16[tt * V_ + r0 + g + 16 * r] = f32_to_bf16(ov);
             });
         }
@@ -375,6 +391,147 @@ __global__ __launch_bounds__(512) void extend_kernel(
         float *dst = S + (size_t)(g + 16 * r) * K_;
         __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
         __builtin_nontemporal_store(s[r][1], reinterpret_cast<f32x4 *>(dst + 64 + 4 * j));
+    }
+}
+
+// The short causal convolution before decode, fused with the decode step.
+// [SGL-PR] (backend integration) runs causal_conv1d_update with silu on the
+// packed projections as a launch of its own before the packed decode, its
+// conv-state slots addressed by the same cache indices as the recurrent
+// state.  Per channel c of a live row:
+//   window = (cs[0, c], ..., cs[W-2, c], x[c])     oldest first
+//   y[c]   = silu(bias[c] + sum_w weight[c, w] window[w]);  cs <- window[1 ..]
+// and y takes the place of the packed q/k/v row of the decode step.
+//
+// One 512-thread workgroup per (row, q/k head): it convolves the q and k
+// channels of that head and the v channels of the HV/H value heads that read
+// it, so every conv-state channel has exactly one workgroup, which reads it
+// before writing it.  y stays in LDS in fp32; the decode step of each of
+// those value heads then runs on the T=1 kernel's thread layout.  The first
+// value head's activation and state loads are issued before the convolution
+// is computed, so its latency hides behind them.
+template <int K_, int V_, int W_>
+__global__ __launch_bounds__(512) void conv_decode_kernel(
+    const uint16_t *__restrict__ x, uint16_t *__restrict__ conv_state,
+    const uint16_t *__restrict__ cw, const uint16_t *__restrict__ cb,
+    const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
+    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float *__restrict__ pool,
+    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV,
+    float scale, int l2norm)
+{
+    static_assert(K_ == 128 && V_ == 128, "conv decode kernel is built for K = V = 128");
+    static_assert(W_ >= 2 && W_ <= 4, "conv width 2..4");
+    constexpr int ROWS = V_ / 32;
+    extern __shared__ float ybuf[];  // [q: K | k: K | v: G V] conv outputs, fp32
+    const int n = blockIdx.x / H;
+    const int hq = blockIdx.x - n * H;
+    const int G = HV / H;
+    const int tid = threadIdx.x & 255;
+    const int r0 = (threadIdx.x >> 8) * (V_ / 2);
+    const int j = tid & 15;
+    const int g = tid >> 4;
+    const size_t D = 2 * (size_t)H * K_ + (size_t)HV * V_;
+    const int nch = 2 * K_ + G * V_;
+
+    const int idx = state_idx[n];
+    if (idx < 0) {  // pad row: zero outputs, no state access
+        for (int i = threadIdx.x; i < G * V_; i += 512) o[((size_t)n * HV + (size_t)hq * G) * V_ + i] = 0;
+        return;
+    }
+
+    // channel ch of this workgroup -> column of the packed row
+    auto column = [&](int ch) -> size_t {
+        return ch < K_       ? (size_t)hq * K_ + ch
+               : ch < 2 * K_ ? (size_t)H * K_ + (size_t)hq * K_ + (ch - K_)
+                             : 2 * (size_t)H * K_ + (size_t)hq * G * V_ + (ch - 2 * K_);
+    };
+    const uint16_t *xrow = x + (size_t)n * D;
+    uint16_t *cs = conv_state + (size_t)idx * (W_ - 1) * D;
+    struct ConvIn {
+        uint16_t xv, st[W_ - 1], wt[W_], bias;
+    };
+    auto conv_load = [&](int ch) {
+        ConvIn c;
+        const size_t col = column(ch);
+        c.xv = xrow[col];
+#pragma unroll
+        for (int w = 0; w < W_ - 1; ++w) c.st[w] = cs[(size_t)w * D + col];
+#pragma unroll
+        for (int w = 0; w < W_; ++w) c.wt[w] = cw[col * W_ + w];
+        c.bias = cb ? cb[col] : (uint16_t)0;
+        return c;
+    };
+    auto conv_finish = [&](int ch, const ConvIn &c) {
+        const size_t col = column(ch);
+        float z = bf16_to_f32(c.bias);
+#pragma unroll
+        for (int w = 0; w < W_ - 1; ++w) z += bf16_to_f32(c.wt[w]) * bf16_to_f32(c.st[w]);
+        z += bf16_to_f32(c.wt[W_ - 1]) * bf16_to_f32(c.xv);
+        ybuf[ch] = z / (1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+#pragma unroll
+        for (int w = 0; w < W_ - 1; ++w) cs[(size_t)w * D + col] = w + 1 < W_ - 1 ? c.st[w + 1] : c.xv;
+    };
+
+    // per value head: its a, dt_bias, b, A_log and state rows
+    uint2 ab[2];
+    f32x4 dt[2];
+    uint16_t braw;
+    float A_l;
+    f32x4 s[ROWS][2];
+    float *S;
+    auto head_load = [&](int gi) {
+        const int hv = hq * G + gi;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            ab[h] = *reinterpret_cast<const uint2 *>(a + ((size_t)n * HV + hv) * K_ + 4 * j + 64 * h);
+            dt[h] = *reinterpret_cast<const f32x4 *>(dt_bias + (size_t)hv * K_ + 4 * j + 64 * h);
+        }
+        braw = b[(size_t)n * HV + hv];
+        A_l = A_log[hv];
+        __builtin_amdgcn_sched_barrier(0);  // activations ahead of the state loads
+        S = pool + ((size_t)idx * HV + hv) * (size_t)(V_ * K_) + (size_t)r0 * K_;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const float *row = S + (size_t)(g + 16 * r) * K_;
+            s[r][0] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 4 * j));
+            s[r][1] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 + 4 * j));
+        }
+    };
+
+    ConvIn c0;
+    const bool has0 = (int)threadIdx.x < nch;
+    if (has0) c0 = conv_load(threadIdx.x);
+    head_load(0);
+    if (has0) conv_finish(threadIdx.x, c0);
+    for (int ch = threadIdx.x + 512; ch < nch; ch += 512) conv_finish(ch, conv_load(ch));
+    __syncthreads();  // y complete in LDS
+
+    for (int gi = 0; gi < G; ++gi) {
+        if (gi > 0) head_load(gi);
+        const int hv = hq * G + gi;
+        TokenPrep pr;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4 *>(ybuf + 4 * j + 64 * h);
+            const f32x4 k4 = *reinterpret_cast<const f32x4 *>(ybuf + K_ + 4 * j + 64 * h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                pr.qv[4 * h + e] = q4[e];
+                pr.kv[4 * h + e] = k4[e];
+            }
+        }
+        prep_core(pr, ab, braw, dt, __builtin_amdgcn_exp2f(A_l * kLog2e), scale, l2norm);
+        float vf[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) vf[r] = ybuf[2 * K_ + gi * V_ + r0 + g + 16 * r];
+        uint16_t *orow = o + ((size_t)n * HV + hv) * V_;
+        token_rows<V_>(s, pr, vf, [&](int r, float ov) {
+            const int row = g + 16 * r;
+            float *dst = S + (size_t)row * K_;
+            __builtin_nontemporal_store(s[r][0], reinterpret_cast<f32x4 *>(dst + 4 * j));
+            __builtin_nontemporal_store(s[r][1], reinterpret_cast<f32x4 *>(dst + 64 + 4 * j));
+            if (j == 0) orow[r0 + row] = f32_to_bf16(ov);
+        });
     }
 }
 
@@ -395,6 +552,32 @@ hipError_t launch_extend(const uint16_t *qkv, const uint16_t *a, const uint16_t 
 {
     hipLaunchKernelGGL((extend_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(512), 0, stream,
                        qkv, a, b, A_log, dt_bias, pool, state_idx, o, T, H, HV, scale, l2norm);
+    return hipGetLastError();
+}
+
+hipError_t launch_conv_decode(const uint16_t *x, uint16_t *conv_state, const uint16_t *cw,
+                              const uint16_t *cb, const uint16_t *a, const uint16_t *b,
+                              const float *A_log, const float *dt_bias, float *pool,
+                              const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int W,
+                              float scale, int l2norm, hipStream_t stream)
+{
+    const size_t lds = sizeof(float) * (2 * 128 + (size_t)(HV / H) * 128);
+    const dim3 grid((unsigned)(B * H)), block(512);
+    switch (W) {
+    case 2:
+        hipLaunchKernelGGL((conv_decode_kernel<128, 128, 2>), grid, block, lds, stream, x, conv_state, cw, cb, a,
+                           b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+        break;
+    case 3:
+        hipLaunchKernelGGL((conv_decode_kernel<128, 128, 3>), grid, block, lds, stream, x, conv_state, cw, cb, a,
+                           b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+        break;
+    case 4:
+        hipLaunchKernelGGL((conv_decode_kernel<128, 128, 4>), grid, block, lds, stream, x, conv_state, cw, cb, a,
+                           b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+        break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

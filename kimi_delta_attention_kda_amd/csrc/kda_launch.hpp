@@ -34,6 +34,12 @@ hipError_t launch_extend(const uint16_t *qkv, const uint16_t *a, const uint16_t 
                          const int32_t *state_idx, uint16_t *o, int B, int T, int H, int HV,
                          float scale, int l2norm, hipStream_t stream);
 
+hipError_t launch_conv_decode(const uint16_t *x, uint16_t *conv_state, const uint16_t *cw,
+                              const uint16_t *cb, const uint16_t *a, const uint16_t *b,
+                              const float *A_log, const float *dt_bias, float *pool,
+                              const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int W,
+                              float scale, int l2norm, hipStream_t stream);
+
 struct ChunkArgs {
     const void *q, *k, *v, *g_raw, *beta_raw;
     const float *A_log, *dt_bias, *h0;

@@ -336,6 +336,43 @@ def extend(seed: int, B: int, T: int, H: int, HV: int, K: int, V: int, P: int, n
                   meta=dict(seed=seed, T=T))
 
 
+@dataclass
+class ConvDecode(Decode):
+    """A decode workload whose qkv row is the input of the short convolution
+    (mixed_qkv), with the convolution's state, weights and bias."""
+    W: int = 4
+    conv_state: np.ndarray = None   # [P, W-1, D] bf16 bits
+    conv_weight: np.ndarray = None  # [D, W] bf16 bits
+    conv_bias: np.ndarray = None    # [D] bf16 bits, or None
+
+    def f64(self) -> dict:
+        out = super().f64()
+        out.update(conv_state=bf16_to_f32(self.conv_state).astype(np.float64),
+                   conv_weight=bf16_to_f32(self.conv_weight).astype(np.float64),
+                   conv_bias=None if self.conv_bias is None else bf16_to_f32(self.conv_bias).astype(np.float64))
+        return out
+
+
+def conv_decode(seed: int, B: int, H: int, HV: int, K: int, V: int, P: int, n_pad: int, W: int = 4, *,
+                bias: bool = True, name: str = "custom") -> ConvDecode:
+    """Draw a decode workload with the short convolution in front: as `decode`
+    (mixed_qkv ~ N(0,1) in place of qkv), then the conv state ~ N(0,1) (earlier
+    inputs of the same kind) and weights and bias ~ U(-1/sqrt(W), 1/sqrt(W))
+    (the default initialisation of a depthwise convolution of width W)."""
+    d = decode(seed, B=B, H=H, HV=HV, K=K, V=V, P=P, n_pad=n_pad, name=name)
+    rng = np.random.default_rng(seed + 1000)
+    D = 2 * H * K + HV * V
+    st = _Streams(seed + 1000)
+    cs = st.normal((P, W - 1, D))
+    lim = 1.0 / np.sqrt(W)
+    w = rng.uniform(-lim, lim, size=(D, W)).astype(np.float32)
+    cb = rng.uniform(-lim, lim, size=D).astype(np.float32) if bias else None
+    return ConvDecode(**{f: getattr(d, f) for f in ("name", "B", "H", "HV", "K", "V", "P", "qkv", "a", "b",
+                                                     "A_log", "dt_bias", "pool", "state_idx", "meta")},
+                      W=W, conv_state=bf16_bits(cs), conv_weight=bf16_bits(w),
+                      conv_bias=None if cb is None else bf16_bits(cb))
+
+
 DECODE_WORKLOAD = dict(name="decode-bf16 B256 H32 HV32 K128 V128 pool512 pad8",
                        B=256, H=32, HV=32, K=128, V=128, P=512, n_pad=8)
 

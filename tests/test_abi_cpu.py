@@ -127,6 +127,28 @@ def test_decode_extend_validation(lib):
     assert extend(lib, B=0) == 0
 
 
+def conv_decode(lib, **kw):
+    args = dict(x=A, cs=A, cw=A, cb=None, a=A, b=A, A_log=B, dt=B, pool=A, idx=A, o=A, B=4, H=2, HV=4,
+                K=128, V=128, W=4, P=8, scale=0.1, flags=1)
+    args.update(kw)
+    return lib.kda_conv_decode_step(args["x"], args["cs"], args["cw"], args["cb"], args["a"], args["b"],
+                                    args["A_log"], args["dt"], args["pool"], args["idx"], args["o"],
+                                    args["B"], args["H"], args["HV"], args["K"], args["V"], args["W"],
+                                    args["P"], args["scale"], args["flags"], None)
+
+
+def test_conv_decode_validation(lib):
+    assert conv_decode(lib, W=5) == -3
+    assert conv_decode(lib, W=1) == -3
+    assert conv_decode(lib, K=64) == -3
+    assert conv_decode(lib, H=1, HV=127) == -3        # conv outputs of a workgroup exceed 64 KiB of LDS
+    assert conv_decode(lib, HV=3) == -2               # HV % H != 0
+    assert conv_decode(lib, cs=None) == -1
+    assert conv_decode(lib, cw=None) == -1
+    assert conv_decode(lib, cb=MIS) == -4
+    assert conv_decode(lib, B=0) == 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 16, 1, 64)
