@@ -96,6 +96,10 @@ KERNEL_SOURCES = {
                   "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
     "decode": ["kimi_delta_attention_kda_amd/csrc/kda_decode.hip",
                "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
+    "extend": ["kimi_delta_attention_kda_amd/csrc/kda_decode.hip",
+               "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
+    "conv_decode": ["kimi_delta_attention_kda_amd/csrc/kda_decode.hip",
+                    "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
 }
 
 
@@ -113,7 +117,8 @@ def measured_traffic(kernel):
 
 
 COPY_CALIB_ELEMS = 64 << 20     # float32 elements read and written by the calibration copy
-KERNEL_MATCH = {"chunk_fwd": "chunk_fwd_kernel", "decode": "decode_kernel"}
+KERNEL_MATCH = {"chunk_fwd": "kda::chunk_fwd_kernel", "decode": "kda::decode_kernel",
+                "extend": "kda::extend_kernel", "conv_decode": "kda::conv_decode_kernel"}
 
 
 def _counter_rows(d):
@@ -388,10 +393,12 @@ def main():
         "extend_us": round(ext_avg * 1e6, 2),
         "extend_gbs": round(ext_gbs, 1),
         "extend_hbm_frac": round(ext_gbs / HBM_PEAK_GBS, 4),
+        "extend_traffic": measured_traffic("extend"),
         "conv_decode_W": CONV_W,
         "conv_decode_us": round(conv_avg * 1e6, 2),
         "conv_decode_gbs": round(conv_gbs, 1),
         "conv_decode_hbm_frac": round(conv_gbs / HBM_PEAK_GBS, 4),
+        "conv_decode_traffic": measured_traffic("conv_decode"),
         "roofline": {"bound": "hbm", "achieved": round(pre_gbs, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(pre_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "chunk_fwd_kernel<bf16,128,128>",
