@@ -45,6 +45,10 @@ def _load():
                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, P,
                                        ctypes.c_int, P, P, ctypes.c_int]
         lib.kda_oracle_fwd.restype = ctypes.c_int
+        lib.kda_oracle_fwd_states.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_double, P,
+                                              ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int]
+        lib.kda_oracle_fwd_states.restype = ctypes.c_int
         lib.kda_oracle_decode.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int64, ctypes.c_double, ctypes.c_int, P,
@@ -78,13 +82,15 @@ def default_threads() -> int:
 
 
 def fwd(q, k, v, a, b, A_log, dt_bias, h0=None, cu_seqlens=None, scale=None,
-        chains=None, n_threads=None, out=None):
+        chains=None, n_threads=None, out=None, chunk_states=None):
     """Token-recurrence forward over packed tokens.
 
     q,k,a: [T,H,dk]; v: [T,H,dv]; b: [T,H]; A_log: [H]; dt_bias: [H,dk];
     h0: [N,H,dv,dk] or None; cu_seqlens: [N+1] or None (one sequence).
     chains: optional iterable of chain ids (seq*H + head) to compute; other
     chains' outputs stay zero.  Returns (o [T,H,dv], hT [N,H,dv,dk]) in fp64.
+    chunk_states=C also returns the state entering every chunk of C tokens,
+    [sum_s ceil(len_s / C), H, dv, dk] (rows of the sequences in order).
     """
     q, k, v, a, b = (_f64(x) for x in (q, k, v, a, b))
     T, H, dk = q.shape
@@ -98,13 +104,25 @@ def fwd(q, k, v, a, b, A_log, dt_bias, h0=None, cu_seqlens=None, scale=None,
     o = np.zeros((T, H, dv)) if out is None else out
     hT = np.zeros((n_seq, H, dv, dk))
     ch = None if chains is None else np.ascontiguousarray(list(chains), np.int32)
-    rc = _load().kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
-                                _ptr(dt_bias), _ptr(h0), _ptr(cu), n_seq, H, dk, dv,
-                                float(scale), _ptr(ch), 0 if ch is None else len(ch),
-                                _ptr(o), _ptr(hT), int(n_threads or default_threads()))
+    nthr = int(n_threads or default_threads())
+    if chunk_states is None:
+        rc = _load().kda_oracle_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+                                    _ptr(dt_bias), _ptr(h0), _ptr(cu), n_seq, H, dk, dv,
+                                    float(scale), _ptr(ch), 0 if ch is None else len(ch),
+                                    _ptr(o), _ptr(hT), nthr)
+        if rc != 0:
+            raise ValueError("kda_oracle_fwd rejected its arguments")
+        return o, hT
+    C = int(chunk_states)
+    nc = int(((np.diff(cu) + C - 1) // C).sum())
+    hc = np.zeros((nc, H, dv, dk))
+    rc = _load().kda_oracle_fwd_states(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(b), _ptr(A_log),
+                                       _ptr(dt_bias), _ptr(h0), _ptr(cu), n_seq, H, dk, dv,
+                                       float(scale), _ptr(ch), 0 if ch is None else len(ch),
+                                       _ptr(o), _ptr(hT), _ptr(hc), C, nthr)
     if rc != 0:
-        raise ValueError("kda_oracle_fwd rejected its arguments")
-    return o, hT
+        raise ValueError("kda_oracle_fwd_states rejected its arguments")
+    return o, hT, hc
 
 
 def decode(qkv, a, b, A_log, dt_bias, pool, state_idx, H, HV, K, V, scale=None,

@@ -43,14 +43,19 @@ static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 /* One (sequence, head) chain of the token recurrence.
  * Activations are packed token-major: x[(tok*H + h)*d + c].
- * S is (dv, dk) row-major, updated in place. */
+ * S is (dv, dk) row-major, updated in place.
+ * Hc: NULL, or where the state before token t = C*i goes (for every i with
+ * C*i < len), at Hc + i * Hc_stride. */
 static void oracle_chain(const double *q, const double *k, const double *v,
                          const double *a, const double *b, double A_exp,
                          const double *dt, double *S, double *o,
                          int64_t tok0, int64_t len, int H, int h, int dk, int dv,
-                         double scale, double *eg, double *u)
+                         double scale, double *eg, double *u,
+                         double *Hc, int C, int64_t Hc_stride)
 {
     for (int64_t t = 0; t < len; ++t) {
+        if (Hc && t % C == 0)
+            memcpy(Hc + (t / C) * Hc_stride, S, sizeof(double) * (size_t)dv * dk);
         const int64_t tok = tok0 + t;
         const double *qt = q + (tok * H + h) * (int64_t)dk;
         const double *kt = k + (tok * H + h) * (int64_t)dk;
@@ -94,15 +99,16 @@ static void oracle_chain(const double *q, const double *k, const double *v,
  *           Outputs of chains not listed are left untouched.
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int kda_oracle_fwd(const double *q, const double *k, const double *v,
-                   const double *a, const double *b, const double *A_log,
-                   const double *dt_bias, const double *h0,
-                   const int64_t *cu_seqlens, int n_seq, int H, int dk, int dv,
-                   double scale, const int32_t *chains, int n_chains,
-                   double *o, double *hT, int n_threads)
+static int oracle_fwd(const double *q, const double *k, const double *v,
+                      const double *a, const double *b, const double *A_log,
+                      const double *dt_bias, const double *h0,
+                      const int64_t *cu_seqlens, int n_seq, int H, int dk, int dv,
+                      double scale, const int32_t *chains, int n_chains,
+                      double *o, double *hT, double *h_chunks, int C, int n_threads)
 {
     if (!q || !k || !v || !a || !b || !A_log || !dt_bias || !cu_seqlens || !o)
         return -1;
+    if (h_chunks && C <= 0) return -1;
     if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
     const int total = chains ? n_chains : n_seq * H;
     int err = 0;
@@ -120,14 +126,50 @@ int kda_oracle_fwd(const double *q, const double *k, const double *v,
         const size_t off = ((size_t)s * H + h) * (size_t)dv * dk;
         if (h0) memcpy(S, h0 + off, sizeof(double) * (size_t)dv * dk);
         else memset(S, 0, sizeof(double) * (size_t)dv * dk);
+        double *Hc = NULL;
+        if (h_chunks) {
+            int64_t cb = 0;   /* chunks of the sequences before s */
+            for (int s2 = 0; s2 < s; ++s2) cb += (cu_seqlens[s2 + 1] - cu_seqlens[s2] + C - 1) / C;
+            Hc = h_chunks + (cb * H + h) * (int64_t)dv * dk;
+        }
         oracle_chain(q, k, v, a, b, exp(A_log[h]), dt_bias + (size_t)h * dk, S, o,
                      cu_seqlens[s], cu_seqlens[s + 1] - cu_seqlens[s], H, h, dk, dv,
-                     scale, eg, u);
+                     scale, eg, u, Hc, C, (int64_t)H * dv * dk);
         if (hT) memcpy(hT + off, S, sizeof(double) * (size_t)dv * dk);
         free(S);
     }
     (void)n_threads;
     return err ? -1 : 0;
+}
+
+int kda_oracle_fwd(const double *q, const double *k, const double *v,
+                   const double *a, const double *b, const double *A_log,
+                   const double *dt_bias, const double *h0,
+                   const int64_t *cu_seqlens, int n_seq, int H, int dk, int dv,
+                   double scale, const int32_t *chains, int n_chains,
+                   double *o, double *hT, int n_threads)
+{
+    return oracle_fwd(q, k, v, a, b, A_log, dt_bias, h0, cu_seqlens, n_seq, H, dk, dv, scale,
+                      chains, n_chains, o, hT, NULL, 0, n_threads);
+}
+
+/*
+ * kda_oracle_fwd with the state entering every chunk of C tokens recorded:
+ * h_chunks [N_chunks, H, dv, dk], row (chunks of the sequences before s) + c
+ * holds the state of (s, head) before token C*c of s (the materialised form:
+ * states stored at chunk boundaries).  N_chunks = sum over s of
+ * ceil(len_s / C).
+ */
+int kda_oracle_fwd_states(const double *q, const double *k, const double *v,
+                          const double *a, const double *b, const double *A_log,
+                          const double *dt_bias, const double *h0,
+                          const int64_t *cu_seqlens, int n_seq, int H, int dk, int dv,
+                          double scale, const int32_t *chains, int n_chains,
+                          double *o, double *hT, double *h_chunks, int C, int n_threads)
+{
+    if (!h_chunks) return -1;
+    return oracle_fwd(q, k, v, a, b, A_log, dt_bias, h0, cu_seqlens, n_seq, H, dk, dv, scale,
+                      chains, n_chains, o, hT, h_chunks, C, n_threads);
 }
 
 /*

@@ -415,6 +415,39 @@ def test_extend_equals_successive_decode_steps():
 
 
 # ----------------------------------------------------------------------------
+# chunk-boundary states (I16): the state entering chunk c of a sequence is the
+# final state of the same recurrence run over the sequence's first C*c tokens
+# (brute force over prefixes); row order follows the sequences.
+# ----------------------------------------------------------------------------
+def test_chunk_states_are_prefix_final_states():
+    r = RNG(81)
+    H, dk, dv, C = 2, 6, 5, 4
+    lens = [9, 0, 4, 7]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k = r.standard_normal((T, H, dk)), r.standard_normal((T, H, dk))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v, a, b = r.standard_normal((T, H, dv)), r.standard_normal((T, H, dk)), r.standard_normal((T, H))
+    A_log, dt_bias = r.uniform(0, 1, H), r.uniform(-1, 1, (H, dk))
+    h0 = 0.1 * r.standard_normal((len(lens), H, dv, dk))
+    o, hT, hc = oracle.fwd(q, k, v, a, b, A_log, dt_bias, h0=h0, cu_seqlens=cu, chunk_states=C, n_threads=2)
+    o2, hT2 = oracle.fwd(q, k, v, a, b, A_log, dt_bias, h0=h0, cu_seqlens=cu, n_threads=2)
+    assert np.array_equal(o, o2) and np.array_equal(hT, hT2)
+    assert hc.shape == (sum((n + C - 1) // C for n in lens), H, dv, dk)
+    row = 0
+    for s, n in enumerate(lens):
+        for c in range((n + C - 1) // C):
+            t0 = int(cu[s])
+            sl = slice(t0, t0 + C * c)
+            _, want = ref.recurrent_matrix_form(q[sl], k[sl], v[sl], a[sl], b[sl], A_log, dt_bias,
+                                                h0=h0[s:s + 1], cu_seqlens=None)
+            assert close(hc[row], want[0], 1e-12), (s, c)
+            row += 1
+    assert row == hc.shape[0]
+
+
+# ----------------------------------------------------------------------------
 # short convolution before decode (I15): width 1 is silu of an affine map;
 # T updates from a zero state are the causal convolution of the whole input
 # sequence (numpy's convolve), and the state ends holding the last W-1 inputs;
