@@ -7,6 +7,10 @@
  *                       sequences, returning the outputs and the final states;
  *   kda_chunk_fwd_pool  the same prefill with the states in a decode state
  *                       pool (read and updated in place through slot indices);
+ *   kda_chunk_fwd_states  the same prefill that also stores the state entering
+ *                       every chunk (the materialised form; its chunk-parallel
+ *                       output pass is kda_chunk_fwd over chunk-length
+ *                       sequences started from those states);
  *   kda_decode_step     one fused T=1 decode step over a pool of states;
  *   kda_decode_extend   T tokens per row applied to the pool states in one
  *                       launch (short extends, speculative verification);
@@ -117,6 +121,34 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v,
                   void *o, float *h_T,
                   int B, int T, int H, int dk, int dv, int n_seq,
                   float scale, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_states -- kda_chunk_fwd that also writes the state entering
+ * every chunk: the materialised form of [LA-06] (chunkwise form: the states at
+ * chunk boundaries are stored, then the outputs are a chunk-parallel pass) and
+ * of [TL-KDA] section 6 (a state snapshot per chunk).
+ *
+ *   h_chunks : [N_chunks, H, dv, dk] float32, written: row
+ *              (chunks of the sequences before s) + c holds the state of
+ *              (sequence s, head) before its chunk c (row 0 of a sequence = its
+ *              h0, or zeros), in the layout of h_T.  N_chunks = sum over
+ *              sequences of ceil(len / 16) (dense input: B * ceil(T / 16)).
+ *              The caller sizes it (the lengths of packed input live in device
+ *              memory and are not checked).
+ * All other arguments, outputs and errors are those of kda_chunk_fwd; the
+ * outputs are bitwise those of kda_chunk_fwd.  h_chunks is fp32 and exact, so
+ * kda_chunk_fwd over the chunks as sequences of their own (cu_seqlens at every
+ * chunk boundary, or for dense input with T % 16 == 0 the same buffers viewed
+ * as B*T/16 sequences of 16 tokens) with h0 = h_chunks reproduces o bitwise,
+ * every chunk an independent chain.
+ */
+int kda_chunk_fwd_states(const void *q, const void *k, const void *v,
+                         const void *g_raw, const void *beta_raw,
+                         const float *A_log, const float *dt_bias,
+                         const float *h0, const int32_t *cu_seqlens, int chunk,
+                         void *o, float *h_T, float *h_chunks,
+                         int B, int T, int H, int dk, int dv, int n_seq,
+                         float scale, kda_dtype dtype, hipStream_t stream);
 
 /*
  * kda_chunk_fwd_pool -- the prefill of kda_chunk_fwd with the states kept in a

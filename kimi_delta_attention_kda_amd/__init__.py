@@ -19,7 +19,7 @@ _lib = None
 KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_check", "kda_decode_step",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_states", "kda_chunk_fwd_check", "kda_decode_step",
            "kda_decode_extend", "kda_conv_decode_step", "kda_status_str")
 
 
@@ -41,6 +41,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.restype = I
     lib.kda_chunk_fwd_pool.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P]
     lib.kda_chunk_fwd_pool.restype = I
+    lib.kda_chunk_fwd_states.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, P, I, I, I, I, I, I, F, I, P]
+    lib.kda_chunk_fwd_states.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.kda_decode_step.restype = I
     lib.kda_decode_extend.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
@@ -75,6 +77,14 @@ def _dev(name, t, dtype=None):
         raise KDAError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq):
+    if o.numel() != B * T * H * dv:
+        raise KDAError("o must hold [B, T, H, dv] elements")
+    for name, t in (("h0", h0), ("h_T", h_T)):
+        if t is not None and t.numel() != n_seq * H * dv * dk:
+            raise KDAError(f"{name} must hold [N, H, dv, dk] elements")
+
+
 def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
               chunk: int = 16, scale=None, output_final_state: bool = True,
               o=None, h_T=None, stream=None):
@@ -107,6 +117,7 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None
     if output_final_state and h_T is None:
         h_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
     _dev("h_T", h_T, torch.float32)
+    _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(load_library().kda_chunk_fwd(
@@ -279,3 +290,88 @@ def conv_decode_step(mixed_qkv, conv_state, conv_weight, conv_bias, a, b, A_log,
         _ptr(A_log), _ptr(dt_bias), _ptr(state_pool), _ptr(state_idx), _ptr(o), B, H, HV, K, V, W, P,
         float(scale), KDA_DECODE_L2NORM if l2norm else 0, ctypes.c_void_p(stream)))
     return o
+
+
+def n_chunks(T: int, B: int = 1, cu_seqlens=None, chunk: int = 16) -> int:
+    """Rows of the materialised chunk states: sum over sequences of
+    ceil(len / chunk) (reads cu_seqlens back to the host if given)."""
+    if cu_seqlens is None:
+        return B * ((T + chunk - 1) // chunk)
+    lens = torch.diff(cu_seqlens.detach().to("cpu", torch.int64))
+    return int(((lens + chunk - 1) // chunk).sum())
+
+
+def chunk_fwd_states(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
+                     chunk: int = 16, scale=None, output_final_state: bool = True, o=None,
+                     h_T=None, h_chunks=None, stream=None):
+    """chunk_fwd that also returns the state entering every chunk.
+    Returns (o, h_T, h_chunks [N_chunks, H, dv, dk] float32)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    act = q.dtype
+    if act not in (torch.float32, torch.bfloat16):
+        raise KDAError("activations must be float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw)):
+        _dev(name, t, act)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("h0", h0)):
+        _dev(name, t, torch.float32)
+    _dev("cu_seqlens", cu_seqlens, torch.int32)
+    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or tuple(beta_raw.shape) != (B, T, H):
+        raise KDAError("inconsistent activation shapes")
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    nc = n_chunks(T, B, cu_seqlens, chunk)
+    if scale is None:
+        scale = dk ** -0.5
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=act, device=q.device)
+    _dev("o", o, act)
+    if output_final_state and h_T is None:
+        h_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
+    _dev("h_T", h_T, torch.float32)
+    if h_chunks is None:
+        h_chunks = torch.empty((nc, H, dv, dk), dtype=torch.float32, device=q.device)
+    _dev("h_chunks", h_chunks, torch.float32)
+    if h_chunks.numel() != nc * H * dv * dk:
+        raise KDAError("h_chunks must hold [N_chunks, H, dv, dk] elements")
+    _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(load_library().kda_chunk_fwd_states(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
+        _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), _ptr(h_chunks), B, T, H, dk, dv, n_seq,
+        float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
+    return o, h_T, h_chunks
+
+
+def chunk_o_from_states(q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, cu_seqlens=None,
+                        chunk: int = 16, scale=None, o=None, stream=None):
+    """The chunk-parallel output pass of the materialised form: kda_chunk_fwd
+    over every chunk as a sequence of its own, started from its state in
+    h_chunks (so all chunks are independent chains).  Dense input with
+    T % chunk == 0 is passed as B*T/chunk sequences of `chunk` tokens (same
+    buffers); otherwise chunk boundaries are passed as cu_seqlens.  Returns o."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if cu_seqlens is None and T % chunk == 0:
+        nb = B * T // chunk
+        shp = lambda x: x.view(nb, chunk, *x.shape[2:])
+        o_ = None if o is None else shp(o)
+        out, _ = chunk_fwd(shp(q), shp(k), shp(v), shp(g_raw), shp(beta_raw), A_log, dt_bias, h0=h_chunks,
+                           chunk=chunk, scale=scale, output_final_state=False, o=o_, stream=stream)
+        return out.view(B, T, H, dv)
+    if cu_seqlens is None:
+        bounds = [(s * T, (s + 1) * T) for s in range(B)]
+    else:
+        cu = cu_seqlens.detach().to("cpu", torch.int64).tolist()
+        bounds = list(zip(cu[:-1], cu[1:]))
+    edges = [0]
+    for bos, eos in bounds:
+        for st in range(bos, eos, chunk):
+            edges.append(min(st + chunk, eos))
+    ccu = torch.tensor(edges, dtype=torch.int32, device=q.device)
+    flat = lambda x: x.reshape(1, B * T, *x.shape[2:])
+    o_ = None if o is None else flat(o)
+    out, _ = chunk_fwd(flat(q), flat(k), flat(v), flat(g_raw), flat(beta_raw), A_log, dt_bias, h0=h_chunks,
+                       cu_seqlens=ccu, chunk=chunk, scale=scale, output_final_state=False, o=o_, stream=stream)
+    return out.view(B, T, H, dv)

@@ -56,8 +56,8 @@ const char *kda_status_str(int status)
 static int chunk_fwd_impl(const void *q, const void *k, const void *v, const void *g_raw,
                           const void *beta_raw, const float *A_log, const float *dt_bias,
                           const float *h0, const int32_t *state_idx, const int32_t *cu_seqlens,
-                          int chunk, void *o, float *h_T, int B, int T, int H, int dk, int dv,
-                          int n_seq, float scale, kda_dtype dtype, hipStream_t stream)
+                          int chunk, void *o, float *h_T, float *h_chunks, int B, int T, int H, int dk,
+                          int dv, int n_seq, float scale, kda_dtype dtype, hipStream_t stream)
 {
     if (chunk != 16) return KDA_ERR_UNSUPPORTED;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -74,7 +74,7 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     if ((long long)n_seq * H * 2 > 0x7fffffffLL) return KDA_ERR_SHAPE;
     if (!A_log || !dt_bias) return KDA_ERR_NULL;
     if (n_seq > 0 && tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !o)) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, cu_seqlens, state_idx};
+    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, h_chunks, cu_seqlens, state_idx};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
     if (n_seq == 0) return KDA_OK;
@@ -88,7 +88,7 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     a.n_teams = 0;
     a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
     a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.state_idx = state_idx; a.cu_seqlens = cu_seqlens;
-    a.o = o; a.h_T = h_T; a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
+    a.o = o; a.h_T = h_T; a.h_chunks = h_chunks; a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
     const hipError_t e = kda::launch_chunk_fwd(a, dtype == KDA_BF16 ? 1 : 0, dk, dv, stream);
     if (e == hipErrorInvalidValue) return KDA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -101,7 +101,18 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw
                   kda_dtype dtype, hipStream_t stream)
 {
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
-                          h_T, B, T, H, dk, dv, n_seq, scale, dtype, stream);
+                          h_T, nullptr, B, T, H, dk, dv, n_seq, scale, dtype, stream);
+}
+
+int kda_chunk_fwd_states(const void *q, const void *k, const void *v, const void *g_raw,
+                         const void *beta_raw, const float *A_log, const float *dt_bias,
+                         const float *h0, const int32_t *cu_seqlens, int chunk, void *o, float *h_T,
+                         float *h_chunks, int B, int T, int H, int dk, int dv, int n_seq, float scale,
+                         kda_dtype dtype, hipStream_t stream)
+{
+    if (n_seq > 0 && T > 0 && !h_chunks) return KDA_ERR_NULL;
+    return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
+                          h_T, h_chunks, B, T, H, dk, dv, n_seq, scale, dtype, stream);
 }
 
 int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *g_raw,
@@ -116,7 +127,7 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *
     // the slots double as h0 (read when a sequence starts) and h_T (written when it
     // ends); each (sequence, head, slab) is read and written by the same workgroup
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_idx, cu_seqlens,
-                          chunk, o, state_pool, B, T, H, dk, dv, n_seq, scale, dtype, stream);
+                          chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, scale, dtype, stream);
 }
 
 int kda_chunk_fwd_check(hipStream_t stream)

@@ -483,7 +483,8 @@ __device__ __forceinline__ void lds_barrier() {   // LDS-only barrier: global op
     asm volatile("" ::: "memory");
 }
 
-template <bool BF16, int DK, int DV, int BDV>
+// SNAP: also store the state entering every chunk to args.h_chunks.
+template <bool BF16, int DK, int DV, int BDV, bool SNAP>
 __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
 {
     using P = PL<BF16, DK, DV>;
@@ -541,6 +542,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         cp.q_base = 0;
         cp.ci = chain_info(args, cp.chain);
         cp.nch = (cp.ci.len + CH - 1) / CH;
+        cursor_seek(cp, p, args, args.n_teams);         // the chain holding this producer's first chunk
         Cursor cd = cp;                                 // the chunk being loaded, one step ahead
         PIn<BF16, DK, DV> cur, nxt;
         prod_load<BF16, DK, DV>(cur, cp, p, args, wu, lane);
@@ -893,7 +895,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     int chain = role.team, c = 0, nch = 0;
     ChainInfo ci{};
     f32x4 S[MT];
-    size_t hbase = 0;
+    size_t hbase = 0, cbase = 0;   // cbase: h_chunks index of the chain's first chunk
     int hrow = 0;
     bool started = false;
     auto store_hT = [&]() {
@@ -911,6 +913,16 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
         // negative slot starts from zero and keeps no final state
         hrow = args.state_idx ? args.state_idx[ci.seq] : ci.seq;
         hbase = (((size_t)(hrow < 0 ? 0 : hrow) * args.H + ci.head) * DV + v0 + ln) * DK;
+        if (SNAP && computes) {
+            // chunks of the sequences before this one
+            if (args.cu_seqlens) {
+                cbase = 0;
+                for (int s2 = 0; s2 < ci.seq; ++s2)
+                    cbase += (size_t)((args.cu_seqlens[s2 + 1] - args.cu_seqlens[s2] + CH - 1) / CH);
+            } else {
+                cbase = (size_t)ci.seq * ((args.T + CH - 1) / CH);
+            }
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             if (args.h0 && computes && hrow >= 0)
@@ -1041,6 +1053,14 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 for (int i = 0; i < 4; ++i) vv[i] = static_cast<float>(v4[i]);
             } else {
                 vv = *reinterpret_cast<const f32x4 *>(pl + voff + lane * 16);
+            }
+            // the state entering this chunk, for the materialised form (same
+            // addressing as h_T, chunk row cbase + c)
+            if constexpr (SNAP) {
+                const size_t at = (((cbase + c) * args.H + ci.head) * DV + v0 + ln) * DK;
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    *reinterpret_cast<f32x4 *>(args.h_chunks + at + tile_chan<BF16>(mt, lq, 0)) = S[mt];
             }
             // R1: W = k~ S, Qs = q~ S ; then decay the state in place
             f32x4 W = {0.f, 0.f, 0.f, 0.f}, Qs = {0.f, 0.f, 0.f, 0.f};
@@ -1250,7 +1270,7 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     }
 }
 
-template <bool BF16, int DK, int DV, int BDV>
+template <bool BF16, int DK, int DV, int BDV, bool SNAP>
 static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
 {
     constexpr int NS = DV / BDV;
@@ -1262,7 +1282,7 @@ static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, chunk_fwd_kernel<BF16, DK, DV, BDV>, NTHR, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, chunk_fwd_kernel<BF16, DK, DV, BDV, SNAP>, NTHR, 0);
     if (e != hipSuccess) return e;
     // every workgroup of the grid must be resident at once (teams wait on each other)
     const int cap_wgs = n_cu * (occ < 1 ? 1 : occ);
@@ -1285,7 +1305,7 @@ static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
     const unsigned per_xcd = a.pair_half > 0 ? (unsigned)(cus_per_xcd + teams_per_xcd * cpt)
                                              : (unsigned)(teams_per_xcd * TS);
     const unsigned grid = 8u * per_xcd;
-    hipLaunchKernelGGL((chunk_fwd_kernel<BF16, DK, DV, BDV>), dim3(grid), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL((chunk_fwd_kernel<BF16, DK, DV, BDV, SNAP>), dim3(grid), dim3(NTHR), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1302,11 +1322,16 @@ static int pick_bdv(int n_chains, int dv)
 hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int dk, int dv, hipStream_t stream)
 {
     const int bdv = pick_bdv(a.n_seq * a.H, dv);
+#define KDA_DISPATCH_S(BF, DKV, DVV, SN)                                                \
+    {                                                                                    \
+        if (bdv == 64 && DVV >= 64) return launch_one<BF, DKV, DVV, 64, SN>(a, stream);  \
+        if (bdv == 32) return launch_one<BF, DKV, DVV, 32, SN>(a, stream);               \
+        return launch_one<BF, DKV, DVV, 16, SN>(a, stream);                              \
+    }
 #define KDA_DISPATCH(BF, DKV, DVV)                                             \
     if (dk == DKV && dv == DVV) {                                              \
-        if (bdv == 64 && DVV >= 64) return launch_one<BF, DKV, DVV, 64>(a, stream); \
-        if (bdv == 32) return launch_one<BF, DKV, DVV, 32>(a, stream);         \
-        return launch_one<BF, DKV, DVV, 16>(a, stream);                        \
+        if (a.h_chunks) KDA_DISPATCH_S(BF, DKV, DVV, true)                     \
+        KDA_DISPATCH_S(BF, DKV, DVV, false)                                    \
     }
     if (dtype == 1) {
         KDA_DISPATCH(true, 128, 128)
@@ -1318,6 +1343,7 @@ hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int dk, int dv, hipSt
         KDA_DISPATCH(false, 64, 64)
     }
 #undef KDA_DISPATCH
+#undef KDA_DISPATCH_S
     return hipErrorInvalidValue;
 }
 

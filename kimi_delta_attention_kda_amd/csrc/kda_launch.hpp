@@ -47,6 +47,7 @@ struct ChunkArgs {
     const int32_t *cu_seqlens;
     void *o;
     float *h_T;
+    float *h_chunks;     // NULL, or [N_chunks][H][DV][DK]: the state entering every chunk
     int T, H, n_seq;     // T: per-sequence length for dense input, total tokens if cu_seqlens
     float scale;
     // workspace (device memory owned by the library)

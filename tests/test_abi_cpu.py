@@ -68,6 +68,24 @@ def test_chunk_validation(lib):
     assert chunk(lib, n_seq=0, B=0) == 0            # nothing to do, no launch
 
 
+def chunk_states(lib, **kw):
+    args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, h0=None, cu=None, chunk=16, o=A,
+                hT=None, hc=A, B=1, T=16, H=1, dk=128, dv=128, n_seq=1, scale=0.1, dtype=1)
+    args.update(kw)
+    return lib.kda_chunk_fwd_states(args["q"], args["k"], args["v"], args["g"], args["b"],
+                                    args["A_log"], args["dt"], args["h0"], args["cu"], args["chunk"],
+                                    args["o"], args["hT"], args["hc"], args["B"], args["T"], args["H"],
+                                    args["dk"], args["dv"], args["n_seq"], args["scale"], args["dtype"],
+                                    None)
+
+
+def test_chunk_states_validation(lib):
+    assert chunk_states(lib, hc=None) == -1
+    assert chunk_states(lib, hc=MIS) == -4
+    assert chunk_states(lib, chunk=64) == -3
+    assert chunk_states(lib, n_seq=0, B=0) == 0
+
+
 def chunk_pool(lib, **kw):
     args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, pool=A, idx=B, cu=None, chunk=16, o=A,
                 B=1, T=16, H=1, dk=128, dv=128, n_seq=1, P=4, scale=0.1, dtype=1)

@@ -59,6 +59,16 @@ def test_small(i):
     check(p, what=f"small{i}")
 
 
+@pytest.mark.parametrize("dtype,dk,dv,H", [("bf16", 128, 128, 2), ("f32", 64, 64, 4)])
+def test_many_short_sequences(dtype, dk, dv, H):
+    """Packed sequences of 0..40 tokens, more (sequence, head) chains than the
+    launch has teams: a team then runs several chains, most shorter than its
+    producers' first chunks."""
+    lengths = [int(x) for x in np.random.default_rng(7).integers(0, 41, size=24)]
+    p = synth.prefill(400, B=1, T=0, H=H, dk=dk, dv=dv, dtype=dtype, lengths=lengths, with_h0=True)
+    check(p, what=f"many-short {dtype} d{dk}x{dv} H{H}")
+
+
 def test_workload1_full():
     check(synth.prefill_workload(1), what="prefill-bf16 B4 H16 T4096")
 

@@ -1,0 +1,70 @@
+"""GPU parity of the materialised form (kda_chunk_fwd_states, then the
+chunk-parallel output pass), through the C ABI:
+- the stored state entering every chunk matches the fp64 oracle's states at
+  chunk boundaries (dense, packed variable-length, fp32 and bf16, with and
+  without h0, and the full prefill workload on sampled heads);
+- the outputs and final states are bitwise those of kda_chunk_fwd;
+- the chunk-parallel pass (every chunk its own chain, started from its stored
+  state) reproduces the outputs bitwise."""
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_kda_amd as kda
+import synth
+from kda_testlib import assert_close, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+CH = 16
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def oracle_states(p, heads=None):
+    f = p.f64(heads)
+    import oracle
+    return oracle.fwd(f["q"], f["k"], f["v"], f["a"], f["b"], f["A_log"], f["dt_bias"], h0=f["h0"],
+                      cu_seqlens=f["cu_seqlens"], scale=f["scale"], chunk_states=CH)
+
+
+def check_states(p, heads=None, what=""):
+    say(what, "tokens", p.tokens, "H", p.H, "dk", p.dk, "dv", p.dv, p.dtype)
+    d = to_device(p)
+    o1, hT1 = kda.chunk_fwd(**d, scale=p.scale)
+    o2, hT2, hc = kda.chunk_fwd_states(**d, scale=p.scale)
+    kda.chunk_fwd_check()
+    assert torch.equal(o1, o2) and torch.equal(hT1, hT2), what + ": outputs differ from kda_chunk_fwd"
+    # chunk-parallel output pass from the stored states
+    dd = {k_: v_ for k_, v_ in d.items() if k_ != "h0"}
+    o3 = kda.chunk_o_from_states(**dd, h_chunks=hc, scale=p.scale)
+    kda.chunk_fwd_check()
+    assert torch.equal(o1, o3), what + ": chunk-parallel pass differs"
+    hs = slice(None) if heads is None else list(heads)
+    got = hc[:, hs].cpu().numpy().astype(np.float64)
+    _, _, want = oracle_states(p, heads)
+    m = assert_close(got, want, p.dtype, what + " h_chunks")
+    say("  h_chunks", m, "rows", got.shape[0])
+
+
+SMALL = [
+    dict(B=2, T=100, H=3, dk=128, dv=128, dtype="bf16", with_h0=True),
+    dict(B=1, T=64, H=2, dk=128, dv=64, dtype="bf16"),
+    dict(B=3, T=33, H=2, dk=64, dv=64, dtype="f32", with_h0=True),
+    dict(B=1, T=0, H=2, dk=128, dv=128, dtype="bf16", lengths=[1, 16, 17, 0, 45, 130], with_h0=True),
+    dict(B=2, T=48, H=2, dk=64, dv=128, dtype="bf16", gate_stress=0.05),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)))
+def test_states_small(i):
+    kw = dict(SMALL[i])
+    lengths = kw.pop("lengths", None)
+    p = synth.prefill(300 + i, lengths=lengths, **kw)
+    check_states(p, what=f"states small{i}")
+
+
+def test_states_workload1_sampled():
+    check_states(synth.prefill_workload(1), heads=[0, 9], what="states prefill-bf16 B4 H16 T4096")
