@@ -16,7 +16,9 @@ fp64 oracle (plain C, OpenMP over chains) timed on the host cores on the same
 prefill workload.  Outside the step, the pool-addressed prefill (same
 workload) and kda_decode_extend with T = 4 tokens per row (decode workload's
 rows, heads and pool) are timed the same way and reported as extra fields,
-as is kda_conv_decode_step (width-4 convolution fused with the decode step).
+as is kda_conv_decode_step (width-4 convolution fused with the decode step)
+and the two passes of the materialised form on the prefill workload
+(kda_chunk_fwd_states, then the chunk-parallel output pass).
 """
 from __future__ import annotations
 
@@ -287,6 +289,37 @@ def main():
     torch.cuda.synchronize()
     pool_avg = float(np.mean([evp[s_][0].elapsed_time(evp[s_][1]) for s_ in range(K)])) * 1e-3
 
+    # the materialised form on the same prefill workload: pass 1 also stores the
+    # fp32 state entering every chunk, pass 2 recomputes the outputs with every
+    # chunk an independent chain started from its stored state
+    nc = kda.n_chunks(p.T, p.B) if p.cu_seqlens is None else kda.n_chunks(0, 1, pin["cu_seqlens"])
+    hcb = torch.empty((nc, p.H, p.dv, p.dk), dtype=torch.float32, device=dev)
+    pin_noh0 = {k_: v_ for k_, v_ in pin.items() if k_ != "h0"}
+
+    def states_call():
+        kda.chunk_fwd_states(**pin, scale=p.scale, o=o, h_T=hT, h_chunks=hcb)
+
+    def chunk_o_call():
+        kda.chunk_o_from_states(**pin_noh0, h_chunks=hcb, scale=p.scale, o=o)
+
+    mat_avg = []
+    for fn in (states_call, chunk_o_call):
+        for _ in range(2):
+            fn()
+        evm = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        torch.cuda.synchronize()
+        evm[0].record()
+        for s_ in range(K):
+            fn()
+            evm[s_ + 1].record()
+        torch.cuda.synchronize()
+        mat_avg.append(float(np.mean([evm[s_].elapsed_time(evm[s_ + 1]) for s_ in range(K)])) * 1e-3)
+    snap_bytes = 4 * nc * p.H * p.dv * p.dk
+    act_bytes = p.tokens * p.H * (2 * (3 * p.dk + p.dv + 1) + 2 * p.dv)
+    states_gbs = (prefill_bytes(p) + snap_bytes) / mat_avg[0] / 1e9
+    chunk_o_gbs = (act_bytes + snap_bytes) / mat_avg[1] / 1e9
+    del hcb
+
     # T = 4 tokens per row through kda_decode_extend (speculative-verify shape) on
     # the decode workload's rows, heads and pool, timed the same way
     de = synth.extend(4, T=EXTEND_T, **{k_: v_ for k_, v_ in synth.DECODE_WORKLOAD.items() if k_ != "name"})
@@ -387,6 +420,10 @@ def main():
         "prefill_tflops": round(flops / pre_avg / 1e12, 2),
         "prefill_mfma_frac": round(flops / pre_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
         "prefill_pool_us": round(pool_avg * 1e6, 2),
+        "states_us": round(mat_avg[0] * 1e6, 2),
+        "states_gbs": round(states_gbs, 1),
+        "chunk_o_us": round(mat_avg[1] * 1e6, 2),
+        "chunk_o_gbs": round(chunk_o_gbs, 1),
         "decode_us": round(dec_avg * 1e6, 2),
         "decode_host_us_per_call": round(host_dec / K * 1e6, 2),
         "extend_T": EXTEND_T,
