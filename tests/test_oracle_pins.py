@@ -448,6 +448,45 @@ def test_chunk_states_are_prefix_final_states():
 
 
 # ----------------------------------------------------------------------------
+# gradients (I17): the fp64 autograd gradients of the PyTorch recurrence match
+# central finite differences of the C oracle's loss sum(o * do) + sum(h_T * dh_T)
+# for every input (two packed sequences, one with a ragged length, with h0).
+# ----------------------------------------------------------------------------
+def test_gradients_match_finite_differences():
+    from oracle import grad
+    r = RNG(91)
+    H, dk, dv = 2, 4, 3
+    cu = np.array([0, 5, 12])
+    T = int(cu[-1])
+    x = dict(q=r.standard_normal((T, H, dk)), k=r.standard_normal((T, H, dk)), v=r.standard_normal((T, H, dv)),
+             a=r.standard_normal((T, H, dk)), b=r.standard_normal((T, H)), A_log=r.uniform(-1, 1, H),
+             dt_bias=r.uniform(-1, 1, (H, dk)), h0=0.3 * r.standard_normal((2, H, dv, dk)))
+    x["k"] /= np.linalg.norm(x["k"], axis=-1, keepdims=True)
+    do, dhT = r.standard_normal((T, H, dv)), r.standard_normal((2, H, dv, dk))
+    scale = 0.7
+
+    def loss(xx):
+        o, hT = oracle.fwd(xx["q"], xx["k"], xx["v"], xx["a"], xx["b"], xx["A_log"], xx["dt_bias"], h0=xx["h0"],
+                           cu_seqlens=cu, scale=scale, n_threads=1)
+        return float((o * do).sum() + (hT * dhT).sum())
+
+    g = grad.backward(x["q"], x["k"], x["v"], x["a"], x["b"], x["A_log"], x["dt_bias"], do, h0=x["h0"],
+                      dh_T=dhT, cu_seqlens=cu, scale=scale)
+    names = dict(q="dq", k="dk", v="dv", a="da", b="db", A_log="dA_log", dt_bias="ddt_bias", h0="dh0")
+    eps = 1e-6
+    for name, gname in names.items():
+        flat = x[name].reshape(-1)
+        for i in r.choice(flat.size, size=min(6, flat.size), replace=False):
+            xp = {k_: np.array(v_, copy=True) for k_, v_ in x.items()}
+            xm = {k_: np.array(v_, copy=True) for k_, v_ in x.items()}
+            xp[name].reshape(-1)[i] += eps
+            xm[name].reshape(-1)[i] -= eps
+            fd = (loss(xp) - loss(xm)) / (2 * eps)
+            got = g[gname].reshape(-1)[i]
+            assert abs(fd - got) <= 1e-6 * max(1.0, abs(fd)), (name, i, fd, got)
+
+
+# ----------------------------------------------------------------------------
 # short convolution before decode (I15): width 1 is silu of an affine map;
 # T updates from a zero state are the causal convolution of the whole input
 # sequence (numpy's convolve), and the state ends holding the last W-1 inputs;
