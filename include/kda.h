@@ -5,6 +5,8 @@
  *
  *   kda_chunk_fwd       chunkwise prefill over dense or packed variable-length
  *                       sequences, returning the outputs and the final states;
+ *   kda_backward        gradients of the prefill with respect to every input,
+ *                       from the states kda_chunk_fwd_states stores;
  *   kda_chunk_fwd_pool  the same prefill with the states in a decode state
  *                       pool (read and updated in place through slot indices);
  *   kda_chunk_fwd_states  the same prefill that also stores the state entering
@@ -149,6 +151,49 @@ int kda_chunk_fwd_states(const void *q, const void *k, const void *v,
                          void *o, float *h_T, float *h_chunks,
                          int B, int T, int H, int dk, int dv, int n_seq,
                          float scale, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * kda_backward -- gradients of the forward of kda_chunk_fwd for a loss whose
+ * gradients with respect to o and to the final states are do and dh_T: the
+ * backward pass of [LA-06] (chunkwise form: a reverse loop over chunks from
+ * the states stored at chunk boundaries).  Per token, with D the gradient
+ * with respect to the state after the token (S' = S Diag(e^g),
+ * u = beta (v - S'k), S+ = S' + u k^T, o = S+ scale q):
+ *   D += do (scale q)^T;  dq = scale S+^T do;  du = D k;  dv = beta du;
+ *   dbeta = du . (v - S'k);  dk = D^T u - beta S'^T du;
+ *   dS' = D - beta du k^T;  dg = column sums of dS' o S';  D <- dS' Diag(e^g);
+ * then through g = -exp(A_log) softplus(g_raw + dt_bias) and
+ * beta = sigmoid(beta_raw) to dg_raw, ddt_bias, dA_log and dbeta_raw, and
+ * dh0 = D before the first token.
+ *
+ * Inputs: q, k, v, g_raw, beta_raw, A_log, dt_bias, cu_seqlens, scale,
+ * B, T, H, n_seq and dtype exactly as given to kda_chunk_fwd_states;
+ *   h_chunks  : its [N_chunks, H, dv, dk] float32 output for those inputs
+ *               and h0;
+ *   do_       : [T_all, H, dv] activation dtype;
+ *   dh_T      : [n_seq, H, dv, dk] float32, or NULL for zero.
+ * Outputs (written; NULL is allowed for dA_log, ddt_bias and dh0):
+ *   dq, dk, dg_raw : [T_all, H, dk], dv : [T_all, H, dv], dbeta_raw : [T_all, H]
+ *                    in the activation dtype;
+ *   dA_log [H], ddt_bias [H, dk], dh0 [n_seq, H, dv, dk] float32.
+ * workspace: device memory of at least kda_backward_workspace_bytes() bytes
+ * (1 MiB per (sequence, head) and a small per-chain area), owned by the
+ * caller; its contents on entry do not matter.
+ * Built for dk = dv = 128 with bfloat16 activations (those of the d = 128
+ * forward; other shapes and float32 return KDA_ERR_UNSUPPORTED).  The result
+ * is deterministic (no atomics).  Returns KDA_OK or a negative kda_status.
+ */
+size_t kda_backward_workspace_bytes(int n_seq, int H, int dk, int dv);
+int kda_backward(const void *q, const void *k, const void *v,
+                 const void *g_raw, const void *beta_raw,
+                 const float *A_log, const float *dt_bias,
+                 const float *h_chunks, const int32_t *cu_seqlens,
+                 const void *do_, const float *dh_T,
+                 void *dq, void *dk, void *dv, void *dg_raw, void *dbeta_raw,
+                 float *dA_log, float *ddt_bias, float *dh0,
+                 void *workspace, size_t workspace_bytes,
+                 int B, int T, int H, int dk_, int dv_, int n_seq,
+                 float scale, kda_dtype dtype, hipStream_t stream);
 
 /*
  * kda_chunk_fwd_pool -- the prefill of kda_chunk_fwd with the states kept in a

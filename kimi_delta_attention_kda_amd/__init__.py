@@ -20,7 +20,8 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_states", "kda_chunk_fwd_check", "kda_decode_step",
-           "kda_decode_extend", "kda_conv_decode_step", "kda_status_str")
+           "kda_decode_extend", "kda_conv_decode_step", "kda_backward", "kda_backward_workspace_bytes",
+           "kda_status_str")
 
 
 class KDAError(RuntimeError):
@@ -49,6 +50,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_extend.restype = I
     lib.kda_conv_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.kda_conv_decode_step.restype = I
+    lib.kda_backward_workspace_bytes.argtypes = [I, I, I, I]
+    lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                 ctypes.c_size_t, I, I, I, I, I, I, F, I, P]
+    lib.kda_backward.restype = I
     lib.kda_chunk_fwd_check.argtypes = [P]
     lib.kda_chunk_fwd_check.restype = I
     lib.kda_status_str.argtypes = [I]
@@ -375,3 +381,53 @@ def chunk_o_from_states(q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, cu_s
     out, _ = chunk_fwd(flat(q), flat(k), flat(v), flat(g_raw), flat(beta_raw), A_log, dt_bias, h0=h_chunks,
                        cu_seqlens=ccu, chunk=chunk, scale=scale, output_final_state=False, o=o_, stream=stream)
     return out.view(B, T, H, dv)
+
+
+def backward(q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, do, dh_T=None, cu_seqlens=None,
+             scale=None, workspace=None, stream=None):
+    """Gradients of the chunkwise forward (see kda_backward in include/kda.h).
+    q, k, v, g_raw, beta_raw, A_log, dt_bias, cu_seqlens, scale: as given to
+    chunk_fwd_states; h_chunks: its third output; do: [B, T, H, dv] (the
+    activation dtype); dh_T: [N, H, dv, dk] float32 or None.  Returns a dict:
+    dq, dk, dv, dg_raw, dbeta_raw (activation dtype, shaped like their
+    inputs), dA_log [H], ddt_bias [H, dk], dh0 [N, H, dv, dk] (float32)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    act = q.dtype
+    if act not in (torch.float32, torch.bfloat16):
+        raise KDAError("activations must be float32 or bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw), ("do", do)):
+        _dev(name, t, act)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("h_chunks", h_chunks), ("dh_T", dh_T)):
+        _dev(name, t, torch.float32)
+    _dev("cu_seqlens", cu_seqlens, torch.int32)
+    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] or do.shape != v.shape \
+            or tuple(beta_raw.shape) != (B, T, H):
+        raise KDAError("inconsistent activation shapes")
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if h_chunks.numel() != n_chunks(T, B, cu_seqlens) * H * dv * dk:
+        raise KDAError("h_chunks must hold [N_chunks, H, dv, dk] elements")
+    if dh_T is not None and dh_T.numel() != n_seq * H * dv * dk:
+        raise KDAError("dh_T must hold [N, H, dv, dk] elements")
+    if scale is None:
+        scale = dk ** -0.5
+    lib = load_library()
+    need = lib.kda_backward_workspace_bytes(n_seq, H, dk, dv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev("workspace", workspace)
+    dev = q.device
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg_raw=torch.empty_like(g_raw), dbeta_raw=torch.empty_like(beta_raw),
+               dA_log=torch.empty((H,), dtype=torch.float32, device=dev),
+               ddt_bias=torch.empty((H, dk), dtype=torch.float32, device=dev),
+               dh0=torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=dev))
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib.kda_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias), _ptr(h_chunks),
+        _ptr(cu_seqlens), _ptr(do), _ptr(dh_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+        _ptr(out["dg_raw"]), _ptr(out["dbeta_raw"]), _ptr(out["dA_log"]), _ptr(out["ddt_bias"]),
+        _ptr(out["dh0"]), _ptr(workspace), workspace.numel() * workspace.element_size(), B, T, H, dk, dv,
+        n_seq, float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
+    return out

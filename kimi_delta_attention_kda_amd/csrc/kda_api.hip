@@ -130,6 +130,52 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *
                           chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, scale, dtype, stream);
 }
 
+size_t kda_backward_workspace_bytes(int n_seq, int H, int dk, int dv)
+{
+    if (n_seq < 0 || H <= 0 || dk != 128 || dv != 128) return 0;
+    return kda::bwd_workspace_bytes(n_seq, H);
+}
+
+int kda_backward(const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,
+                 const float *A_log, const float *dt_bias, const float *h_chunks,
+                 const int32_t *cu_seqlens, const void *do_, const float *dh_T, void *dq, void *dk,
+                 void *dv, void *dg_raw, void *dbeta_raw, float *dA_log, float *ddt_bias, float *dh0,
+                 void *workspace, size_t workspace_bytes, int B, int T, int H, int dk_, int dv_,
+                 int n_seq, float scale, kda_dtype dtype, hipStream_t stream)
+{
+    // the stored states come from the bf16 d = 128 forward (fp32 activations are built for dk = 64 only)
+    if (dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (dk_ != 128 || dv_ != 128) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || H <= 0 || n_seq < 0) return KDA_ERR_SHAPE;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_SHAPE;
+    } else if (n_seq != B) {
+        return KDA_ERR_SHAPE;
+    }
+    const long long tokens = cu_seqlens ? (long long)T : (long long)B * T;
+    if (tokens * H * 128 > 0x7fffffffLL * 8) return KDA_ERR_SHAPE;
+    if ((long long)n_seq * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (n_seq == 0) return KDA_OK;
+    if (!A_log || !dt_bias || !workspace) return KDA_ERR_NULL;
+    if (tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !h_chunks || !do_ || !dq || !dk || !dv ||
+                       !dg_raw || !dbeta_raw))
+        return KDA_ERR_NULL;
+    if (workspace_bytes < kda::bwd_workspace_bytes(n_seq, H)) return KDA_ERR_SHAPE;
+    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, cu_seqlens, do_, dh_T,
+                          dq, dk, dv, dg_raw, dbeta_raw, dA_log, ddt_bias, dh0, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    kda::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw; a.do_ = do_;
+    a.A_log = A_log; a.dt_bias = dt_bias; a.h_chunks = h_chunks; a.dh_T = dh_T; a.cu_seqlens = cu_seqlens;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg_raw = dg_raw; a.dbeta_raw = dbeta_raw;
+    a.dA_log = dA_log; a.ddt_bias = ddt_bias; a.dh0 = dh0;
+    a.work = static_cast<float *>(workspace); a.work_params = nullptr;
+    a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
+    const hipError_t e = kda::launch_bwd(a, dtype == KDA_BF16 ? 1 : 0, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int kda_chunk_fwd_check(hipStream_t stream)
 {
     void *ws = nullptr;

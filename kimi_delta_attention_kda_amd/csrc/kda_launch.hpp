@@ -59,6 +59,20 @@ struct ChunkArgs {
     int pair_half;         // workgroups per XCD in the first dispatch round (0: no CU pairing)
 };
 
+struct BwdArgs {
+    const void *q, *k, *v, *g_raw, *beta_raw, *do_;
+    const float *A_log, *dt_bias, *h_chunks, *dh_T;
+    const int32_t *cu_seqlens;
+    void *dq, *dk, *dv, *dg_raw, *dbeta_raw;
+    float *dA_log, *ddt_bias, *dh0;
+    float *work;          // caller's workspace: per-chain token states, then per-chain parameter sums
+    float *work_params;   // set by the launcher
+    int T, H, n_seq;      // T: per-sequence length for dense input, total tokens if cu_seqlens
+    float scale;
+};
+size_t bwd_workspace_bytes(int n_seq, int H);
+hipError_t launch_bwd(const BwdArgs &a, int dtype, hipStream_t stream);
+
 // Bytes of the flag area (team blocks, then a 256-byte block for the error word).
 inline size_t chunk_flag_bytes() { return sizeof(int) * ((size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS + 64); }
 // Device bytes of the chunk-forward workspace.

@@ -189,6 +189,16 @@ class Prefill:
         return out
 
 
+def cotangents(seed: int, tokens: int, H: int, dv: int, dk: int, n_seq: int, with_dhT: bool = True):
+    """Gradients flowing into the forward's outputs for a backward test: do ~
+    N(0, 1) per (token, head, column) as bf16 bits, and dh_T ~ N(0, 0.02^2)
+    float32 (or None)."""
+    st = _Streams(seed + 2000)
+    do = bf16_bits(st.normal((tokens, H, dv)))
+    dhT = st.normal((n_seq, H, dv, dk), 0.02) if with_dhT else None
+    return do, dhT
+
+
 def prefill(seed: int, B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16", *,
             lengths=None, n_var: int = 0, with_h0: bool = False, A_log_hi: float = LOG16,
             gate_stress: float = 0.0, name: str = "custom") -> Prefill:

@@ -167,6 +167,30 @@ def test_conv_decode_validation(lib):
     assert conv_decode(lib, B=0) == 0
 
 
+def backward(lib, **kw):
+    args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, hc=A, cu=None, do=A, dhT=None, dq=A, dk=A, dv=A,
+                dg=A, db=A, dA=None, ddt=None, dh0=None, ws=A, wsb=1 << 30, B=1, T=16, H=1, dk_=128, dv_=128,
+                n_seq=1, scale=0.1, dtype=1)
+    args.update(kw)
+    return lib.kda_backward(*(args[k_] for k_ in ("q", "k", "v", "g", "b", "A_log", "dt", "hc", "cu", "do",
+                                                  "dhT", "dq", "dk", "dv", "dg", "db", "dA", "ddt", "dh0",
+                                                  "ws", "wsb", "B", "T", "H", "dk_", "dv_", "n_seq", "scale",
+                                                  "dtype")), None)
+
+
+def test_backward_validation(lib):
+    assert lib.kda_backward_workspace_bytes(2, 3, 128, 128) == 6 * (16 * 128 * 128 + 129) * 4
+    assert lib.kda_backward_workspace_bytes(2, 3, 64, 128) == 0
+    assert backward(lib, dtype=0) == -3               # float32 activations: no d = 128 forward to pair with
+    assert backward(lib, dk_=64) == -3
+    assert backward(lib, wsb=1024) == -2              # workspace too small
+    assert backward(lib, ws=None) == -1
+    assert backward(lib, hc=None) == -1
+    assert backward(lib, do=MIS) == -4
+    assert backward(lib, n_seq=2) == -2               # dense input needs n_seq == B
+    assert backward(lib, n_seq=0, B=0) == 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 16, 1, 64)
