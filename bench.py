@@ -18,7 +18,8 @@ workload) and kda_decode_extend with T = 4 tokens per row (decode workload's
 rows, heads and pool) are timed the same way and reported as extra fields,
 as is kda_conv_decode_step (width-4 convolution fused with the decode step)
 and the two passes of the materialised form on the prefill workload
-(kda_chunk_fwd_states, then the chunk-parallel output pass).
+(kda_chunk_fwd_states, then the chunk-parallel output pass), and
+kda_backward from those states.
 """
 from __future__ import annotations
 
@@ -318,7 +319,26 @@ def main():
     act_bytes = p.tokens * p.H * (2 * (3 * p.dk + p.dv + 1) + 2 * p.dv)
     states_gbs = (prefill_bytes(p) + snap_bytes) / mat_avg[0] / 1e9
     chunk_o_gbs = (act_bytes + snap_bytes) / mat_avg[1] / 1e9
-    del hcb
+
+    # the backward from those stored states (seeded do, no dh_T), timed the same way
+    do_bits, _ = synth.cotangents(1, p.tokens, p.H, p.dv, p.dk, p.n_seq, with_dhT=False)
+    dob = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(dev).reshape(o.shape)
+    wsb = torch.empty(kda.load_library().kda_backward_workspace_bytes(p.n_seq, p.H, p.dk, p.dv),
+                      dtype=torch.uint8, device=dev)
+
+    def backward_call():
+        kda.backward(**pin_noh0, h_chunks=hcb, do=dob, scale=p.scale, workspace=wsb)
+
+    backward_call()
+    evb = [torch.cuda.Event(enable_timing=True) for _ in range(min(K, 5) + 1)]
+    torch.cuda.synchronize()
+    evb[0].record()
+    for s_ in range(len(evb) - 1):
+        backward_call()
+        evb[s_ + 1].record()
+    torch.cuda.synchronize()
+    bwd_avg = float(np.mean([evb[s_].elapsed_time(evb[s_ + 1]) for s_ in range(len(evb) - 1)])) * 1e-3
+    del hcb, wsb, dob
 
     # T = 4 tokens per row through kda_decode_extend (speculative-verify shape) on
     # the decode workload's rows, heads and pool, timed the same way
@@ -424,6 +444,7 @@ def main():
         "states_gbs": round(states_gbs, 1),
         "chunk_o_us": round(mat_avg[1] * 1e6, 2),
         "chunk_o_gbs": round(chunk_o_gbs, 1),
+        "backward_us": round(bwd_avg * 1e6, 2),
         "decode_us": round(dec_avg * 1e6, 2),
         "decode_host_us_per_call": round(host_dec / K * 1e6, 2),
         "extend_T": EXTEND_T,
