@@ -323,7 +323,7 @@ def main():
     # the backward from those stored states (seeded do, no dh_T), timed the same way
     do_bits, _ = synth.cotangents(1, p.tokens, p.H, p.dv, p.dk, p.n_seq, with_dhT=False)
     dob = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).to(dev).reshape(o.shape)
-    wsb = torch.empty(kda.load_library().kda_backward_workspace_bytes(p.n_seq, p.H, p.dk, p.dv),
+    wsb = torch.empty(kda.backward_workspace_bytes(p.n_seq, p.H, p.tokens),
                       dtype=torch.uint8, device=dev)
 
     def backward_call():

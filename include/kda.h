@@ -176,14 +176,15 @@ int kda_chunk_fwd_states(const void *q, const void *k, const void *v,
  *   dq, dk, dg_raw : [T_all, H, dk], dv : [T_all, H, dv], dbeta_raw : [T_all, H]
  *                    in the activation dtype;
  *   dA_log [H], ddt_bias [H, dk], dh0 [n_seq, H, dv, dk] float32.
- * workspace: device memory of at least kda_backward_workspace_bytes() bytes
- * (1 MiB per (sequence, head) and a small per-chain area), owned by the
- * caller; its contents on entry do not matter.
+ * workspace: device memory of at least kda_backward_workspace_bytes() bytes,
+ * owned by the caller (1 MiB per (sequence, head) for the recomputed token
+ * states, 1.5 KiB per (token, head) for partial column sums, and a small area
+ * per block of 64 tokens); its contents on entry do not matter.
  * Built for dk = dv = 128 with bfloat16 activations (those of the d = 128
  * forward; other shapes and float32 return KDA_ERR_UNSUPPORTED).  The result
  * is deterministic (no atomics).  Returns KDA_OK or a negative kda_status.
  */
-size_t kda_backward_workspace_bytes(int n_seq, int H, int dk, int dv);
+size_t kda_backward_workspace_bytes(int n_seq, int H, int dk, int dv, int64_t total_tokens);
 int kda_backward(const void *q, const void *k, const void *v,
                  const void *g_raw, const void *beta_raw,
                  const float *A_log, const float *dt_bias,

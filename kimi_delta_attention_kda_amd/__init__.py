@@ -50,7 +50,7 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_extend.restype = I
     lib.kda_conv_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.kda_conv_decode_step.restype = I
-    lib.kda_backward_workspace_bytes.argtypes = [I, I, I, I]
+    lib.kda_backward_workspace_bytes.argtypes = [I, I, I, I, ctypes.c_int64]
     lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                  ctypes.c_size_t, I, I, I, I, I, I, F, I, P]
@@ -412,7 +412,7 @@ def backward(q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, do, dh_T=None, 
     if scale is None:
         scale = dk ** -0.5
     lib = load_library()
-    need = lib.kda_backward_workspace_bytes(n_seq, H, dk, dv)
+    need = lib.kda_backward_workspace_bytes(n_seq, H, dk, dv, B * T)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _dev("workspace", workspace)
@@ -431,3 +431,8 @@ def backward(q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, do, dh_T=None, 
         _ptr(out["dh0"]), _ptr(workspace), workspace.numel() * workspace.element_size(), B, T, H, dk, dv,
         n_seq, float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
     return out
+
+
+def backward_workspace_bytes(n_seq: int, H: int, total_tokens: int, dk: int = 128, dv: int = 128) -> int:
+    """Bytes of device workspace kda_backward needs (0: unsupported shape)."""
+    return int(load_library().kda_backward_workspace_bytes(n_seq, H, dk, dv, total_tokens))

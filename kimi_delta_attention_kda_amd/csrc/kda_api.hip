@@ -130,10 +130,10 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *
                           chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, scale, dtype, stream);
 }
 
-size_t kda_backward_workspace_bytes(int n_seq, int H, int dk, int dv)
+size_t kda_backward_workspace_bytes(int n_seq, int H, int dk, int dv, int64_t total_tokens)
 {
-    if (n_seq < 0 || H <= 0 || dk != 128 || dv != 128) return 0;
-    return kda::bwd_workspace_bytes(n_seq, H);
+    if (n_seq < 0 || H <= 0 || dk != 128 || dv != 128 || total_tokens < 0) return 0;
+    return kda::bwd_workspace_bytes(n_seq, H, total_tokens);
 }
 
 int kda_backward(const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,
@@ -160,7 +160,7 @@ int kda_backward(const void *q, const void *k, const void *v, const void *g_raw,
     if (tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !h_chunks || !do_ || !dq || !dk || !dv ||
                        !dg_raw || !dbeta_raw))
         return KDA_ERR_NULL;
-    if (workspace_bytes < kda::bwd_workspace_bytes(n_seq, H)) return KDA_ERR_SHAPE;
+    if (workspace_bytes < kda::bwd_workspace_bytes(n_seq, H, tokens)) return KDA_ERR_SHAPE;
     const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, cu_seqlens, do_, dh_T,
                           dq, dk, dv, dg_raw, dbeta_raw, dA_log, ddt_bias, dh0, workspace};
     for (const void *p : ptrs)
@@ -170,8 +170,8 @@ int kda_backward(const void *q, const void *k, const void *v, const void *g_raw,
     a.A_log = A_log; a.dt_bias = dt_bias; a.h_chunks = h_chunks; a.dh_T = dh_T; a.cu_seqlens = cu_seqlens;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg_raw = dg_raw; a.dbeta_raw = dbeta_raw;
     a.dA_log = dA_log; a.ddt_bias = ddt_bias; a.dh0 = dh0;
-    a.work = static_cast<float *>(workspace); a.work_params = nullptr;
-    a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
+    a.work = static_cast<float *>(workspace); a.part = a.part_beta = a.params = nullptr;
+    a.T = T; a.H = H; a.n_seq = n_seq; a.T_all = tokens; a.scale = scale;
     const hipError_t e = kda::launch_bwd(a, dtype == KDA_BF16 ? 1 : 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -19,13 +19,16 @@
 // entering state (kda_chunk_fwd_states), its 16 per-token states recomputed in
 // fp32 and kept in the caller's workspace, then the adjoint token by token.
 //
-// MI355X mapping: one 512-thread workgroup per (sequence, head) chain, the
-// state and its gradient in registers on the T=1 decode kernel's layout
-// (half p, thread (g, j): rows 64p + g + 16r, r < 4, and columns 4j.., 64+4j..).
-// Row sums (w, du) run over the 16 lanes of a row group with DPP; column sums
-// (dq, dk, dg) and the beta sum over rows go through LDS.  No atomics: the
-// result is deterministic.  The per-chain sums of dA_log and ddt_bias are
-// reduced over sequences by a second small kernel.
+// MI355X mapping: four 512-thread workgroups per (sequence, head) chain, one
+// per quarter of the state's 128 rows (rows are independent given the token's
+// vectors), so the prefill workload's 64 chains fill 256 compute units.  A
+// thread holds one row and 8 columns (4j.., 64+4j..) of the state and of its
+// gradient in registers; the row sums (w, du) run over the 16 lanes of a row
+// group with DPP.  The column sums (dq, dk, dg) and the beta sum over a
+// quarter's rows go through LDS and are written per token and quarter; a
+// second kernel adds the quarters, applies the chain rule through the gate
+// and beta, and sums dA_log and ddt_bias over token blocks, and a third sums
+// those blocks.  No atomics: the result is deterministic.
 #include <stdint.h>
 
 #include "kda_device.hpp"
@@ -51,17 +54,24 @@ __device__ __forceinline__ void st(void *p, size_t i, float x) {
 
 }  // namespace
 
+constexpr int NQ = 4;            // row quarters per chain (workgroups per chain)
+constexpr int QR = BV / NQ;      // rows per workgroup
+constexpr int TB = 64;           // tokens per block of the finishing kernel
+
 template <bool BF16>
 __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
 {
-    constexpr int ROWS = BV / 32;
-    __shared__ f32x4 Lq[BCH][BK / 4], Lk[BCH][BK / 4], Le[BCH][BK / 4], Lg[BCH][BK / 4], Ls[BCH][BK / 4];
-    __shared__ float Lv[BCH][BV], Ldo[BCH][BV], Lu[BCH][BV], Lvw[BCH][BV];
+    __shared__ f32x4 Lq[BCH][BK / 4], Lk[BCH][BK / 4], Le[BCH][BK / 4];
+    __shared__ float Lv[BCH][QR], Ldo[BCH][QR], Lu[BCH][QR], Lvw[BCH][QR];
     __shared__ float Lbeta[BCH];
-    __shared__ float red[3][32][BK];     // column partials of dqb, dk, dg per row group
-    __shared__ float rowred[32];         // beta-gradient partials per row group
+    // column partials of dqb, dk, dg and the beta terms per row, double-buffered
+    // over tokens so one barrier per token suffices: token t's partials are
+    // summed while token t-1's are written to the other buffer, and the barrier
+    // of token t-1 orders the sums of t before the writes of t-2
+    __shared__ float red[2][3][QR][BK];
+    __shared__ float rowred[2][QR];
 
-    const int chain = blockIdx.x;
+    const int chain = blockIdx.x / NQ, quarter = blockIdx.x - chain * NQ;
     const int seq = chain / a.H, head = chain - seq * a.H;
     size_t bos;
     int len;
@@ -78,27 +88,24 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
     }
     const int nch = (len + BCH - 1) / BCH;
     const int tid = threadIdx.x;
-    const int half = tid >> 8, tl = tid & 255, g = tl >> 4, j = tl & 15;
-    const int r0 = 64 * half;
-    const int grp = 16 * half + g;                    // row group 0..31
+    const int g = tid >> 4, j = tid & 15;             // row g of the quarter, columns 4j.., 64+4j..
+    const int row = quarter * QR + g;
     const size_t H = a.H;
     const float A = expf(a.A_log[head]);
 
-    // gradient of the state after the last token
-    f32x4 D[ROWS][2];
+    // gradient of the state after the last token (this thread's row and columns)
+    f32x4 D[2];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            if (a.dh_T) {
-                const size_t at = (((size_t)seq * H + head) * BV + r0 + g + 16 * r) * BK + 4 * j + 64 * h2;
-                D[r][h2] = *reinterpret_cast<const f32x4 *>(a.dh_T + at);
-            } else {
-                D[r][h2] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+    for (int h2 = 0; h2 < 2; ++h2) {
+        if (a.dh_T) {
+            const size_t at = (((size_t)seq * H + head) * BV + row) * BK + 4 * j + 64 * h2;
+            D[h2] = *reinterpret_cast<const f32x4 *>(a.dh_T + at);
+        } else {
+            D[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    float acc_dt = 0.f, acc_A = 0.f;   // threads 256..383 own column tid - 256 of ddt_bias / dA_log
-    float *scr = a.work + (size_t)chain * BCH * BV * BK;
+    }
+    // workspace: this workgroup's token states [BCH][QR][BK]
+    float *scr = a.work + ((size_t)chain * NQ + quarter) * BCH * QR * BK;
 
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * BCH;
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
             const int tt = tid >> 5, c4 = 4 * (tid & 31);
             if (tt < nt) {
                 const size_t tok = bos + t0 + tt;
-                f32x4 qv, kv, ev, gv, sv;
+                f32x4 qv, kv, ev;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const size_t i = (tok * H + head) * BK + c4 + e;
@@ -116,21 +123,15 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
                     const float sp = z > 20.f ? z : log1pf(expf(z));
                     qv[e] = a.scale * ld<BF16>(a.q, i);
                     kv[e] = ld<BF16>(a.k, i);
-                    gv[e] = -A * sp;
-                    ev[e] = expf(gv[e]);
-                    sv[e] = sigmoid_f(z);
+                    ev[e] = expf(-A * sp);
                 }
                 Lq[tt][tid & 31] = qv;
                 Lk[tt][tid & 31] = kv;
                 Le[tt][tid & 31] = ev;
-                Lg[tt][tid & 31] = gv;
-                Ls[tt][tid & 31] = sv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const size_t iv = (tok * H + head) * BV + c4 + e;
-                    Lv[tt][c4 + e] = ld<BF16>(a.v, iv);
-                    Ldo[tt][c4 + e] = ld<BF16>(a.do_, iv);
-                }
+                const int r = tid & 31;
+                const size_t iv = (tok * H + head) * BV + quarter * QR + r;
+                Lv[tt][r] = ld<BF16>(a.v, iv);
+                Ldo[tt][r] = ld<BF16>(a.do_, iv);
             }
             if (tid < nt) Lbeta[tid] = sigmoid_f(ld<BF16>(a.beta_raw, (bos + t0 + tid) * H + head));
         }
@@ -138,172 +139,183 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
 
         // ---- forward recompute from the stored entering state; keep every token's
         // entering state (this thread's elements) in the workspace
-        f32x4 S[ROWS][2];
+        f32x4 S[2];
         {
-            const float *hc = a.h_chunks + ((cbase + c) * H + head) * (size_t)BV * BK;
+            const float *hc = a.h_chunks + (((cbase + c) * H + head) * BV + row) * (size_t)BK;
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-                    S[r][h2] = *reinterpret_cast<const f32x4 *>(hc + (size_t)(r0 + g + 16 * r) * BK + 4 * j + 64 * h2);
+            for (int h2 = 0; h2 < 2; ++h2) S[h2] = *reinterpret_cast<const f32x4 *>(hc + 4 * j + 64 * h2);
         }
         for (int tt = 0; tt < nt; ++tt) {
-            float *sc = scr + (size_t)tt * BV * BK;
-            f32x4 e4[2], k4[2];
+            float *sc = scr + ((size_t)tt * QR + g) * BK;
+            float w = 0.f;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                e4[h2] = Le[tt][j + 16 * h2];
-                k4[h2] = Lk[tt][j + 16 * h2];
+                const f32x4 e4 = Le[tt][j + 16 * h2], k4 = Lk[tt][j + 16 * h2];
+                *reinterpret_cast<f32x4 *>(sc + 4 * j + 64 * h2) = S[h2];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    S[h2][e] *= e4[e];
+                    w += S[h2][e] * k4[e];
+                }
             }
-            const float beta = Lbeta[tt];
+            w = row16_sum(w);
+            const float vw = Lv[tt][g] - w;
+            const float u = Lbeta[tt] * vw;
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) {
-                const int row = r0 + g + 16 * r;
-                float w = 0.f;
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const f32x4 k4 = Lk[tt][j + 16 * h2];
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    *reinterpret_cast<f32x4 *>(sc + (size_t)row * BK + 4 * j + 64 * h2) = S[r][h2];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        S[r][h2][e] *= e4[h2][e];
-                        w += S[r][h2][e] * k4[h2][e];
-                    }
-                }
-                w = row16_sum(w);
-                const float vw = Lv[tt][row] - w;
-                const float u = beta * vw;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) S[r][h2][e] += u * k4[h2][e];
-                if (j == 0) {
-                    Lu[tt][row] = u;
-                    Lvw[tt][row] = vw;
-                }
+                for (int e = 0; e < 4; ++e) S[h2][e] += u * k4[e];
+            }
+            if (j == 0) {
+                Lu[tt][g] = u;
+                Lvw[tt][g] = vw;
             }
         }
         __syncthreads();
 
-        // ---- adjoint, tokens in reverse
+        // ---- adjoint, tokens in reverse; each token's entering state is loaded one
+        // token ahead
+        f32x4 snext[2];
+        {
+            const float *sc = scr + ((size_t)(nt - 1) * QR + g) * BK;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) snext[h2] = *reinterpret_cast<const f32x4 *>(sc + 4 * j + 64 * h2);
+        }
         for (int tt = nt - 1; tt >= 0; --tt) {
             const size_t tok = bos + t0 + tt;
-            const float *sc = scr + (size_t)tt * BV * BK;
-            f32x4 e4[2], k4[2], q4[2];
+            const int rb = tt & 1;
+            const f32x4 scur[2] = {snext[0], snext[1]};
+            if (tt > 0) {
+                const float *sc = scr + ((size_t)(tt - 1) * QR + g) * BK;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) snext[h2] = *reinterpret_cast<const f32x4 *>(sc + 4 * j + 64 * h2);
+            }
+            const float beta = Lbeta[tt];
+            const float u = Lu[tt][g], vw = Lvw[tt][g], dO = Ldo[tt][g];
+            f32x4 e4[2], k4[2], Sd[2], Sp[2];
+            float du = 0.f;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 e4[h2] = Le[tt][j + 16 * h2];
                 k4[h2] = Lk[tt][j + 16 * h2];
-                q4[h2] = Lq[tt][j + 16 * h2];
-            }
-            const float beta = Lbeta[tt];
-            f32x4 pq[2] = {}, pk[2] = {}, pg[2] = {};
-            float pb = 0.f;
+                const f32x4 q4 = Lq[tt][j + 16 * h2];
+                const f32x4 s0 = scur[h2];
+                f32x4 pq;
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) {
-                const int row = r0 + g + 16 * r;
-                const float u = Lu[tt][row], vw = Lvw[tt][row], dO = Ldo[tt][row];
-                f32x4 Sd[2], Sp[2];
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sc + (size_t)row * BK + 4 * j + 64 * h2);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        Sd[h2][e] = s0[e] * e4[h2][e];           // S'
-                        Sp[h2][e] = Sd[h2][e] + u * k4[h2][e];   // S+
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    Sd[h2][e] = s0[e] * e4[h2][e];              // S'
+                    Sp[h2][e] = Sd[h2][e] + u * k4[h2][e];      // S+
+                    D[h2][e] += dO * q4[e];
+                    pq[e] = Sp[h2][e] * dO;
+                    du += D[h2][e] * k4[h2][e];
                 }
-                float du = 0.f;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        D[r][h2][e] += dO * q4[h2][e];
-                        pq[h2][e] += Sp[h2][e] * dO;
-                        du += D[r][h2][e] * k4[h2][e];
-                    }
-                du = row16_sum(du);
-                const float dw = -beta * du;
-                if (j == 0) {
-                    st<BF16>(a.dv, (tok * H + head) * BV + row, beta * du);
-                    pb += du * vw;
-                }
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float dSd = D[r][h2][e] + dw * k4[h2][e];
-                        pk[h2][e] += D[r][h2][e] * u + Sd[h2][e] * dw;
-                        pg[h2][e] += dSd * Sd[h2][e];
-                        D[r][h2][e] = dSd * e4[h2][e];
-                    }
+                *reinterpret_cast<f32x4 *>(&red[rb][0][g][4 * j + 64 * h2]) = pq;
             }
-            // column partials of this row group -> LDS
+            du = row16_sum(du);
+            const float dw = -beta * du;
+            if (j == 0) {
+                st<BF16>(a.dv, (tok * H + head) * BV + row, beta * du);
+                rowred[rb][g] = du * vw;
+            }
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-                *reinterpret_cast<f32x4 *>(&red[0][grp][4 * j + 64 * h2]) = pq[h2];
-                *reinterpret_cast<f32x4 *>(&red[1][grp][4 * j + 64 * h2]) = pk[h2];
-                *reinterpret_cast<f32x4 *>(&red[2][grp][4 * j + 64 * h2]) = pg[h2];
+                f32x4 pk, pg;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float dSd = D[h2][e] + dw * k4[h2][e];
+                    pk[e] = D[h2][e] * u + Sd[h2][e] * dw;
+                    pg[e] = dSd * Sd[h2][e];
+                    D[h2][e] = dSd * e4[h2][e];
+                }
+                *reinterpret_cast<f32x4 *>(&red[rb][1][g][4 * j + 64 * h2]) = pk;
+                *reinterpret_cast<f32x4 *>(&red[rb][2][g][4 * j + 64 * h2]) = pg;
             }
-            if (j == 0) rowred[grp] = pb;
             __syncthreads();
+            // this quarter's column sums and beta term for the token
             if (tid < 3 * BK) {
                 const int qty = tid >> 7, col = tid & (BK - 1);
                 float sum = 0.f;
 #pragma unroll 8
-                for (int gg = 0; gg < 32; ++gg) sum += red[qty][gg][col];
-                const size_t i = (tok * H + head) * BK + col;
-                if (qty == 0) {
-                    st<BF16>(a.dq, i, a.scale * sum);
-                } else if (qty == 1) {
-                    st<BF16>(a.dk, i, sum);
-                } else {
-                    const f32x4 gz = Lg[tt][col >> 2], sz = Ls[tt][col >> 2];
-                    const float dz = -A * sz[col & 3] * sum;
-                    st<BF16>(a.dg_raw, i, dz);
-                    acc_dt += dz;
-                    acc_A += sum * gz[col & 3];
-                }
+                for (int gg = 0; gg < QR; ++gg) sum += red[rb][qty][gg][col];
+                a.part[((size_t)quarter * a.T_all + tok) * H * (3 * BK) + head * (3 * BK) + qty * BK + col] = sum;
             } else if (tid == 3 * BK) {
                 float sb = 0.f;
-                for (int gg = 0; gg < 32; ++gg) sb += rowred[gg];
-                const float beta_t = Lbeta[tt];
-                st<BF16>(a.dbeta_raw, tok * H + head, sb * beta_t * (1.f - beta_t));
+                for (int gg = 0; gg < QR; ++gg) sb += rowred[rb][gg];
+                a.part_beta[((size_t)quarter * a.T_all + tok) * H + head] = sb;
             }
-            __syncthreads();
         }
+        __syncthreads();   // the chunk's sums done before the next chunk's staging and writes
     }
 
     // gradient of the initial state
     if (a.dh0) {
 #pragma unroll
-        for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const size_t at = (((size_t)seq * H + head) * BV + r0 + g + 16 * r) * BK + 4 * j + 64 * h2;
-                *reinterpret_cast<f32x4 *>(a.dh0 + at) = D[r][h2];
-            }
-    }
-    // this chain's sums for ddt_bias (per channel) and dA_log
-    float *part = a.work_params + (size_t)chain * (BK + 1);
-    if (tid >= 2 * BK && tid < 3 * BK) part[tid - 2 * BK] = acc_dt;
-    // dA_log: sum the 128 column threads' terms (they are waves 4 and 5)
-    __syncthreads();
-    if (tid >= 2 * BK && tid < 3 * BK) red[0][0][tid - 2 * BK] = acc_A;
-    __syncthreads();
-    if (tid == 0) {
-        float s = 0.f;
-        for (int cc = 0; cc < BK; ++cc) s += red[0][0][cc];
-        part[BK] = s;
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const size_t at = (((size_t)seq * H + head) * BV + row) * BK + 4 * j + 64 * h2;
+            *reinterpret_cast<f32x4 *>(a.dh0 + at) = D[h2];
+        }
     }
 }
 
-// dA_log[h] and ddt_bias[h, :] from the per-chain sums, summed over sequences.
-__global__ __launch_bounds__(128) void bwd_params_kernel(const float *__restrict__ part, float *__restrict__ dA_log,
-                                                          float *__restrict__ ddt_bias, int n_seq, int H)
+// Per token block and head: add the quarters' column sums and apply the chain
+// rule through q's scale, the gate (dz = -A sigmoid(z) dg with
+// z = g_raw + dt_bias) and beta (db = dbeta beta (1 - beta)); the block's sums
+// of dz (ddt_bias) and dg . g (dA_log) go to params[block][head].
+template <bool BF16>
+__global__ __launch_bounds__(BK) void bwd_finish_kernel(BwdArgs a)
+{
+    __shared__ float sA[BK];
+    const int blk = blockIdx.x, head = blockIdx.y, col = threadIdx.x;
+    const size_t H = a.H;
+    const float A = expf(a.A_log[head]);
+    const float dtb = a.dt_bias[(size_t)head * BK + col];
+    float acc_dt = 0.f, acc_A = 0.f;
+    const size_t tend = min((size_t)a.T_all, (size_t)(blk + 1) * TB);
+    for (size_t tok = (size_t)blk * TB; tok < tend; ++tok) {
+        float sq = 0.f, sk = 0.f, sg = 0.f;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) {
+            const float *p = a.part + ((size_t)qq * a.T_all + tok) * H * (3 * BK) + head * (3 * BK);
+            sq += p[col];
+            sk += p[BK + col];
+            sg += p[2 * BK + col];
+        }
+        const size_t i = (tok * H + head) * BK + col;
+        st<BF16>(a.dq, i, a.scale * sq);
+        st<BF16>(a.dk, i, sk);
+        const float z = ld<BF16>(a.g_raw, i) + dtb;
+        const float sp = z > 20.f ? z : log1pf(expf(z));
+        const float dz = -A * sigmoid_f(z) * sg;
+        st<BF16>(a.dg_raw, i, dz);
+        acc_dt += dz;
+        acc_A += sg * (-A * sp);
+        if (col == 0) {
+            float sb = 0.f;
+#pragma unroll
+            for (int qq = 0; qq < NQ; ++qq) sb += a.part_beta[((size_t)qq * a.T_all + tok) * H + head];
+            const float beta = sigmoid_f(ld<BF16>(a.beta_raw, tok * H + head));
+            st<BF16>(a.dbeta_raw, tok * H + head, sb * beta * (1.f - beta));
+        }
+    }
+    float *pp = a.params + ((size_t)blk * H + head) * (BK + 1);
+    pp[col] = acc_dt;
+    sA[col] = acc_A;
+    __syncthreads();
+    if (col == 0) {
+        float s = 0.f;
+        for (int cc = 0; cc < BK; ++cc) s += sA[cc];
+        pp[BK] = s;
+    }
+}
+
+// dA_log[h] and ddt_bias[h, :] from the per-block sums.
+__global__ __launch_bounds__(BK) void bwd_params_kernel(const float *__restrict__ part, float *__restrict__ dA_log,
+                                                         float *__restrict__ ddt_bias, int n_blk, int H)
 {
     const int head = blockIdx.x, col = threadIdx.x;
     float sdt = 0.f, sA = 0.f;
-    for (int s = 0; s < n_seq; ++s) {
+    for (int s = 0; s < n_blk; ++s) {
         const float *p = part + ((size_t)s * H + head) * (BK + 1);
         sdt += p[col];
         if (col == 0) sA += p[BK];
@@ -312,10 +324,12 @@ __global__ __launch_bounds__(128) void bwd_params_kernel(const float *__restrict
     if (col == 0 && dA_log) dA_log[head] = sA;
 }
 
-size_t bwd_workspace_bytes(int n_seq, int H)
+size_t bwd_workspace_bytes(int n_seq, int H, long long tokens)
 {
-    const size_t chains = (size_t)n_seq * H;
-    return chains * ((size_t)BCH * BV * BK + BK + 1) * sizeof(float);
+    const size_t chains = (size_t)n_seq * H, nblk = (size_t)((tokens + TB - 1) / TB);
+    return sizeof(float) * (chains * BCH * BV * BK                 // token states
+                            + (size_t)NQ * tokens * H * (3 * BK + 1)   // quarter column sums, beta terms
+                            + nblk * H * (BK + 1));                    // block parameter sums
 }
 
 hipError_t launch_bwd(const BwdArgs &args, int dtype, hipStream_t stream)
@@ -323,13 +337,27 @@ hipError_t launch_bwd(const BwdArgs &args, int dtype, hipStream_t stream)
     BwdArgs a = args;
     const int n_chains = a.n_seq * a.H;
     if (n_chains == 0) return hipSuccess;
-    a.work_params = a.work + (size_t)n_chains * BCH * BV * BK;
     if (dtype != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_kernel<true>, dim3((unsigned)n_chains), dim3(512), 0, stream, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_params_kernel, dim3((unsigned)a.H), dim3(BK), 0, stream, a.work_params, a.dA_log,
-                       a.ddt_bias, a.n_seq, a.H);
+    const size_t H = a.H;
+    a.part = a.work + (size_t)n_chains * BCH * BV * BK;
+    a.part_beta = a.part + (size_t)NQ * a.T_all * H * (3 * BK);
+    a.params = a.part_beta + (size_t)NQ * a.T_all * H;
+    const int nblk = (int)((a.T_all + TB - 1) / TB);
+    if (a.T_all > 0) {
+        hipLaunchKernelGGL(bwd_kernel<true>, dim3((unsigned)(n_chains * NQ)), dim3(512), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(bwd_finish_kernel<true>, dim3((unsigned)nblk, (unsigned)a.H), dim3(BK), 0, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    } else {
+        // no tokens: dh0 = dh_T; parameter gradients zero
+        hipLaunchKernelGGL(bwd_kernel<true>, dim3((unsigned)(n_chains * NQ)), dim3(512), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(bwd_params_kernel, dim3((unsigned)a.H), dim3(BK), 0, stream, a.params, a.dA_log,
+                       a.ddt_bias, nblk, a.H);
     return hipGetLastError();
 }
 

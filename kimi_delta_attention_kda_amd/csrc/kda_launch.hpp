@@ -65,12 +65,13 @@ struct BwdArgs {
     const int32_t *cu_seqlens;
     void *dq, *dk, *dv, *dg_raw, *dbeta_raw;
     float *dA_log, *ddt_bias, *dh0;
-    float *work;          // caller's workspace: per-chain token states, then per-chain parameter sums
-    float *work_params;   // set by the launcher
+    float *work;          // caller's workspace: token states, then the partial sums below
+    float *part, *part_beta, *params;   // set by the launcher (inside work)
     int T, H, n_seq;      // T: per-sequence length for dense input, total tokens if cu_seqlens
+    long long T_all;      // total tokens
     float scale;
 };
-size_t bwd_workspace_bytes(int n_seq, int H);
+size_t bwd_workspace_bytes(int n_seq, int H, long long tokens);
 hipError_t launch_bwd(const BwdArgs &a, int dtype, hipStream_t stream);
 
 // Bytes of the flag area (team blocks, then a 256-byte block for the error word).
