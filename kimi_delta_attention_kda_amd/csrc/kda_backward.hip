@@ -17,7 +17,8 @@
 // reverse loop over chunks from the states stored at chunk boundaries; this
 // kernel does the same: chunks in reverse, each restarted from its stored
 // entering state (kda_chunk_fwd_states), its 16 per-token states recomputed in
-// fp32 and kept in the caller's workspace, then the adjoint token by token.
+// fp32 and kept in registers (both token loops fully unrolled, 128 VGPRs of
+// history per thread), then the adjoint token by token.
 //
 // MI355X mapping: four 512-thread workgroups per (sequence, head) chain, one
 // per quarter of the state's 128 rows (rows are independent given the token's
@@ -104,8 +105,6 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
             D[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // workspace: this workgroup's token states [BCH][QR][BK]
-    float *scr = a.work + ((size_t)chain * NQ + quarter) * BCH * QR * BK;
 
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * BCH;
@@ -145,13 +144,15 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) S[h2] = *reinterpret_cast<const f32x4 *>(hc + 4 * j + 64 * h2);
         }
-        for (int tt = 0; tt < nt; ++tt) {
-            float *sc = scr + ((size_t)tt * QR + g) * BK;
+        f32x4 hist[BCH][2];   // entering state of every token of the chunk (this thread's elements)
+#pragma unroll
+        for (int tt = 0; tt < BCH; ++tt) {
+            if (tt < nt) {
             float w = 0.f;
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
                 const f32x4 e4 = Le[tt][j + 16 * h2], k4 = Lk[tt][j + 16 * h2];
-                *reinterpret_cast<f32x4 *>(sc + 4 * j + 64 * h2) = S[h2];
+                hist[tt][h2] = S[h2];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     S[h2][e] *= e4[e];
@@ -171,26 +172,17 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
                 Lu[tt][g] = u;
                 Lvw[tt][g] = vw;
             }
+            }
         }
         __syncthreads();
 
-        // ---- adjoint, tokens in reverse; each token's entering state is loaded one
-        // token ahead
-        f32x4 snext[2];
-        {
-            const float *sc = scr + ((size_t)(nt - 1) * QR + g) * BK;
+        // ---- adjoint, tokens in reverse (fully unrolled: the history stays in registers)
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) snext[h2] = *reinterpret_cast<const f32x4 *>(sc + 4 * j + 64 * h2);
-        }
-        for (int tt = nt - 1; tt >= 0; --tt) {
+        for (int tt = BCH - 1; tt >= 0; --tt) {
+            if (tt < nt) {
             const size_t tok = bos + t0 + tt;
             const int rb = tt & 1;
-            const f32x4 scur[2] = {snext[0], snext[1]};
-            if (tt > 0) {
-                const float *sc = scr + ((size_t)(tt - 1) * QR + g) * BK;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) snext[h2] = *reinterpret_cast<const f32x4 *>(sc + 4 * j + 64 * h2);
-            }
+            const f32x4 scur[2] = {hist[tt][0], hist[tt][1]};
             const float beta = Lbeta[tt];
             const float u = Lu[tt][g], vw = Lvw[tt][g], dO = Ldo[tt][g];
             f32x4 e4[2], k4[2], Sd[2], Sp[2];
@@ -243,6 +235,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
                 float sb = 0.f;
                 for (int gg = 0; gg < QR; ++gg) sb += rowred[rb][gg];
                 a.part_beta[((size_t)quarter * a.T_all + tok) * H + head] = sb;
+            }
             }
         }
         __syncthreads();   // the chunk's sums done before the next chunk's staging and writes
@@ -326,9 +319,9 @@ __global__ __launch_bounds__(BK) void bwd_params_kernel(const float *__restrict_
 
 size_t bwd_workspace_bytes(int n_seq, int H, long long tokens)
 {
-    const size_t chains = (size_t)n_seq * H, nblk = (size_t)((tokens + TB - 1) / TB);
-    return sizeof(float) * (chains * BCH * BV * BK                 // token states
-                            + (size_t)NQ * tokens * H * (3 * BK + 1)   // quarter column sums, beta terms
+    (void)n_seq;
+    const size_t nblk = (size_t)((tokens + TB - 1) / TB);
+    return sizeof(float) * ((size_t)NQ * tokens * H * (3 * BK + 1)   // quarter column sums, beta terms
                             + nblk * H * (BK + 1));                    // block parameter sums
 }
 
@@ -339,7 +332,7 @@ hipError_t launch_bwd(const BwdArgs &args, int dtype, hipStream_t stream)
     if (n_chains == 0) return hipSuccess;
     if (dtype != 1) return hipErrorInvalidValue;
     const size_t H = a.H;
-    a.part = a.work + (size_t)n_chains * BCH * BV * BK;
+    a.part = a.work;
     a.part_beta = a.part + (size_t)NQ * a.T_all * H * (3 * BK);
     a.params = a.part_beta + (size_t)NQ * a.T_all * H;
     const int nblk = (int)((a.T_all + TB - 1) / TB);

@@ -65,7 +65,7 @@ struct BwdArgs {
     const int32_t *cu_seqlens;
     void *dq, *dk, *dv, *dg_raw, *dbeta_raw;
     float *dA_log, *ddt_bias, *dh0;
-    float *work;          // caller's workspace: token states, then the partial sums below
+    float *work;          // caller's workspace: the partial sums below
     float *part, *part_beta, *params;   // set by the launcher (inside work)
     int T, H, n_seq;      // T: per-sequence length for dense input, total tokens if cu_seqlens
     long long T_all;      // total tokens
