@@ -195,8 +195,9 @@ def main():
         traffic_summary(*args.traffic_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (the path shards by head/sequence with "
-              "no exchange; multi-GPU runs are not part of it). Use --gpus 1.", file=sys.stderr)
+        print("bench.py: the benchmark runs on one GPU only (the path shards by head/sequence with "
+              "no exchange between GPUs; a multi-GPU run is not implemented). Use --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
