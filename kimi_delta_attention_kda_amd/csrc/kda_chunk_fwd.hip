@@ -1270,6 +1270,11 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
     }
 }
 
+__global__ __launch_bounds__(256) void chunk_flags_clear_kernel(int *flags, int n)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) flags[i] = 0;
+}
+
 template <bool BF16, int DK, int DV, int BDV, bool SNAP>
 static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
 {
@@ -1300,7 +1305,11 @@ static hipError_t launch_one(ChunkArgs a, hipStream_t stream)
     const int cus_per_xcd = n_cu / 8;
     const int cpt = (TS + 1) / 2;
     a.pair_half = (occ >= 2 && n_cu % 8 == 0 && teams_per_xcd * cpt <= cus_per_xcd) ? cus_per_xcd : 0;
-    e = hipMemsetAsync(a.flags, 0, chunk_flag_bytes(), stream);
+    // flags and the error word start at zero: a small fill kernel (not a memset,
+    // so that a caller may capture the launch in a graph)
+    hipLaunchKernelGGL(chunk_flags_clear_kernel, dim3(16), dim3(256), 0, stream, a.flags,
+                       (int)(chunk_flag_bytes() / sizeof(int)));
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned per_xcd = a.pair_half > 0 ? (unsigned)(cus_per_xcd + teams_per_xcd * cpt)
                                              : (unsigned)(teams_per_xcd * TS);
