@@ -3,6 +3,7 @@ in one launch) against the fp64 oracle, through the C ABI.  It covers:
 - small shapes with grouped heads and pads, gate stress and the un-normalised
   form;
 - the full decode width (B = 256, HV = 32) at T = 4;
+- T past one 16-token window (T = 37: three windows, the last partial);
 - T = 1, which must be bitwise kda_decode_step;
 - T tokens, which must be bitwise T successive kda_decode_step calls;
 - pad rows and unreferenced slots left bitwise untouched."""
@@ -67,7 +68,7 @@ def check_extend(d, l2norm=True, what=""):
 
 
 @pytest.mark.parametrize("B,T,H,HV,pads", [(1, 2, 4, 4, 0), (6, 5, 2, 8, 1), (32, 4, 8, 16, 3),
-                                           (16, 16, 4, 4, 2)])
+                                           (16, 16, 4, 4, 2), (5, 37, 2, 4, 1)])
 def test_extend_small(B, T, H, HV, pads):
     d = synth.extend(70 + B + T, B=B, T=T, H=H, HV=HV, K=128, V=128, P=B + 5, n_pad=pads)
     check_extend(d, what=f"extend B{B} T{T} H{H} HV{HV}")
