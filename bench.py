@@ -307,10 +307,13 @@ def main():
         kda.chunk_fwd_states(**pin, scale=p.scale, o=o, h_T=hT, h_chunks=hcb)
 
     def chunk_o_call():
+        kda.chunk_o(**pin_noh0, h_chunks=hcb, scale=p.scale, o=o)
+
+    def chunk_o_fwd_route_call():
         kda.chunk_o_from_states(**pin_noh0, h_chunks=hcb, scale=p.scale, o=o)
 
     mat_avg = []
-    for fn in (states_call, chunk_o_call):
+    for fn in (states_call, chunk_o_call, chunk_o_fwd_route_call):
         for _ in range(2):
             fn()
         evm = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
@@ -456,6 +459,7 @@ def main():
         "states_gbs": round(states_gbs, 1),
         "chunk_o_us": round(mat_avg[1] * 1e6, 2),
         "chunk_o_gbs": round(chunk_o_gbs, 1),
+        "chunk_o_fwd_route_us": round(mat_avg[2] * 1e6, 2),
         "backward_us": round(bwd_avg * 1e6, 2),
         "decode_us": round(dec_avg * 1e6, 2),
         "decode_host_us_per_call": round(host_dec / K * 1e6, 2),

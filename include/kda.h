@@ -5,6 +5,7 @@
  *
  *   kda_chunk_fwd       chunkwise prefill over dense or packed variable-length
  *                       sequences, returning the outputs and the final states;
+ *   kda_chunk_o         the materialised form's chunk-parallel output pass;
  *   kda_backward        gradients of the prefill with respect to every input,
  *                       from the states kda_chunk_fwd_states stores;
  *   kda_chunk_fwd_pool  the same prefill with the states in a decode state
@@ -151,6 +152,29 @@ int kda_chunk_fwd_states(const void *q, const void *k, const void *v,
                          void *o, float *h_T, float *h_chunks,
                          int B, int T, int H, int dk, int dv, int n_seq,
                          float scale, kda_dtype dtype, hipStream_t stream);
+
+/*
+ * kda_chunk_o -- the chunk-parallel output pass of the materialised form
+ * ([LA-06] chunkwise form; [TL-KDA] section 6): every chunk's outputs from the
+ * state entering it, each chunk independently.  Per chunk of 16 tokens with
+ * S0 = h_chunks[row] (G the chunk-local cumulative gate):
+ *   U = (I - L)^{-1} beta (v - (k e^G) S0^T),  o = scale ((q e^G) S0^T + Mqk U),
+ * L and Mqk as in kda_chunk_fwd (formed from per-pair exponents, fp32).
+ * Inputs as given to kda_chunk_fwd_states (q, k, v, g_raw, beta_raw, A_log,
+ * dt_bias, cu_seqlens, B, T, H, n_seq, scale) and its h_chunks output;
+ * n_chunks = its row count (sum of ceil(len / 16); B * ceil(T / 16) for
+ * dense input, checked).  Writes o [T_all, H, dv].  Built for bfloat16 with
+ * dk = dv = 128 (else KDA_ERR_UNSUPPORTED; kda_chunk_fwd over chunk-length
+ * sequences with h0 = h_chunks is the general route and reproduces
+ * kda_chunk_fwd bitwise; this pass agrees with it to bf16 rounding).
+ * Returns KDA_OK or a negative kda_status.
+ */
+int kda_chunk_o(const void *q, const void *k, const void *v,
+                const void *g_raw, const void *beta_raw,
+                const float *A_log, const float *dt_bias,
+                const float *h_chunks, const int32_t *cu_seqlens, void *o,
+                int B, int T, int H, int dk, int dv, int n_seq, int n_chunks,
+                float scale, kda_dtype dtype, hipStream_t stream);
 
 /*
  * kda_backward -- gradients of the forward of kda_chunk_fwd for a loss whose

@@ -20,7 +20,7 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
 EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_states", "kda_chunk_fwd_check", "kda_decode_step",
-           "kda_decode_extend", "kda_conv_decode_step", "kda_backward", "kda_backward_workspace_bytes",
+           "kda_decode_extend", "kda_conv_decode_step", "kda_chunk_o", "kda_backward", "kda_backward_workspace_bytes",
            "kda_status_str")
 
 
@@ -50,6 +50,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_decode_extend.restype = I
     lib.kda_conv_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
     lib.kda_conv_decode_step.restype = I
+    lib.kda_chunk_o.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P]
+    lib.kda_chunk_o.restype = I
     lib.kda_backward_workspace_bytes.argtypes = [I, I, I, I, ctypes.c_int64]
     lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
@@ -350,13 +352,48 @@ def chunk_fwd_states(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqle
     return o, h_T, h_chunks
 
 
+def chunk_o(q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, cu_seqlens=None, scale=None, o=None,
+            stream=None):
+    """The chunk-parallel output pass of the materialised form (kda_chunk_o):
+    every chunk's outputs from its state in h_chunks, one workgroup per
+    (chunk, head).  bfloat16, dk = dv = 128.  Returns o [B, T, H, dv]."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    for name, t in (("q", q), ("k", k), ("v", v), ("g_raw", g_raw), ("beta_raw", beta_raw)):
+        _dev(name, t, torch.bfloat16)
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias), ("h_chunks", h_chunks)):
+        _dev(name, t, torch.float32)
+    _dev("cu_seqlens", cu_seqlens, torch.int32)
+    if k.shape != q.shape or g_raw.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or tuple(beta_raw.shape) != (B, T, H):
+        raise KDAError("inconsistent activation shapes")
+    n_seq = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    nc = n_chunks(T, B, cu_seqlens)
+    if h_chunks.numel() != nc * H * dv * dk:
+        raise KDAError("h_chunks must hold [N_chunks, H, dv, dk] elements")
+    if scale is None:
+        scale = dk ** -0.5
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    _dev("o", o, torch.bfloat16)
+    if o.numel() != B * T * H * dv:
+        raise KDAError("o must hold [B, T, H, dv] elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(load_library().kda_chunk_o(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias), _ptr(h_chunks),
+        _ptr(cu_seqlens), _ptr(o), B, T, H, dk, dv, n_seq, nc, float(scale), KDA_BF16, ctypes.c_void_p(stream)))
+    return o
+
+
 def chunk_o_from_states(q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, cu_seqlens=None,
                         chunk: int = 16, scale=None, o=None, stream=None):
-    """The chunk-parallel output pass of the materialised form: kda_chunk_fwd
-    over every chunk as a sequence of its own, started from its state in
-    h_chunks (so all chunks are independent chains).  Dense input with
-    T % chunk == 0 is passed as B*T/chunk sequences of `chunk` tokens (same
-    buffers); otherwise chunk boundaries are passed as cu_seqlens.  Returns o."""
+    """The chunk-parallel output pass of the materialised form through
+    kda_chunk_fwd: every chunk as a sequence of its own, started from its
+    state in h_chunks (so all chunks are independent chains; bitwise the
+    outputs of kda_chunk_fwd).  Dense input with T % chunk == 0 is passed as
+    B*T/chunk sequences of `chunk` tokens (same buffers); otherwise chunk
+    boundaries are passed as cu_seqlens.  Returns o."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     if cu_seqlens is None and T % chunk == 0:

@@ -130,6 +130,33 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *
                           chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, scale, dtype, stream);
 }
 
+int kda_chunk_o(const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,
+                const float *A_log, const float *dt_bias, const float *h_chunks,
+                const int32_t *cu_seqlens, void *o, int B, int T, int H, int dk, int dv, int n_seq,
+                int n_chunks, float scale, kda_dtype dtype, hipStream_t stream)
+{
+    if (dtype != KDA_BF16 || dk != 128 || dv != 128) return KDA_ERR_UNSUPPORTED;
+    if (B < 0 || T < 0 || H <= 0 || n_seq < 0 || n_chunks < 0) return KDA_ERR_SHAPE;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_SHAPE;
+    } else {
+        if (n_seq != B) return KDA_ERR_SHAPE;
+        if ((long long)n_chunks != (long long)B * ((T + 15) / 16)) return KDA_ERR_SHAPE;
+    }
+    if ((long long)n_chunks * H > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (n_chunks == 0 || n_seq == 0) return KDA_OK;
+    if (!q || !k || !v || !g_raw || !beta_raw || !A_log || !dt_bias || !h_chunks || !o) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h_chunks, cu_seqlens, o};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    kda::ChunkOArgs a;
+    a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
+    a.A_log = A_log; a.dt_bias = dt_bias; a.h_chunks = h_chunks; a.cu_seqlens = cu_seqlens;
+    a.o = o; a.T = T; a.H = H; a.scale = scale;
+    const hipError_t e = kda::launch_chunk_o(a, n_chunks, stream);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 size_t kda_backward_workspace_bytes(int n_seq, int H, int dk, int dv, int64_t total_tokens)
 {
     if (n_seq < 0 || H <= 0 || dk != 128 || dv != 128 || total_tokens < 0) return 0;

@@ -59,6 +59,16 @@ struct ChunkArgs {
     int pair_half;         // workgroups per XCD in the first dispatch round (0: no CU pairing)
 };
 
+struct ChunkOArgs {
+    const void *q, *k, *v, *g_raw, *beta_raw;
+    const float *A_log, *dt_bias, *h_chunks;
+    const int32_t *cu_seqlens;
+    void *o;
+    int T, H;           // T: per-sequence length for dense input, total tokens if cu_seqlens
+    float scale;
+};
+hipError_t launch_chunk_o(const ChunkOArgs &a, long long n_chunks, hipStream_t stream);
+
 struct BwdArgs {
     const void *q, *k, *v, *g_raw, *beta_raw, *do_;
     const float *A_log, *dt_bias, *h_chunks, *dh_T;

@@ -167,6 +167,23 @@ def test_conv_decode_validation(lib):
     assert conv_decode(lib, B=0) == 0
 
 
+def chunk_o(lib, **kw):
+    args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, hc=A, cu=None, o=A, B=2, T=20, H=1, dk=128, dv=128,
+                n_seq=2, nc=4, scale=0.1, dtype=1)
+    args.update(kw)
+    return lib.kda_chunk_o(*(args[k_] for k_ in ("q", "k", "v", "g", "b", "A_log", "dt", "hc", "cu", "o", "B",
+                                                 "T", "H", "dk", "dv", "n_seq", "nc", "scale", "dtype")), None)
+
+
+def test_chunk_o_validation(lib):
+    assert chunk_o(lib, dtype=0) == -3
+    assert chunk_o(lib, dk=64) == -3
+    assert chunk_o(lib, nc=3) == -2                   # dense: B * ceil(T / 16) rows
+    assert chunk_o(lib, hc=None) == -1
+    assert chunk_o(lib, o=MIS) == -4
+    assert chunk_o(lib, B=0, n_seq=0, nc=0) == 0
+
+
 def backward(lib, **kw):
     args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, hc=A, cu=None, do=A, dhT=None, dq=A, dk=A, dv=A,
                 dg=A, db=A, dA=None, ddt=None, dh0=None, ws=A, wsb=1 << 30, B=1, T=16, H=1, dk_=128, dv_=128,

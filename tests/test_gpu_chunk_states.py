@@ -4,15 +4,17 @@ chunk-parallel output pass), through the C ABI:
   chunk boundaries (dense, packed variable-length, fp32 and bf16, with and
   without h0, and the full prefill workload on sampled heads);
 - the outputs and final states are bitwise those of kda_chunk_fwd;
-- the chunk-parallel pass (every chunk its own chain, started from its stored
-  state) reproduces the outputs bitwise."""
+- the chunk-parallel pass through kda_chunk_fwd (every chunk its own chain,
+  started from its stored state) reproduces the outputs bitwise;
+- the dedicated chunk-parallel kernel (kda_chunk_o, bf16 d = 128) matches the
+  oracle's outputs within the bf16 tolerance."""
 import numpy as np
 import pytest
 import torch
 
 import kimi_delta_attention_kda_amd as kda
 import synth
-from kda_testlib import assert_close, run_oracle, to_device
+from kda_testlib import assert_close, metrics, run_oracle, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +44,15 @@ def check_states(p, heads=None, what=""):
     o3 = kda.chunk_o_from_states(**dd, h_chunks=hc, scale=p.scale)
     kda.chunk_fwd_check()
     assert torch.equal(o1, o3), what + ": chunk-parallel pass differs"
+    if p.dtype == "bf16" and p.dk == 128 and p.dv == 128:
+        o4 = kda.chunk_o(**dd, h_chunks=hc, scale=p.scale)
+        torch.cuda.synchronize()
+        ro, _ = run_oracle(p, heads)
+        hs_ = slice(None) if heads is None else list(heads)
+        got4 = o4.float().cpu().numpy().reshape(p.tokens, p.H, p.dv)[:, hs_].astype(np.float64)
+        m4 = assert_close(got4, ro, p.dtype, what + " kda_chunk_o")
+        got1 = o1.float().cpu().numpy().reshape(p.tokens, p.H, p.dv)[:, hs_].astype(np.float64)
+        say("  kda_chunk_o", m4, " vs fused", metrics(got4, got1))
     hs = slice(None) if heads is None else list(heads)
     got = hc[:, hs].cpu().numpy().astype(np.float64)
     _, _, want = oracle_states(p, heads)
