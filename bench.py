@@ -105,6 +105,8 @@ KERNEL_SOURCES = {
                     "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
     "backward": ["kimi_delta_attention_kda_amd/csrc/kda_backward.hip",
                  "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
+    "chunk_o": ["kimi_delta_attention_kda_amd/csrc/kda_chunk_o.hip",
+                "kimi_delta_attention_kda_amd/csrc/kda_device.hpp"],
 }
 
 
@@ -126,7 +128,7 @@ COPY_CALIB_ELEMS = 64 << 20     # float32 elements read and written by the calib
 # chunk-parallel pass are other instantiations of the same template)
 KERNEL_MATCH = {"chunk_fwd": "kda::chunk_fwd_kernel<true, 128, 128, 32, false>", "decode": "kda::decode_kernel",
                 "extend": "kda::extend_kernel", "conv_decode": "kda::conv_decode_kernel",
-                "backward": "kda::bwd_kernel"}
+                "backward": "kda::bwd_kernel", "chunk_o": "kda::chunk_o_kernel"}
 
 
 def _counter_rows(d):
