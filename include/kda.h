@@ -202,7 +202,7 @@ int kda_chunk_o(const void *q, const void *k, const void *v,
  *   dA_log [H], ddt_bias [H, dk], dh0 [n_seq, H, dv, dk] float32.
  * workspace: device memory of at least kda_backward_workspace_bytes() bytes,
  * owned by the caller (about 6 KiB per (token, head) for partial column sums,
- * and a small area per block of 64 tokens); its contents on entry do not
+ * and a small area per block of 16 tokens); its contents on entry do not
  * matter.
  * Built for dk = dv = 128 with bfloat16 activations (those of the d = 128
  * forward; other shapes and float32 return KDA_ERR_UNSUPPORTED).  The result

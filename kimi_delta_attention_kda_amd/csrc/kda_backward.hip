@@ -57,7 +57,7 @@ __device__ __forceinline__ void st(void *p, size_t i, float x) {
 
 constexpr int NQ = 4;            // row quarters per chain (workgroups per chain)
 constexpr int QR = BV / NQ;      // rows per workgroup
-constexpr int TB = 64;           // tokens per block of the finishing kernel
+constexpr int TB = 16;           // tokens per block of the finishing kernel
 
 template <bool BF16>
 __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
@@ -265,6 +265,7 @@ __global__ __launch_bounds__(BK) void bwd_finish_kernel(BwdArgs a)
     const float dtb = a.dt_bias[(size_t)head * BK + col];
     float acc_dt = 0.f, acc_A = 0.f;
     const size_t tend = min((size_t)a.T_all, (size_t)(blk + 1) * TB);
+#pragma unroll 4
     for (size_t tok = (size_t)blk * TB; tok < tend; ++tok) {
         float sq = 0.f, sk = 0.f, sg = 0.f;
 #pragma unroll
@@ -307,14 +308,27 @@ __global__ __launch_bounds__(BK) void bwd_params_kernel(const float *__restrict_
                                                          float *__restrict__ ddt_bias, int n_blk, int H)
 {
     const int head = blockIdx.x, col = threadIdx.x;
-    float sdt = 0.f, sA = 0.f;
-    for (int s = 0; s < n_blk; ++s) {
-        const float *p = part + ((size_t)s * H + head) * (BK + 1);
-        sdt += p[col];
-        if (col == 0) sA += p[BK];
+    // eight independent partial sums keep eight loads in flight (fixed order: deterministic)
+    float sdt[8] = {}, sA[8] = {};
+    int s = 0;
+    for (; s + 8 <= n_blk; s += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float *p = part + ((size_t)(s + u) * H + head) * (BK + 1);
+            sdt[u] += p[col];
+            if (col == 0) sA[u] += p[BK];
+        }
     }
-    if (ddt_bias) ddt_bias[(size_t)head * BK + col] = sdt;
-    if (col == 0 && dA_log) dA_log[head] = sA;
+    for (int u = 0; s < n_blk; ++s, ++u) {
+        const float *p = part + ((size_t)s * H + head) * (BK + 1);
+        sdt[u] += p[col];
+        if (col == 0) sA[u] += p[BK];
+    }
+    float tdt = 0.f, tA = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { tdt += sdt[u]; tA += sA[u]; }
+    if (ddt_bias) ddt_bias[(size_t)head * BK + col] = tdt;
+    if (col == 0 && dA_log) dA_log[head] = tA;
 }
 
 size_t bwd_workspace_bytes(int n_seq, int H, long long tokens)

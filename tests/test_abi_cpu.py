@@ -196,8 +196,8 @@ def backward(lib, **kw):
 
 
 def test_backward_validation(lib):
-    # quarter column sums and beta terms per (token, head), block sums per 64 tokens
-    assert lib.kda_backward_workspace_bytes(2, 3, 128, 128, 100) == 4 * (4 * 100 * 3 * (3 * 128 + 1) + 2 * 3 * 129)
+    # quarter column sums and beta terms per (token, head), block sums per 16 tokens
+    assert lib.kda_backward_workspace_bytes(2, 3, 128, 128, 100) == 4 * (4 * 100 * 3 * (3 * 128 + 1) + 7 * 3 * 129)
     assert lib.kda_backward_workspace_bytes(2, 3, 64, 128, 100) == 0
     assert backward(lib, dtype=0) == -3               # float32 activations: no d = 128 forward to pair with
     assert backward(lib, dk_=64) == -3
