@@ -92,3 +92,27 @@ def test_decode_steps_match_prefill():
         outs.append(o[0])
     assert_close(np.stack(outs), o_pre, "bf16", "decode-vs-prefill o")
     assert_close(pool.cpu().numpy(), h_pre, "bf16", "decode-vs-prefill state")
+
+
+def test_decode_graph_replay():
+    """kda_decode_step recorded in a HIP graph (a serving decode loop): each of
+    several replays, with eager work and synchronisations between them, is
+    bitwise the same step run eagerly on a copy of the pool."""
+    d = synth.decode(63, B=32, H=4, HV=8, K=128, V=128, P=40, n_pad=2)
+    say("decode graph replay B32 H4 HV8")
+    ins = dict(qkv=bf16_dev(d.qkv), a=bf16_dev(d.a), b=bf16_dev(d.b), A_log=torch.from_numpy(d.A_log).cuda(),
+               dt_bias=torch.from_numpy(d.dt_bias).cuda(), state_idx=torch.from_numpy(d.state_idx).cuda())
+    pool_g = torch.from_numpy(d.pool).cuda()
+    pool_e = pool_g.clone()
+    o_g = torch.empty((d.B, d.HV, d.V), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kda.decode_step(**ins, state_pool=pool_g, num_heads=d.H, num_v_heads=d.HV, scale=d.scale, o=o_g)
+    for rep in range(3):
+        g.replay()
+        o_e = kda.decode_step(**ins, state_pool=pool_e, num_heads=d.H, num_v_heads=d.HV, scale=d.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g.view(torch.int16), o_e.view(torch.int16)), rep
+        assert torch.equal(pool_g, pool_e), rep
+        float(torch.arange(1000, device="cuda", dtype=torch.float32).sum())   # eager work between replays
