@@ -19,11 +19,9 @@
 
 namespace kda {
 
-// Producer workgroups per team for a d_v slab of bdv columns.  A 64-column
-// slab has four computing waves per consumer and a team of two consumers for
-// d_v = 128; six producers then keep up with it and a team still fills four
-// compute units in pairs.  Narrower slabs (more consumers) take four.
-constexpr int producer_wgs(int bdv) { return bdv >= 64 ? 6 : 4; }
+// Producer workgroups per team of the chunkwise prefill (each builds every
+// fourth chunk of the team's chains).
+constexpr int KDA_PRODUCER_WGS = 4;
 
 hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
                          const float *A_log, const float *dt_bias, float *pool,
