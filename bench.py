@@ -181,6 +181,43 @@ def traffic_summary(fetch_dir, write_dir):
         print(json.dumps({k: rec[k] for k in ("kernel", "bytes_per_launch", "fetch_bytes", "write_bytes")}))
 
 
+MFMA_COUNTERS = ("MfmaUtil", "MfmaFlopsBF16", "MfmaFlopsF32")
+
+
+def mfma_summary(pmc_dir):
+    """MFMA use of the prefill kernel from one rocprofv3 --pmc run with the
+    derived counters MfmaUtil (MFMA busy cycles over GPU-active cycles x SIMDs,
+    percent) and MfmaFlopsBF16 / MfmaFlopsF32 (MFMA math ops x 512 per
+    dispatch): the per-dispatch mean goes to profiles/chunk_fwd_mfma.json with
+    the hash of the kernel's sources."""
+    import numpy as np
+    rows = _counter_rows(pmc_dir)
+    rec = {"kernel": "chunk_fwd", "source_hash": source_hash(KERNEL_SOURCES["chunk_fwd"])}
+    for c in MFMA_COUNTERS:
+        vals = [v for k, n, v in rows if n == c and KERNEL_MATCH["chunk_fwd"] in k]
+        if not vals:
+            raise SystemExit(f"no {c} rows for the prefill kernel under {pmc_dir}")
+        rec[c] = {"mean_per_dispatch": float(np.mean(vals)), "dispatches": len(vals)}
+    rec["mfma_flops_per_launch"] = rec["MfmaFlopsBF16"]["mean_per_dispatch"] + rec["MfmaFlopsF32"]["mean_per_dispatch"]
+    rec["mfma_util_pct"] = rec["MfmaUtil"]["mean_per_dispatch"]
+    with open(os.path.join(PROFILES, "chunk_fwd_mfma.json"), "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps({k: rec[k] for k in ("kernel", "mfma_flops_per_launch", "mfma_util_pct")}))
+
+
+def measured_mfma():
+    """(MFMA flops per launch, MFMA busy percent) of the prefill kernel from the
+    committed counter summary, if taken on the current kernel source."""
+    path = os.path.join(PROFILES, "chunk_fwd_mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash(KERNEL_SOURCES["chunk_fwd"]):
+        return None
+    return t["mfma_flops_per_launch"], t["mfma_util_pct"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,13 +225,23 @@ def main():
     ap.add_argument("--warmup", type=int, default=25)
     ap.add_argument("--prefill-workload", type=int, default=1, choices=[1, 2, 3])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="for counter and trace runs: skip the pool-addressed prefill and the "
+                         "chunk-parallel pass through kda_chunk_fwd, which launch the prefill's "
+                         "kernel instantiation on other work and would mix into its per-kernel figures")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run one calibration copy kernel of known size (for --pmc runs)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/<kernel>_traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--mfma-summary", metavar="PMC_DIR",
+                    help="write profiles/chunk_fwd_mfma.json from a rocprofv3 --pmc run of "
+                         + " ".join(MFMA_COUNTERS) + " and exit")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the benchmark runs on one GPU only (the path shards by head/sequence with "
@@ -304,15 +351,17 @@ def main():
     def prefill_pool_call():
         kda.chunk_fwd_pool(**pin_pool, state_pool=ppool, state_idx=pidx, scale=p.scale, o=o)
 
-    for _ in range(2):
-        prefill_pool_call()
-    evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
-    for s_ in range(K):
-        evp[s_][0].record()
-        prefill_pool_call()
-        evp[s_][1].record()
-    torch.cuda.synchronize()
-    pool_avg = float(np.mean([evp[s_][0].elapsed_time(evp[s_][1]) for s_ in range(K)])) * 1e-3
+    pool_avg = None
+    if not args.profile:
+        for _ in range(2):
+            prefill_pool_call()
+        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+        for s_ in range(K):
+            evp[s_][0].record()
+            prefill_pool_call()
+            evp[s_][1].record()
+        torch.cuda.synchronize()
+        pool_avg = float(np.mean([evp[s_][0].elapsed_time(evp[s_][1]) for s_ in range(K)])) * 1e-3
 
     # the materialised form on the same prefill workload: pass 1 also stores the
     # fp32 state entering every chunk, pass 2 recomputes the outputs with every
@@ -331,7 +380,7 @@ def main():
         kda.chunk_o_from_states(**pin_noh0, h_chunks=hcb, scale=p.scale, o=o)
 
     mat_avg = []
-    for fn in (states_call, chunk_o_call, chunk_o_fwd_route_call):
+    for fn in (states_call, chunk_o_call) + (() if args.profile else (chunk_o_fwd_route_call,)):
         for _ in range(2):
             fn()
         evm = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
@@ -451,8 +500,11 @@ def main():
         cpu = {"value": th_cnt / tcpu / 1e6, "unit": "Mtok*head/s", "cores": threads,
                "kind": "oracle", "sample": f"{sample}, run {reps} times", "seconds": round(el, 3)}
 
-    traffic = measured_traffic("chunk_fwd")
+    # the committed counter summaries were taken on the default prefill workload
+    on_profiled = args.prefill_workload == 1
+    traffic = measured_traffic("chunk_fwd") if on_profiled else None
     traffic_d = measured_traffic("decode")
+    mfma = measured_mfma() if on_profiled else None
     line = {
         "metric": "KDA chunk-fwd Mtok*head/s (+ % of HBM/MFMA roofline); decode step us at B=256",
         "value": round(value, 2),
@@ -472,12 +524,17 @@ def main():
         "prefill_us": round(pre_avg * 1e6, 2),
         "prefill_tflops": round(flops / pre_avg / 1e12, 2),
         "prefill_mfma_frac": round(flops / pre_avg / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
-        "prefill_pool_us": round(pool_avg * 1e6, 2),
+        # counter evidence (rocprofv3 MfmaFlops*, MfmaUtil) when taken on the current source
+        "prefill_mfma_counters": (None if mfma is None else
+                                  {"mfma_flops_per_launch": mfma[0],
+                                   "mfma_tflops": round(mfma[0] / pre_avg / 1e12, 2),
+                                   "mfma_busy_pct": round(mfma[1], 2)}),
+        "prefill_pool_us": None if pool_avg is None else round(pool_avg * 1e6, 2),
         "states_us": round(mat_avg[0] * 1e6, 2),
         "states_gbs": round(states_gbs, 1),
         "chunk_o_us": round(mat_avg[1] * 1e6, 2),
         "chunk_o_gbs": round(chunk_o_gbs, 1),
-        "chunk_o_fwd_route_us": round(mat_avg[2] * 1e6, 2),
+        "chunk_o_fwd_route_us": round(mat_avg[2] * 1e6, 2) if len(mat_avg) > 2 else None,
         "backward_us": round(bwd_avg * 1e6, 2),
         "decode_us": round(dec_avg * 1e6, 2),
         "decode_graph_us": round(dec_graph_avg * 1e6, 2),
