@@ -14,13 +14,17 @@
 //   U = (I - L)^{-1} beta (v - k~ S0^T),   O = q~ S0^T + Mqk U.
 //
 // MI355X mapping: one 256-thread workgroup per (chunk, head), no cross-
-// workgroup synchronisation.  The two d_k x d_v products with the state
-// (k~ S0^T, q~ S0^T) run on bf16 16x16x32 MFMA: each wave takes 32 of the 128
-// output columns, and its B fragments are loaded straight from S0's rows
-// (d_k is contiguous in them), issued first so the 64 KiB per workgroup
-// stream in while the gate, L, Mqk and INV are built.  L and Mqk are formed
-// from the per-pair exponents G_i - G_j <= 0 (no factored e^{+-G}, so nothing
-// can overflow) and, with INV (forward substitution), U and O, stay in fp32.
+// workgroup synchronisation.  Thread t holds token t % 16 and channels
+// 8 (t / 16) .. + 7, so a 16-lane DPP row holds one channel group for all 16
+// tokens and the chunk-local gate cumsum is a row scan.  The two d_k x d_v
+// products with the state (k~ S0^T, q~ S0^T) run on bf16 16x16x32 MFMA: each
+// wave takes 32 of the 128 output columns, and its B fragments are loaded
+// straight from S0's rows (d_k is contiguous in them), issued right after the
+// inputs so the 64 KiB per workgroup stream in while the gate is built.  L and
+// Mqk are formed in fp32 from the per-pair exponents G_i - G_j <= 0 (no
+// factored e^{+-G}, so nothing can overflow), the 136 pairs spread evenly over
+// each 16-lane row; INV (Neumann products), U and O are 16x16 fp32 MFMA
+// products in registers.
 #include <stdint.h>
 
 #include "kda_device.hpp"
@@ -30,18 +34,49 @@ namespace kda {
 
 namespace {
 constexpr int C = 16, DK = 128, DV = 128;
+
+// DPP within a 16-lane row: row_shr n gives x of the lane n below (0 past the
+// row start), for the inclusive scan over the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
+                                                                 false));
 }
+__device__ __forceinline__ float row_scan(float x) {
+    x += dpp_row<0x111>(x);
+    x += dpp_row<0x112>(x);
+    x += dpp_row<0x114>(x);
+    x += dpp_row<0x118>(x);
+    return x;
+}
+
+// 16x16 products in C layout on the fp32 matrix core, with no data movement:
+// given XT = C layout of X^T (lane (lq, ln) element r = X[ln][4lq + r], which is
+// the A operand's element) and Y in C layout (the B operand's element), X Y in
+// C layout.
+__device__ __forceinline__ f32x4 prod16(f32x4 XT, f32x4 Y) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(XT[r], Y[r], acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4 plus_eye(f32x4 X, int ln, int lq) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) X[r] += (4 * lq + r == ln) ? 1.f : 0.f;
+    return X;
+}
+}  // namespace
 
 __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
 {
-    // channel-major (token index fastest), so that threads working on different
-    // token pairs read different banks: gate (log2 units), then its cumulative
-    // sum; scale q and k in fp32 (zero past the chunk's tokens)
-    __shared__ float GT[DK][C], qT[DK][C], kT[DK][C];
-    __shared__ float2 part[2][C * (C + 1) / 2];  // L and Mqk sums over the two channel halves
-    __shared__ __attribute__((aligned(16))) uint16_t kt[C][DK], qt[C][DK];   // k~, q~ as bf16
-    __shared__ float Lm[C][C], Mq[C][C], Inv[C][C];
-    __shared__ float vs[C][DV], us[C][DV];       // v, then u; U
+    // token rows padded by 16 bytes, so that 16-byte reads of the same columns
+    // of different rows fall in different banks
+    __shared__ __attribute__((aligned(16))) float Gr[C][DK + 4];           // cumulative gate (log2 units)
+    __shared__ __attribute__((aligned(16))) float kr[C][DK + 4], qr[C][DK + 4];      // k, q in fp32
+    __shared__ __attribute__((aligned(16))) uint16_t kt[C][DK + 8], qt[C][DK + 8];   // k~, q~ as bf16
+    __shared__ float2 part[4][C * (C + 1) / 2];  // per wave: (L, Mqk) sums over its 32 channels
+    __shared__ __attribute__((aligned(16))) float Lm[C][C + 4], Mq[C][C + 4];
+    __shared__ __attribute__((aligned(16))) float vs[C][DV + 4];
     __shared__ float bs[C];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -75,8 +110,23 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
     const size_t tok0 = bos + (size_t)c * C;
     const int nt = min(C, len - c * C);
 
-    // ---- S0 fragments first: wave w, column tile ct (n = 32w + 16ct + ln),
-    // K-step s: channels 32s + 8lq .. + 7 of S0's row n
+    // ---- inputs first: token t = lane % 16, channels 8 cg .. + 7 with cg = tid / 16
+    const int t = ln, c8 = 8 * (tid >> 4);
+    const bool live = t < nt;
+    uint4 qw = make_uint4(0, 0, 0, 0), kw = qw, aw = qw, vw = qw;
+    if (live) {
+        const size_t i0 = ((tok0 + t) * H + head) * DK + c8;
+        qw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + i0);
+        kw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + i0);
+        aw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.g_raw) + i0);
+        vw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + i0);
+    }
+    uint16_t braw = 0;
+    if (tid < nt) braw = static_cast<const uint16_t *>(a.beta_raw)[(tok0 + tid) * H + head];
+
+    // ---- then the S0 fragments (younger, so waiting for the inputs never waits
+    // for them): wave w, column tile ct (n = 32w + 16ct + ln), K-step s:
+    // channels 32s + 8lq .. + 7 of S0's row n
     const float *S0 = a.h_chunks + (crow * H + head) * (size_t)DV * DK;
     f32x4 sf[2][4][2];
 #pragma unroll
@@ -88,104 +138,51 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
             sf[ct][s][1] = *reinterpret_cast<const f32x4 *>(p + 4);
         }
 
-    // ---- inputs: thread t takes token t / 16, channels 8 (t % 16) .. + 7
+    // ---- gate (log2 units) and its chunk-local cumulative sum (row scan over
+    // the tokens); k~, q~ as bf16 rows; padding tokens have zero q, k and gate
     const float A = expf(a.A_log[head]);
     {
-        const int t = tid >> 4, c8 = 8 * (tid & 15);
-        const bool live = t < nt;
-        const size_t i0 = ((tok0 + (live ? t : 0)) * H + head) * DK + c8;
-        uint4 qw = make_uint4(0, 0, 0, 0), kw = qw, aw = qw, vw = qw;
-        if (live) {
-            qw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + i0);
-            kw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + i0);
-            aw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.g_raw) + i0);
-            vw = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) + i0);
-        }
         const uint32_t qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w},
                        aa[4] = {aw.x, aw.y, aw.z, aw.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
+        float G[8];
+        f32x4 v4[2], k4[2], q4[2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int sh = 16 * (e & 1);
-            // g in log2 units: -A log2(1 + 2^{z log2 e}) (softplus = z above z = 20)
+            // -A log2(1 + 2^{z log2 e}) (softplus = z above z = 20)
             const float y = (bf16_to_f32((uint16_t)(aa[e >> 1] >> sh)) + a.dt_bias[(size_t)head * DK + c8 + e]) * kLog2e;
             const float sp2 = y > 20.f * kLog2e ? y : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(y));
-            GT[c8 + e][t] = live ? -A * sp2 : 0.f;
-            qT[c8 + e][t] = a.scale * bf16_to_f32((uint16_t)(qa[e >> 1] >> sh));
-            kT[c8 + e][t] = bf16_to_f32((uint16_t)(ka[e >> 1] >> sh));
-            vs[t][c8 + e] = bf16_to_f32((uint16_t)(va[e >> 1] >> sh));
+            G[e] = row_scan(live ? -A * sp2 : 0.f);
+            v4[e >> 2][e & 3] = bf16_to_f32((uint16_t)(va[e >> 1] >> sh));
+            k4[e >> 2][e & 3] = bf16_to_f32((uint16_t)(ka[e >> 1] >> sh));
+            q4[e >> 2][e & 3] = bf16_to_f32((uint16_t)(qa[e >> 1] >> sh));
         }
-        if (tid < C) {
-            const float b = tid < nt ? bf16_to_f32(static_cast<const uint16_t *>(a.beta_raw)[(tok0 + tid) * H + head]) : 0.f;
-            bs[tid] = tid < nt ? sigmoid_f(b) : 0.f;
+        uint32_t kto[4], qto[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const float g0 = __builtin_amdgcn_exp2f(G[e]), g1 = __builtin_amdgcn_exp2f(G[e + 1]);
+            const int sh0 = 0, sh1 = 16;
+            kto[e >> 1] = pack_bf16x2(bf16_to_f32((uint16_t)(ka[e >> 1] >> sh0)) * g0,
+                                      bf16_to_f32((uint16_t)(ka[e >> 1] >> sh1)) * g1);
+            qto[e >> 1] = pack_bf16x2(a.scale * bf16_to_f32((uint16_t)(qa[e >> 1] >> sh0)) * g0,
+                                      a.scale * bf16_to_f32((uint16_t)(qa[e >> 1] >> sh1)) * g1);
         }
+        *reinterpret_cast<uint4 *>(&kt[t][c8]) = uint4{kto[0], kto[1], kto[2], kto[3]};
+        *reinterpret_cast<uint4 *>(&qt[t][c8]) = uint4{qto[0], qto[1], qto[2], qto[3]};
+        *reinterpret_cast<f32x4 *>(&kr[t][c8]) = k4[0];
+        *reinterpret_cast<f32x4 *>(&kr[t][c8 + 4]) = k4[1];
+        *reinterpret_cast<f32x4 *>(&qr[t][c8]) = q4[0];
+        *reinterpret_cast<f32x4 *>(&qr[t][c8 + 4]) = q4[1];
+        *reinterpret_cast<f32x4 *>(&Gr[t][c8]) = f32x4{G[0], G[1], G[2], G[3]};
+        *reinterpret_cast<f32x4 *>(&Gr[t][c8 + 4]) = f32x4{G[4], G[5], G[6], G[7]};
+        *reinterpret_cast<f32x4 *>(&vs[t][c8]) = v4[0];
+        *reinterpret_cast<f32x4 *>(&vs[t][c8 + 4]) = v4[1];
+        if (tid < C) bs[tid] = tid < nt ? sigmoid_f(bf16_to_f32(braw)) : 0.f;
     }
     __syncthreads();
-    // chunk-local cumulative gate, per channel
-    if (tid < DK) {
-        float run = 0.f;
-#pragma unroll
-        for (int t = 0; t < C; ++t) {
-            run += GT[tid][t];
-            GT[tid][t] = run;
-        }
-    }
-    __syncthreads();
-    // k~, q~ (bf16 MFMA operands); L and Mqk from per-pair exponents
-    {
-        const int t = tid >> 4, c8 = 8 * (tid & 15);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float eg = __builtin_amdgcn_exp2f(GT[c8 + e][t]);
-            kt[t][c8 + e] = f32_to_bf16(kT[c8 + e][t] * eg);
-            qt[t][c8 + e] = f32_to_bf16(qT[c8 + e][t] * eg);
-        }
-    }
-    // L and Mqk: pair p = (i, j), i >= j, over channel half hf (tasks p + 136 hf)
-    constexpr int NPAIR = C * (C + 1) / 2;
-    for (int task = tid; task < 2 * NPAIR; task += 256) {
-        const int hf = task >= NPAIR ? 1 : 0, p = task - hf * NPAIR;
-        int i = 0;
-        while ((i + 1) * (i + 2) / 2 <= p) ++i;
-        const int j = p - i * (i + 1) / 2;
-        float sl = 0.f, sm = 0.f;
-#pragma unroll 8
-        for (int cc = 64 * hf; cc < 64 * hf + 64; ++cc) {
-            const float e = __builtin_amdgcn_exp2f(GT[cc][i] - GT[cc][j]);   // exponent <= 0
-            const float kj = kT[cc][j] * e;
-            sl += kT[cc][i] * kj;
-            sm += qT[cc][i] * kj;
-        }
-        part[hf][p] = make_float2(sl, sm);
-    }
-    __syncthreads();
-    if (tid < NPAIR) {
-        int i = 0;
-        while ((i + 1) * (i + 2) / 2 <= tid) ++i;
-        const int j = tid - i * (i + 1) / 2;
-        const float sl = part[0][tid].x + part[1][tid].x, sm = part[0][tid].y + part[1][tid].y;
-        Lm[i][j] = i > j ? -bs[i] * sl : 0.f;
-        Mq[i][j] = sm;
-        if (i != j) {
-            Lm[j][i] = 0.f;
-            Mq[j][i] = 0.f;
-        }
-    }
-    __syncthreads();
-    // INV = (I - L)^{-1} by forward substitution, one column per thread
-    if (tid < C) {
-        const int j = tid;
-        float x[C];
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            float s = i == j ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < C; ++m)
-                if (m < i) s += Lm[i][m] * x[m];
-            x[i] = i < j ? 0.f : s;
-            Inv[i][j] = x[i];
-        }
-    }
-    // W = k~ S0^T and Qs = q~ S0^T on MFMA (A fragments: row ln = token, channels 32s + 8lq ..)
+
+    // ---- W = k~ S0^T and Qs = q~ S0^T on MFMA (A fragments: row ln = token,
+    // channels 32s + 8lq ..), column tile ct of the wave
     f32x4 W[2], Qs[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
@@ -208,56 +205,87 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
             Qs[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, b, Qs[ct], 0, 0, 0);
         }
     }
-    // u = beta (v - W): C layout, rows 4lq + r, column n
+
+    // ---- L and Mqk from per-pair exponents G_i - G_j <= 0 over this lane's 8
+    // channels: pair p = (i, j), i >= j, p = i (i + 1) / 2 + j, for p = ln,
+    // ln + 16, ... (8 or 9 pairs per lane); the wave's four channel groups are
+    // added across the lanes 16 and 32 apart, the waves through LDS.
+    constexpr int NPAIR = C * (C + 1) / 2;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const int n = 32 * w + 16 * ct + ln;
+    for (int k = 0; k < (NPAIR + 15) / 16; ++k) {
+        const int p = ln + 16 * k;
+        float l = 0.f, m = 0.f;
+        if (p < NPAIR) {
+            int i = (int)((__builtin_sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);   // exact for p < 136
+            i += (i + 1) * (i + 2) / 2 <= p ? 1 : 0;
+            i -= i * (i + 1) / 2 > p ? 1 : 0;
+            const int j = p - i * (i + 1) / 2;
+            const f32x4 gi0 = *reinterpret_cast<const f32x4 *>(&Gr[i][c8]), gi1 = *reinterpret_cast<const f32x4 *>(&Gr[i][c8 + 4]);
+            const f32x4 gj0 = *reinterpret_cast<const f32x4 *>(&Gr[j][c8]), gj1 = *reinterpret_cast<const f32x4 *>(&Gr[j][c8 + 4]);
+            const f32x4 ki[2] = {*reinterpret_cast<const f32x4 *>(&kr[i][c8]), *reinterpret_cast<const f32x4 *>(&kr[i][c8 + 4])};
+            const f32x4 kj[2] = {*reinterpret_cast<const f32x4 *>(&kr[j][c8]), *reinterpret_cast<const f32x4 *>(&kr[j][c8 + 4])};
+            const f32x4 qi[2] = {*reinterpret_cast<const f32x4 *>(&qr[i][c8]), *reinterpret_cast<const f32x4 *>(&qr[i][c8 + 4])};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 4 * lq + r;
-            us[i][n] = bs[i] * (vs[i][n] - W[ct][r]);
+            for (int e = 0; e < 8; ++e) {
+                const float gi = e < 4 ? gi0[e] : gi1[e - 4], gj = e < 4 ? gj0[e] : gj1[e - 4];
+                const float kx = kj[e >> 2][e & 3] * __builtin_amdgcn_exp2f(gi - gj);
+                l = __builtin_fmaf(ki[e >> 2][e & 3], kx, l);
+                m = __builtin_fmaf(qi[e >> 2][e & 3], kx, m);
+            }
         }
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        m += __shfl_xor(m, 16);
+        m += __shfl_xor(m, 32);
+        if (lane < 16 && p < NPAIR) part[w][p] = make_float2(l, m);
     }
     __syncthreads();
-    // U = INV u (fp32), into vs
-    f32x4 U[2];
+    {
+        const int i = tid >> 4, jj = tid & 15;
+        float sl = 0.f, sm = 0.f;
+        if (jj <= i) {
+            const int p = i * (i + 1) / 2 + jj;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const int n = 32 * w + 16 * ct + ln;
-        float ucol[C];
-#pragma unroll
-        for (int m = 0; m < C; ++m) ucol[m] = us[m][n];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 4 * lq + r;
-            float s = 0.f;
-#pragma unroll
-            for (int m = 0; m < C; ++m) s += Inv[i][m] * ucol[m];
-            U[ct][r] = s;
+            for (int ww = 0; ww < 4; ++ww) {
+                sl += part[ww][p].x;
+                sm += part[ww][p].y;
+            }
         }
-    }
-    __syncthreads();   // all of u read before U overwrites the v buffer
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-        const int n = 32 * w + 16 * ct + ln;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vs[4 * lq + r][n] = U[ct][r];
+        Lm[i][jj] = i > jj ? -bs[i] * sl : 0.f;
+        Mq[i][jj] = i >= jj ? a.scale * sm : 0.f;
     }
     __syncthreads();
-    // O = Qs + Mqk U, stored for the chunk's tokens
+
+    // ---- INV = (I - L)^{-1} = (I + L)(I + L^2)(I + L^4)(I + L^8) on the fp32
+    // matrix core, in C layout (each wave on its own), then per column tile
+    // U = INV beta (v - W) and O = Qs + Mqk U
+    f32x4 L, LT, MT;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L[r] = Lm[4 * lq + r][ln];              // L[4lq + r][ln]
+    LT = *reinterpret_cast<const f32x4 *>(&Lm[ln][4 * lq]);              // L[ln][4lq + r]
+    MT = *reinterpret_cast<const f32x4 *>(&Mq[ln][4 * lq]);              // Mqk[ln][4lq + r]
+    const f32x4 L2 = prod16(LT, L), L2T = prod16(L, LT);
+    const f32x4 L4 = prod16(L2T, L2), L4T = prod16(L2, L2T);
+    const f32x4 L8 = prod16(L4T, L4);
+    // A^T = ((I + L)(I + L^2))^T,  B = (I + L^4)(I + L^8),  INV^T = B^T A^T
+    const f32x4 AT = prod16(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
+    const f32x4 Bm = prod16(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
+    const f32x4 IT = prod16(Bm, AT);
+    f32x4 bet;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bet[r] = bs[4 * lq + r];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
         const int n = 32 * w + 16 * ct + ln;
-        float Ucol[C];
+        f32x4 u;
 #pragma unroll
-        for (int m = 0; m < C; ++m) Ucol[m] = vs[m][n];
+        for (int r = 0; r < 4; ++r) u[r] = bet[r] * (vs[4 * lq + r][n] - W[ct][r]);
+        const f32x4 U = prod16(IT, u);
+        const f32x4 O = Qs[ct] + prod16(MT, U);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 4 * lq + r;
-            float s = Qs[ct][r];
-#pragma unroll
-            for (int m = 0; m < C; ++m) s += Mq[i][m] * Ucol[m];
-            if (i < nt) static_cast<uint16_t *>(a.o)[((tok0 + i) * H + head) * DV + n] = f32_to_bf16(s);
+            if (i < nt) static_cast<uint16_t *>(a.o)[((tok0 + i) * H + head) * DV + n] = f32_to_bf16(O[r]);
         }
     }
 }
