@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
 {
     // token rows padded by 16 bytes, so that 16-byte reads of the same columns
     // of different rows fall in different banks
-    __shared__ __attribute__((aligned(16))) float Gr[C][DK + 4];           // cumulative gate (log2 units)
+    __shared__ __attribute__((aligned(16))) float Dr[C][DK + 4];           // per-token decay e^{g}
     __shared__ __attribute__((aligned(16))) float kr[C][DK + 4], qr[C][DK + 4];      // k, q in fp32
     __shared__ __attribute__((aligned(16))) uint16_t kt[C][DK + 8], qt[C][DK + 8];   // k~, q~ as bf16
     __shared__ float2 part[4][C * (C + 1) / 2];  // per wave: (L, Mqk) sums over its 32 channels
@@ -145,14 +145,16 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
         const uint32_t qa[4] = {qw.x, qw.y, qw.z, qw.w}, ka[4] = {kw.x, kw.y, kw.z, kw.w},
                        aa[4] = {aw.x, aw.y, aw.z, aw.w}, va[4] = {vw.x, vw.y, vw.z, vw.w};
         float G[8];
-        f32x4 v4[2], k4[2], q4[2];
+        f32x4 v4[2], k4[2], q4[2], d4[2];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int sh = 16 * (e & 1);
             // -A log2(1 + 2^{z log2 e}) (softplus = z above z = 20)
             const float y = (bf16_to_f32((uint16_t)(aa[e >> 1] >> sh)) + a.dt_bias[(size_t)head * DK + c8 + e]) * kLog2e;
             const float sp2 = y > 20.f * kLog2e ? y : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(y));
-            G[e] = row_scan(live ? -A * sp2 : 0.f);
+            const float g = live ? -A * sp2 : 0.f;
+            d4[e >> 2][e & 3] = __builtin_amdgcn_exp2f(g);
+            G[e] = row_scan(g);
             v4[e >> 2][e & 3] = bf16_to_f32((uint16_t)(va[e >> 1] >> sh));
             k4[e >> 2][e & 3] = bf16_to_f32((uint16_t)(ka[e >> 1] >> sh));
             q4[e >> 2][e & 3] = bf16_to_f32((uint16_t)(qa[e >> 1] >> sh));
@@ -173,8 +175,8 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
         *reinterpret_cast<f32x4 *>(&kr[t][c8 + 4]) = k4[1];
         *reinterpret_cast<f32x4 *>(&qr[t][c8]) = q4[0];
         *reinterpret_cast<f32x4 *>(&qr[t][c8 + 4]) = q4[1];
-        *reinterpret_cast<f32x4 *>(&Gr[t][c8]) = f32x4{G[0], G[1], G[2], G[3]};
-        *reinterpret_cast<f32x4 *>(&Gr[t][c8 + 4]) = f32x4{G[4], G[5], G[6], G[7]};
+        *reinterpret_cast<f32x4 *>(&Dr[t][c8]) = d4[0];
+        *reinterpret_cast<f32x4 *>(&Dr[t][c8 + 4]) = d4[1];
         *reinterpret_cast<f32x4 *>(&vs[t][c8]) = v4[0];
         *reinterpret_cast<f32x4 *>(&vs[t][c8 + 4]) = v4[1];
         if (tid < C) bs[tid] = tid < nt ? sigmoid_f(bf16_to_f32(braw)) : 0.f;
@@ -206,38 +208,56 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
         }
     }
 
-    // ---- L and Mqk from per-pair exponents G_i - G_j <= 0 over this lane's 8
-    // channels: pair p = (i, j), i >= j, p = i (i + 1) / 2 + j, for p = ln,
-    // ln + 16, ... (8 or 9 pairs per lane); the wave's four channel groups are
-    // added across the lanes 16 and 32 apart, the waves through LDS.
-    constexpr int NPAIR = C * (C + 1) / 2;
+    // ---- L and Mqk.  For a column j the factor e^{G_i - G_j} of rows i = j, j+1,
+    // ... is the running product of the tokens' decays e^{g_i} (all <= 1, so
+    // nothing can overflow, and no exponential per pair).  Lane t of a 16-lane
+    // row takes the columns j1 = min(t, 15 - t) and j2 = 15 - j1 (17 pairs in
+    // all) over 4 of the row's 8 channels (the lower half for t < 8); lanes t
+    // and 15 - t hold the two halves of the same pairs.  Step s covers row
+    // j1 + s of column j1 for s < 16 - j1, then row j2 + s - (16 - j1) of j2.
+    {
+        const int j1 = min(t, 15 - t), j2 = 15 - j1, n1 = 16 - j1;
+        const int cc = c8 + (t < 8 ? 0 : 4);
+        const f32x4 kj1 = *reinterpret_cast<const f32x4 *>(&kr[j1][cc]);
+        const f32x4 kj2 = *reinterpret_cast<const f32x4 *>(&kr[j2][cc]);
+        f32x4 r = {1.f, 1.f, 1.f, 1.f};
+        float pl[C + 1], pm[C + 1];
 #pragma unroll
-    for (int k = 0; k < (NPAIR + 15) / 16; ++k) {
-        const int p = ln + 16 * k;
-        float l = 0.f, m = 0.f;
-        if (p < NPAIR) {
-            int i = (int)((__builtin_sqrtf(8.f * p + 1.f) - 1.f) * 0.5f);   // exact for p < 136
-            i += (i + 1) * (i + 2) / 2 <= p ? 1 : 0;
-            i -= i * (i + 1) / 2 > p ? 1 : 0;
-            const int j = p - i * (i + 1) / 2;
-            const f32x4 gi0 = *reinterpret_cast<const f32x4 *>(&Gr[i][c8]), gi1 = *reinterpret_cast<const f32x4 *>(&Gr[i][c8 + 4]);
-            const f32x4 gj0 = *reinterpret_cast<const f32x4 *>(&Gr[j][c8]), gj1 = *reinterpret_cast<const f32x4 *>(&Gr[j][c8 + 4]);
-            const f32x4 ki[2] = {*reinterpret_cast<const f32x4 *>(&kr[i][c8]), *reinterpret_cast<const f32x4 *>(&kr[i][c8 + 4])};
-            const f32x4 kj[2] = {*reinterpret_cast<const f32x4 *>(&kr[j][c8]), *reinterpret_cast<const f32x4 *>(&kr[j][c8 + 4])};
-            const f32x4 qi[2] = {*reinterpret_cast<const f32x4 *>(&qr[i][c8]), *reinterpret_cast<const f32x4 *>(&qr[i][c8 + 4])};
+        for (int st = 0; st < C + 1; ++st) {
+            const bool first = st < n1;
+            const int i = first ? j1 + st : j2 + (st - n1);
+            const bool diag = st == 0 || st == n1;
+            const f32x4 di = *reinterpret_cast<const f32x4 *>(&Dr[i][cc]);
+            const f32x4 ki = *reinterpret_cast<const f32x4 *>(&kr[i][cc]);
+            const f32x4 qi = *reinterpret_cast<const f32x4 *>(&qr[i][cc]);
+            const f32x4 kj = first ? kj1 : kj2;
+            float l = 0.f, m = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float gi = e < 4 ? gi0[e] : gi1[e - 4], gj = e < 4 ? gj0[e] : gj1[e - 4];
-                const float kx = kj[e >> 2][e & 3] * __builtin_amdgcn_exp2f(gi - gj);
-                l = __builtin_fmaf(ki[e >> 2][e & 3], kx, l);
-                m = __builtin_fmaf(qi[e >> 2][e & 3], kx, m);
+            for (int e = 0; e < 4; ++e) {
+                r[e] = diag ? 1.f : r[e] * di[e];
+                const float kx = kj[e] * r[e];
+                l = __builtin_fmaf(ki[e], kx, l);
+                m = __builtin_fmaf(qi[e], kx, m);
+            }
+            // the row's other channel half (lane 15 - t), then the wave's other rows
+            l += dpp_row<0x140>(l);   // row_mirror
+            m += dpp_row<0x140>(m);
+            pl[st] = l;
+            pm[st] = m;
+        }
+#pragma unroll
+        for (int st = 0; st < C + 1; ++st) {
+            float l = pl[st], m = pm[st];
+            l += __shfl_xor(l, 16);
+            l += __shfl_xor(l, 32);
+            m += __shfl_xor(m, 16);
+            m += __shfl_xor(m, 32);
+            if (lane < 8) {
+                const bool first = st < n1;
+                const int i = first ? j1 + st : j2 + (st - n1), j = first ? j1 : j2;
+                part[w][i * (i + 1) / 2 + j] = make_float2(l, m);
             }
         }
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        m += __shfl_xor(m, 16);
-        m += __shfl_xor(m, 32);
-        if (lane < 16 && p < NPAIR) part[w][p] = make_float2(l, m);
     }
     __syncthreads();
     {
