@@ -21,10 +21,10 @@
 // wave takes 32 of the 128 output columns, and its B fragments are loaded
 // straight from S0's rows (d_k is contiguous in them), issued right after the
 // inputs so the 64 KiB per workgroup stream in while the gate is built.  L and
-// Mqk are formed in fp32 from the per-pair exponents G_i - G_j <= 0 (no
-// factored e^{+-G}, so nothing can overflow), the 136 pairs spread evenly over
-// each 16-lane row; INV (Neumann products), U and O are 16x16 fp32 MFMA
-// products in registers.
+// Mqk are formed in fp32 with e^{G_i - G_j} (i >= j) as running products of the
+// tokens' decays (all <= 1: no factored e^{+-G}, so nothing can overflow), the
+// 136 pairs spread evenly over each 16-lane row; INV (Neumann products), U and
+// O are 16x16 fp32 MFMA products in registers.
 #include <stdint.h>
 
 #include "kda_device.hpp"
