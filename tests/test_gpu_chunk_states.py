@@ -66,6 +66,8 @@ SMALL = [
     dict(B=3, T=33, H=2, dk=64, dv=64, dtype="f32", with_h0=True),
     dict(B=1, T=0, H=2, dk=128, dv=128, dtype="bf16", lengths=[1, 16, 17, 0, 45, 130], with_h0=True),
     dict(B=2, T=48, H=2, dk=64, dv=128, dtype="bf16", gate_stress=0.05),
+    # strong decays at d = 128: the chunk-parallel kernel's running decay products underflow
+    dict(B=2, T=70, H=2, dk=128, dv=128, dtype="bf16", gate_stress=0.05, with_h0=True),
 ]
 
 
