@@ -159,11 +159,13 @@ int kda_chunk_fwd_states(const void *q, const void *k, const void *v,
  * state entering it, each chunk independently.  Per chunk of 16 tokens with
  * S0 = h_chunks[row] (G the chunk-local cumulative gate):
  *   U = (I - L)^{-1} beta (v - (k e^G) S0^T),  o = scale ((q e^G) S0^T + Mqk U),
- * L and Mqk as in kda_chunk_fwd (formed from per-pair exponents, fp32).
+ * L and Mqk as in kda_chunk_fwd (in fp32, their factors e^{G_i - G_j} as
+ * running products of the tokens' decays).
  * Inputs as given to kda_chunk_fwd_states (q, k, v, g_raw, beta_raw, A_log,
  * dt_bias, cu_seqlens, B, T, H, n_seq, scale) and its h_chunks output;
  * n_chunks = its row count (sum of ceil(len / 16); B * ceil(T / 16) for
- * dense input, checked).  Writes o [T_all, H, dv].  Built for bfloat16 with
+ * dense input, checked; with cu_seqlens the device-side lengths decide, and
+ * rows past them are skipped).  Writes o [T_all, H, dv].  Built for bfloat16 with
  * dk = dv = 128 (else KDA_ERR_UNSUPPORTED; kda_chunk_fwd over chunk-length
  * sequences with h0 = h_chunks is the general route and reproduces
  * kda_chunk_fwd bitwise; this pass agrees with it to bf16 rounding).

@@ -152,7 +152,7 @@ int kda_chunk_o(const void *q, const void *k, const void *v, const void *g_raw, 
     kda::ChunkOArgs a;
     a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
     a.A_log = A_log; a.dt_bias = dt_bias; a.h_chunks = h_chunks; a.cu_seqlens = cu_seqlens;
-    a.o = o; a.T = T; a.H = H; a.scale = scale;
+    a.o = o; a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
     const hipError_t e = kda::launch_chunk_o(a, n_chunks, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -90,13 +90,13 @@ __global__ __launch_bounds__(256) void chunk_o_kernel(ChunkOArgs a)
     int len;
     if (a.cu_seqlens) {
         size_t acc = 0;
-        seq = 0;
-        for (;; ++seq) {
+        for (seq = 0; seq < a.n_seq; ++seq) {
             const int l = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
             const size_t nchs = (size_t)((l + C - 1) / C);
             if (crow < acc + nchs) break;
             acc += nchs;
         }
+        if (seq == a.n_seq) return;              // a row past the sequences' chunks: nothing to do
         c = (int)(crow - acc);
         bos = (size_t)a.cu_seqlens[seq];
         len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];

@@ -63,6 +63,7 @@ struct ChunkOArgs {
     const int32_t *cu_seqlens;
     void *o;
     int T, H;           // T: per-sequence length for dense input, total tokens if cu_seqlens
+    int n_seq;          // sequences (bounds the search of a chunk row in cu_seqlens)
     float scale;
 };
 hipError_t launch_chunk_o(const ChunkOArgs &a, long long n_chunks, hipStream_t stream);

@@ -81,3 +81,29 @@ def test_states_small(i):
 
 def test_states_workload1_sampled():
     check_states(synth.prefill_workload(1), heads=[0, 9], what="states prefill-bf16 B4 H16 T4096")
+
+
+def test_chunk_o_extra_rows_skipped():
+    """kda_chunk_o with packed sequences reads the lengths on the device: a
+    row count above theirs (from a C caller) leaves the extra workgroups idle
+    and the outputs unchanged."""
+    import ctypes
+    p = synth.prefill(320, B=1, T=0, H=2, dk=128, dv=128, dtype="bf16", lengths=[5, 33, 16, 0, 21])
+    d = to_device(p)
+    say("chunk_o extra rows", "tokens", p.tokens)
+    _, _, hc = kda.chunk_fwd_states(**d, scale=p.scale)
+    dd = {k_: v_ for k_, v_ in d.items() if k_ != "h0"}
+    o_ref = kda.chunk_o(**dd, h_chunks=hc, scale=p.scale)
+    torch.cuda.synchronize()
+    o2 = torch.zeros_like(o_ref)
+    B, T, H, dk = d["q"].shape
+    nc = hc.shape[0]
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = kda.load_library().kda_chunk_o(
+        ptr(d["q"]), ptr(d["k"]), ptr(d["v"]), ptr(d["g_raw"]), ptr(d["beta_raw"]), ptr(d["A_log"]),
+        ptr(d["dt_bias"]), ptr(hc), ptr(d["cu_seqlens"]), ptr(o2), B, T, H, dk, 128,
+        d["cu_seqlens"].numel() - 1, nc + 7, ctypes.c_float(p.scale), 1,
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(o2, o_ref)
