@@ -129,3 +129,35 @@ def test_zero_length_sequence_keeps_h0():
     say("zero-length sequence")
     o, hT = run_gpu(p)
     assert np.array_equal(hT[0], p.h0[0].astype(np.float64))
+
+
+def test_prefill_graph_replay():
+    """kda_chunk_fwd recorded in a HIP graph (its flag clear is a fill kernel,
+    not a memset): every replay, with eager prefills in between, equals the
+    eager result bitwise."""
+    p = synth.prefill(78, B=2, T=300, H=4, dk=128, dv=128, dtype="bf16", with_h0=True)
+    d = to_device(p)
+    print("[case] prefill graph replay B2 T300 H4", flush=True)
+    o_ref, h_ref = kda.chunk_fwd(**d, scale=p.scale)     # also sets up the library's workspace
+    kda.chunk_fwd_check()
+    o, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        kda.chunk_fwd(**d, scale=p.scale, o=o, h_T=hT)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kda.chunk_fwd(**d, scale=p.scale, o=o, h_T=hT)
+    for _ in range(4):
+        o.zero_()
+        hT.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        kda.chunk_fwd_check()
+        assert torch.equal(o, o_ref) and torch.equal(hT, h_ref)
+        o2, h2 = kda.chunk_fwd(**d, scale=p.scale)       # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o2, o_ref) and torch.equal(h2, h_ref)
+    del g
