@@ -65,6 +65,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
     __shared__ f32x4 Lq[BCH][BK / 4], Lk[BCH][BK / 4], Le[BCH][BK / 4];
     __shared__ float Lv[BCH][QR], Ldo[BCH][QR], Lu[BCH][QR], Lvw[BCH][QR];
     __shared__ float Lbeta[BCH];
+    __shared__ float Ldtb[BK];                  // dt_bias of the head
     // column partials of dqb, dk, dg and the beta terms per row, double-buffered
     // over tokens so one barrier per token suffices: token t's partials are
     // summed while token t-1's are written to the other buffer, and the barrier
@@ -106,44 +107,67 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
         }
     }
 
+    // A chunk's inputs as this thread loads them (token tid / 32, channels
+    // 4 (tid % 32) .. + 3 of q, k and g_raw; this quarter's v and do of row
+    // tid % 32; beta of token tid if tid < 16) and its entering state (this
+    // thread's elements).  The next chunk's are loaded halfway through this
+    // chunk's adjoint, when half the history registers are free, so no chunk
+    // waits for memory.  Tokens past the sequence repeat its last token (in
+    // bounds; never used).
+    struct Raw {
+        float q[4], k[4], g[4], v, dO, b;
+        f32x4 S[2];
+    } raw;
+    const int st_t = tid >> 5, st_c4 = 4 * (tid & 31), st_r = tid & 31;
+    auto load_raw = [&](int c) {
+        const int nt = min(BCH, len - c * BCH);
+        const size_t tok = bos + (size_t)c * BCH + min(st_t, nt - 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const size_t i = (tok * H + head) * BK + st_c4 + e;
+            raw.q[e] = ld<BF16>(a.q, i);
+            raw.k[e] = ld<BF16>(a.k, i);
+            raw.g[e] = ld<BF16>(a.g_raw, i);
+        }
+        const size_t iv = (tok * H + head) * BV + quarter * QR + st_r;
+        raw.v = ld<BF16>(a.v, iv);
+        raw.dO = ld<BF16>(a.do_, iv);
+        raw.b = tid < nt ? ld<BF16>(a.beta_raw, (bos + (size_t)c * BCH + tid) * H + head) : 0.f;
+        const float *hc = a.h_chunks + (((cbase + c) * H + head) * BV + row) * (size_t)BK;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) raw.S[h2] = *reinterpret_cast<const f32x4 *>(hc + 4 * j + 64 * h2);
+    };
+    if (nch > 0) load_raw(nch - 1);
+    if (tid < BK) Ldtb[tid] = a.dt_bias[(size_t)head * BK + tid];
+    __syncthreads();
+
     for (int c = nch - 1; c >= 0; --c) {
         const int t0 = c * BCH;
         const int nt = min(BCH, len - t0);
         // ---- stage the chunk's per-token values
         {
-            const int tt = tid >> 5, c4 = 4 * (tid & 31);
+            const int tt = st_t;
             if (tt < nt) {
-                const size_t tok = bos + t0 + tt;
                 f32x4 qv, kv, ev;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const size_t i = (tok * H + head) * BK + c4 + e;
-                    const float z = ld<BF16>(a.g_raw, i) + a.dt_bias[(size_t)head * BK + c4 + e];
-                    const float sp = z > 20.f ? z : log1pf(expf(z));
-                    qv[e] = a.scale * ld<BF16>(a.q, i);
-                    kv[e] = ld<BF16>(a.k, i);
-                    ev[e] = expf(-A * sp);
+                    qv[e] = a.scale * raw.q[e];
+                    kv[e] = raw.k[e];
+                    ev[e] = gate_decay(raw.g[e] + Ldtb[st_c4 + e], A);   // hardware exp2 / log2
                 }
                 Lq[tt][tid & 31] = qv;
                 Lk[tt][tid & 31] = kv;
                 Le[tt][tid & 31] = ev;
-                const int r = tid & 31;
-                const size_t iv = (tok * H + head) * BV + quarter * QR + r;
-                Lv[tt][r] = ld<BF16>(a.v, iv);
-                Ldo[tt][r] = ld<BF16>(a.do_, iv);
+                Lv[tt][st_r] = raw.v;
+                Ldo[tt][st_r] = raw.dO;
             }
-            if (tid < nt) Lbeta[tid] = sigmoid_f(ld<BF16>(a.beta_raw, (bos + t0 + tid) * H + head));
+            if (tid < nt) Lbeta[tid] = sigmoid_f(raw.b);
         }
         __syncthreads();
 
         // ---- forward recompute from the stored entering state; keep every token's
-        // entering state (this thread's elements) in the workspace
-        f32x4 S[2];
-        {
-            const float *hc = a.h_chunks + (((cbase + c) * H + head) * BV + row) * (size_t)BK;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) S[h2] = *reinterpret_cast<const f32x4 *>(hc + 4 * j + 64 * h2);
-        }
+        // entering state (this thread's elements) in registers
+        f32x4 S[2] = {raw.S[0], raw.S[1]};
         f32x4 hist[BCH][2];   // entering state of every token of the chunk (this thread's elements)
 #pragma unroll
         for (int tt = 0; tt < BCH; ++tt) {
@@ -179,6 +203,7 @@ __global__ __launch_bounds__(512) void bwd_kernel(BwdArgs a)
         // ---- adjoint, tokens in reverse (fully unrolled: the history stays in registers)
 #pragma unroll
         for (int tt = BCH - 1; tt >= 0; --tt) {
+            if (tt == BCH / 2 - 1 && c > 0) load_raw(c - 1);   // half the history is free now
             if (tt < nt) {
             const size_t tok = bos + t0 + tt;
             const int rb = tt & 1;
