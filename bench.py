@@ -19,7 +19,9 @@ rows, heads and pool) are timed the same way and reported as extra fields,
 as is kda_conv_decode_step (width-4 convolution fused with the decode step)
 and the two passes of the materialised form on the prefill workload
 (kda_chunk_fwd_states, then the chunk-parallel output pass), and
-kda_backward from those states.
+kda_backward from those states.  `copy_reference` is a plain device copy
+of 256 MiB timed the same way: the streaming bandwidth this GPU reaches in
+practice, beside the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -216,6 +218,27 @@ def measured_mfma():
     if t.get("source_hash") != source_hash(KERNEL_SOURCES["chunk_fwd"]):
         return None
     return t["mfma_flops_per_launch"], t["mfma_util_pct"]
+
+
+def copy_reference(dev, reps=20):
+    """Device-to-device copy of COPY_CALIB_ELEMS float32 (read + write), timed with
+    events on the current stream: the bandwidth a plain streaming kernel reaches on
+    this GPU, a second reference beside the 8 TB/s peak."""
+    import torch
+    x = torch.ones(COPY_CALIB_ELEMS, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del x, y
+    return 2 * 4 * COPY_CALIB_ELEMS / t / 1e9
 
 
 def main():
@@ -475,6 +498,7 @@ def main():
     value = tokheads / pre_avg / 1e6
     pre_gbs = pbytes / pre_avg / 1e9
     dec_gbs = dbytes / dec_graph_avg / 1e9
+    copy_gbs = copy_reference(dev)
 
     # ---------------- CPU baseline: fp64 oracle on the same prefill workload
     cpu = None
@@ -558,6 +582,10 @@ def main():
                             "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                             "traffic": traffic_d, "kernel": "decode_kernel<128,128>",
                             "algorithmic_bytes": dbytes},
+        "copy_reference": {"kernel": f"torch copy_ of {4 * COPY_CALIB_ELEMS >> 20} MiB float32",
+                           "gbs": round(copy_gbs, 1), "frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+                           "decode_frac_of_copy": round(dec_gbs / copy_gbs, 4),
+                           "prefill_frac_of_copy": round(pre_gbs / copy_gbs, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
