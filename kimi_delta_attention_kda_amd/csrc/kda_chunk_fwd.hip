@@ -940,12 +940,13 @@ __global__ __launch_bounds__(NTHR, 2) void chunk_fwd_kernel(ChunkArgs args)
                 vv = *reinterpret_cast<const f32x4 *>(pl + voff + lane * 16);
             }
             // the state entering this chunk, for the materialised form (same
-            // addressing as h_T, chunk row cbase + c)
+            // addressing as h_T, chunk row cbase + c); non-temporal stores, so
+            // that the snapshots do not evict the payload ring from L2
             if constexpr (SNAP) {
                 const size_t at = (((cbase + c) * args.H + ci.head) * DV + v0 + ln) * DK;
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt)
-                    *reinterpret_cast<f32x4 *>(args.h_chunks + at + tile_chan<BF16>(mt, lq, 0)) = S[mt];
+                    __builtin_nontemporal_store(S[mt], reinterpret_cast<f32x4 *>(args.h_chunks + at + tile_chan<BF16>(mt, lq, 0)));
             }
             // R1: W = k~ S, Qs = q~ S ; then decay the state in place
             f32x4 W = {0.f, 0.f, 0.f, 0.f}, Qs = {0.f, 0.f, 0.f, 0.f};
