@@ -43,12 +43,13 @@
  *   - The calls enqueue work on `stream` and return without synchronising;
  *     results are ready once the caller synchronises the stream.  A kernel
  *     fault surfaces at that synchronisation.
- *   - kda_decode_step, kda_decode_extend and kda_conv_decode_step allocate
- *     nothing.  kda_chunk_fwd(_pool) uses a device
- *     workspace (ring buffers and flags for its producer/consumer teams,
- *     about 64 MiB) that the library allocates on the first call on each
- *     device and keeps until the process exits; calls that overlap in time
- *     on one device share it and must not run concurrently.
+ *   - No entry point allocates memory.  kda_backward takes a caller-owned
+ *     workspace (size from kda_backward_workspace_bytes).  Calls on different
+ *     streams may overlap: no kernel keeps state between launches or shares
+ *     scratch memory with another launch.
+ *   - Invalid input that lives in device memory (a pool slot index >= P) is
+ *     handled by the kernels as documented per entry point and recorded in a
+ *     sticky per-device error word, which kda_device_check() reads and clears.
  *   - Results are deterministic (no atomics in the arithmetic): the same
  *     inputs give bitwise-identical outputs.
  */
@@ -69,7 +70,7 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = -3, /* valid but not built (head dim, chunk size, dtype) */
     KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     KDA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
-    KDA_ERR_TIMEOUT = -6      /* a chunk-forward team wait gave up (see kda_chunk_fwd_check) */
+    KDA_ERR_SLOT = -6         /* a kernel met a pool slot index >= P (see kda_device_check) */
 } kda_status;
 
 typedef enum {
@@ -82,19 +83,20 @@ typedef enum {
  * "L 矩阵的构造", "Mqk 矩阵的构造", "为什么 CHUNK16", "K2 内核如何消费";
  * sequence loop inside the workgroup as in [TL-KDA] section 6.4).
  *
- * Per chunk of C = 16 tokens of one (sequence, head):
- *   G = chunk-local cumulative gate (log domain),
+ * Per chunk of C = 16 tokens of one (sequence, head), G the chunk-local
+ * cumulative gate and S the state as (dk, dv):
  *   L  (16x16, strictly lower) and Mqk (16x16, lower incl. diagonal) by MFMA,
  *   INV = (I - L)^{-1} by Neumann squaring,
- *   U = INV (beta * (v - (k e^G) S^T)),  O = (q e^G) S^T + Mqk U (times scale),
- *   S <- S Diag(e^{G_C}) + U^T (k e^{G_C - G})   (after the output).
- * The state-independent part of each chunk (gate, decayed operands, L, Mqk,
- * INV) is built by producer workgroups and handed through an on-device ring
- * to consumer workgroups, one per d_v slab, that carry the fp32 state slab in
- * registers through the sequential chunk loop.  The workgroups of one launch
- * wait on each other, so the launch needs the GPU's compute units to itself:
- * if other kernels occupy them, a wait may give up after about a second,
- * which kda_chunk_fwd_check() reports.
+ *   U = INV beta (v - (k e^G) S) = u' - w S with u' = INV beta v, w = INV beta (k e^G),
+ *   O = scale ((q e^G) S + Mqk U),
+ *   S <- Diag(e^{G_C}) S + (k e^{G_C - G})^T U   (after the output).
+ * One workgroup carries one (sequence, head, group of state columns) through
+ * the whole sequence; inside it, prep waves build each chunk's
+ * state-independent operands (gate, decayed operands, L, Mqk, INV, w, u')
+ * three chunks ahead while consumer waves hold the fp32 state columns in MFMA
+ * accumulators and run the recurrence.  Workgroups never wait on each other
+ * and the launch uses no memory besides its arguments.  Packed sequences are
+ * scheduled longest first (up to 128 sequences).
  *
  * Layout (T_all = B*T for dense input, = T for packed input):
  *   q, k, g_raw : [T_all, H, dk]   activation dtype, q and k expected
@@ -239,7 +241,9 @@ int kda_backward(const void *q, const void *k, const void *v,
  *   state_idx  : [n_seq] int32 slot per sequence (device memory).  Live
  *                entries must be distinct and < P (duplicates race; not
  *                checked on the host because the indices live in device
- *                memory).
+ *                memory).  An entry >= P is treated like a negative one
+ *                (zero start, no final state, no pool access) and recorded
+ *                for kda_device_check.
  * Returns KDA_OK or a negative kda_status (KDA_ERR_SHAPE for P <= 0,
  * KDA_ERR_NULL for a missing pool or index array).
  */
@@ -269,8 +273,10 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v,
  *   A_log      : [HV] float32       dt_bias : [HV*K] float32
  *   state_pool : [P, HV, V, K] float32, updated in place
  *   state_idx  : [B] int32 slot per row; < 0 marks a pad row.  Live entries
- *                must be distinct and < P (duplicates race; not checked on
- *                the host because the indices live in device memory).
+ *                must be distinct (duplicates race; not checked on the host
+ *                because the indices live in device memory).  An entry >= P
+ *                is handled as a pad row (zero output, no state access) and
+ *                recorded for kda_device_check.
  *   o          : [B, HV, V] bf16
  *   K, V       : 128 each.  HV % H == 0.
  *   flags      : bit 0 set = L2-normalise q and k in the kernel.
@@ -299,8 +305,9 @@ int kda_decode_step(const void *qkv, const void *a, const void *b,
  *   A_log      : [HV] float32           dt_bias : [HV*K] float32
  *   state_pool : [P, HV, V, K] float32, updated in place
  *   state_idx  : [B] int32 slot per row; < 0 marks a pad row (all T outputs
- *                zero, no state access).  Live entries must be distinct and
- *                < P (not checked on the host: device memory).
+ *                zero, no state access).  Live entries must be distinct (not
+ *                checked on the host: device memory); an entry >= P is
+ *                handled as a pad row and recorded for kda_device_check.
  *   o          : [B, T, HV, V] bf16; o[n, t] is read from the state after
  *                token t.
  *   K, V       : 128 each.  HV % H == 0.  T >= 0 (T == 0 launches nothing).
@@ -327,7 +334,8 @@ int kda_decode_extend(const void *qkv, const void *a, const void *b,
  *   conv_state[idx, :, c] <- window[1 .. W-1],
  * computed in fp32, and y (not rounded) is the qkv row of kda_decode_step's
  * update, which then updates state_pool[idx] and writes o[n].  A pad row
- * (idx < 0) gets zero outputs and touches neither state.
+ * (idx < 0) gets zero outputs and touches neither state; so does a row with
+ * idx >= P, which is also recorded for kda_device_check.
  *
  * Layout:
  *   mixed_qkv   : [B, D] bf16 (q heads, k heads, v heads, before the conv)
@@ -347,12 +355,14 @@ int kda_conv_decode_step(const void *mixed_qkv, void *conv_state,
                          float scale, int flags, hipStream_t stream);
 
 /*
- * kda_chunk_fwd_check -- synchronise `stream` and report whether the last
- * kda_chunk_fwd on the current device completed its team waits
- * (KDA_OK) or gave up on one (KDA_ERR_TIMEOUT; its outputs are then invalid).
- * For tests and debugging; the normal path never needs it.
+ * kda_device_check -- synchronise `stream`, then read and clear the current
+ * device's error word: KDA_ERR_SLOT if, since the last check, a kernel of
+ * this library met a pool slot index >= P (kda_decode_step,
+ * kda_decode_extend, kda_conv_decode_step, kda_chunk_fwd_pool; the row was
+ * handled as a pad), else KDA_OK.  KDA_ERR_HIP if the synchronisation or the
+ * copy fails.
  */
-int kda_chunk_fwd_check(hipStream_t stream);
+int kda_device_check(hipStream_t stream);
 
 /* Human-readable name of a kda_status value (static string). */
 const char *kda_status_str(int status);

@@ -19,7 +19,7 @@ _lib = None
 KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_states", "kda_chunk_fwd_check", "kda_decode_step",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_states", "kda_device_check", "kda_decode_step",
            "kda_decode_extend", "kda_conv_decode_step", "kda_chunk_o", "kda_backward", "kda_backward_workspace_bytes",
            "kda_status_str")
 
@@ -57,8 +57,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_backward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                  ctypes.c_size_t, I, I, I, I, I, I, F, I, P]
     lib.kda_backward.restype = I
-    lib.kda_chunk_fwd_check.argtypes = [P]
-    lib.kda_chunk_fwd_check.restype = I
+    lib.kda_device_check.argtypes = [P]
+    lib.kda_device_check.restype = I
     lib.kda_status_str.argtypes = [I]
     lib.kda_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -178,12 +178,19 @@ def chunk_fwd_pool(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_i
     return o
 
 
-def chunk_fwd_check(stream=None):
-    """Synchronise the stream and raise if the last chunk_fwd gave up on a
-    team wait (its outputs would be invalid)."""
+KDA_ERR_SLOT = -6
+
+
+def device_check(stream=None) -> int:
+    """Synchronise the stream, then read and clear the device error word:
+    returns 0, or KDA_ERR_SLOT (-6) if a kernel met a pool slot index >= P
+    since the last check (those rows were handled as pads)."""
     if stream is None:
         stream = torch.cuda.current_stream().cuda_stream
-    _check(load_library().kda_chunk_fwd_check(ctypes.c_void_p(stream)))
+    rc = load_library().kda_device_check(ctypes.c_void_p(stream))
+    if rc not in (0, KDA_ERR_SLOT):
+        _check(rc)
+    return rc
 
 
 def decode_step(qkv, a, b, A_log, dt_bias, state_pool, state_idx, num_heads: int,

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk_fwd.hip", "kda_backward.hip", "kda_chunk_o.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_fwd.hip", "kda_fwd_f32.hip", "kda_backward.hip", "kda_chunk_o.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

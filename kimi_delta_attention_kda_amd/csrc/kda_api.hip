@@ -1,6 +1,9 @@
 // kda_api.hip -- extern "C" entry points of libkda (see include/kda.h):
-// argument validation on the host, then one kernel launch on the caller's
-// stream.  No allocation, no synchronisation, no global mutable state.
+// argument validation on the host, then kernel launches on the caller's
+// stream.  No device allocation and no synchronisation.  The one piece of
+// library state is a per-device error word in device memory, which kernels
+// set when they meet an invalid slot index in device memory and which
+// kda_device_check reads and clears.
 #include <stdint.h>
 
 #include <mutex>
@@ -12,24 +15,28 @@ namespace {
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Chunk-forward workspace: one block of device memory per device, allocated on
-// first use and kept until the process exits (team ring buffers + flags).
-constexpr int kMaxDevices = 64;
-std::mutex g_ws_mutex;
-void *g_ws[kMaxDevices] = {};
+// The device error word: one int per GPU (a __device__ variable exists once per
+// device the library runs on).  Its address is looked up once per device.
+__device__ int g_kda_device_errors;
 
-hipError_t workspace(void **out)
+constexpr int kMaxDevices = 64;
+std::mutex g_err_mutex;
+int *g_err_ptr[kMaxDevices] = {};
+
+hipError_t error_word(int **out)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    if (!g_ws[dev]) {
-        e = hipMalloc(&g_ws[dev], kda::chunk_workspace_bytes());
-        if (e != hipSuccess) { g_ws[dev] = nullptr; return e; }
+    std::lock_guard<std::mutex> lock(g_err_mutex);
+    if (!g_err_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_kda_device_errors));
+        if (e != hipSuccess) return e;
+        g_err_ptr[dev] = static_cast<int *>(p);
     }
-    *out = g_ws[dev];
+    *out = g_err_ptr[dev];
     return hipSuccess;
 }
 
@@ -46,7 +53,7 @@ const char *kda_status_str(int status)
     case KDA_ERR_UNSUPPORTED: return "unsupported configuration (head dims, chunk size or dtype)";
     case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDA_ERR_HIP: return "HIP launch error";
-    case KDA_ERR_TIMEOUT: return "a chunk-forward team wait timed out (workgroups not co-resident)";
+    case KDA_ERR_SLOT: return "a kernel met a pool slot index >= P (treated as a pad row)";
     default: return "unknown status";
     }
 }
@@ -57,7 +64,7 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
                           const void *beta_raw, const float *A_log, const float *dt_bias,
                           const float *h0, const int32_t *state_idx, const int32_t *cu_seqlens,
                           int chunk, void *o, float *h_T, float *h_chunks, int B, int T, int H, int dk,
-                          int dv, int n_seq, float scale, kda_dtype dtype, hipStream_t stream)
+                          int dv, int n_seq, int P, float scale, kda_dtype dtype, hipStream_t stream)
 {
     if (chunk != 16) return KDA_ERR_UNSUPPORTED;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -79,17 +86,14 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
     if (n_seq == 0) return KDA_OK;
 
-    void *ws = nullptr;
-    if (workspace(&ws) != hipSuccess) return KDA_ERR_HIP;
-    kda::ChunkArgs a;
-    a.ring = static_cast<unsigned char *>(ws);
-    a.flags = reinterpret_cast<int *>(a.ring + (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES);
-    a.err = a.flags + (size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS;
-    a.n_teams = 0;
+    kda::FwdArgs a;
+    if (error_word(&a.err) != hipSuccess) return KDA_ERR_HIP;
     a.q = q; a.k = k; a.v = v; a.g_raw = g_raw; a.beta_raw = beta_raw;
     a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.state_idx = state_idx; a.cu_seqlens = cu_seqlens;
-    a.o = o; a.h_T = h_T; a.h_chunks = h_chunks; a.T = T; a.H = H; a.n_seq = n_seq; a.scale = scale;
-    const hipError_t e = kda::launch_chunk_fwd(a, dtype == KDA_BF16 ? 1 : 0, dk, dv, stream);
+    a.o = o; a.h_T = h_T; a.h_chunks = h_chunks; a.T = T; a.H = H; a.n_seq = n_seq; a.P = P;
+    a.scale = scale;
+    const hipError_t e = dtype == KDA_BF16 ? kda::launch_fwd_bf16(a, dk, dv, stream)
+                                           : kda::launch_fwd_f32(a, dk, dv, stream);
     if (e == hipErrorInvalidValue) return KDA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -101,7 +105,7 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw
                   kda_dtype dtype, hipStream_t stream)
 {
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
-                          h_T, nullptr, B, T, H, dk, dv, n_seq, scale, dtype, stream);
+                          h_T, nullptr, B, T, H, dk, dv, n_seq, 0, scale, dtype, stream);
 }
 
 int kda_chunk_fwd_states(const void *q, const void *k, const void *v, const void *g_raw,
@@ -112,7 +116,7 @@ int kda_chunk_fwd_states(const void *q, const void *k, const void *v, const void
 {
     if (n_seq > 0 && T > 0 && !h_chunks) return KDA_ERR_NULL;
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
-                          h_T, h_chunks, B, T, H, dk, dv, n_seq, scale, dtype, stream);
+                          h_T, h_chunks, B, T, H, dk, dv, n_seq, 0, scale, dtype, stream);
 }
 
 int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *g_raw,
@@ -127,7 +131,7 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *
     // the slots double as h0 (read when a sequence starts) and h_T (written when it
     // ends); each (sequence, head, slab) is read and written by the same workgroup
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_idx, cu_seqlens,
-                          chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, scale, dtype, stream);
+                          chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, P, scale, dtype, stream);
 }
 
 int kda_chunk_o(const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,
@@ -203,17 +207,18 @@ int kda_backward(const void *q, const void *k, const void *v, const void *g_raw,
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-int kda_chunk_fwd_check(hipStream_t stream)
+int kda_device_check(hipStream_t stream)
 {
-    void *ws = nullptr;
-    if (workspace(&ws) != hipSuccess) return KDA_ERR_HIP;
+    int *err = nullptr;
+    if (error_word(&err) != hipSuccess) return KDA_ERR_HIP;
     if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
-    const int *err = reinterpret_cast<const int *>(static_cast<unsigned char *>(ws) +
-                                                   (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES) +
-                     (size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS;
     int h = 0;
     if (hipMemcpy(&h, err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return KDA_ERR_HIP;
-    return h ? KDA_ERR_TIMEOUT : KDA_OK;
+    if (h) {
+        const int zero = 0;
+        if (hipMemcpy(err, &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess) return KDA_ERR_HIP;
+    }
+    return (h & KDA_DEVERR_SLOT) ? KDA_ERR_SLOT : KDA_OK;
 }
 
 int kda_decode_step(const void *qkv, const void *a, const void *b, const float *A_log,
@@ -229,10 +234,12 @@ int kda_decode_step(const void *qkv, const void *a, const void *b, const float *
     const void *ptrs[] = {qkv, a, b, A_log, dt_bias, state_pool, state_idx, o};
     for (const void *p : ptrs)
         if (!aligned16(p)) return KDA_ERR_ALIGN;
+    int *err = nullptr;
+    if (error_word(&err) != hipSuccess) return KDA_ERR_HIP;
     const hipError_t e = kda::launch_decode(
         static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(a),
         static_cast<const uint16_t *>(b), A_log, dt_bias, state_pool, state_idx,
-        static_cast<uint16_t *>(o), B, H, HV, scale, flags & KDA_DECODE_L2NORM, stream);
+        static_cast<uint16_t *>(o), B, H, HV, P, scale, flags & KDA_DECODE_L2NORM, err, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -250,10 +257,12 @@ int kda_decode_extend(const void *qkv, const void *a, const void *b, const float
     const void *ptrs[] = {qkv, a, b, A_log, dt_bias, state_pool, state_idx, o};
     for (const void *p : ptrs)
         if (!aligned16(p)) return KDA_ERR_ALIGN;
+    int *err = nullptr;
+    if (error_word(&err) != hipSuccess) return KDA_ERR_HIP;
     const hipError_t e = kda::launch_extend(
         static_cast<const uint16_t *>(qkv), static_cast<const uint16_t *>(a),
         static_cast<const uint16_t *>(b), A_log, dt_bias, state_pool, state_idx,
-        static_cast<uint16_t *>(o), B, T, H, HV, scale, flags & KDA_DECODE_L2NORM, stream);
+        static_cast<uint16_t *>(o), B, T, H, HV, P, scale, flags & KDA_DECODE_L2NORM, err, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -276,11 +285,13 @@ int kda_conv_decode_step(const void *mixed_qkv, void *conv_state, const void *co
                           state_pool, state_idx, o};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    int *err = nullptr;
+    if (error_word(&err) != hipSuccess) return KDA_ERR_HIP;
     const hipError_t e = kda::launch_conv_decode(
         static_cast<const uint16_t *>(mixed_qkv), static_cast<uint16_t *>(conv_state),
         static_cast<const uint16_t *>(conv_weight), static_cast<const uint16_t *>(conv_bias),
         static_cast<const uint16_t *>(a), static_cast<const uint16_t *>(b), A_log, dt_bias, state_pool,
-        state_idx, static_cast<uint16_t *>(o), B, H, HV, W, scale, flags & KDA_DECODE_L2NORM, stream);
+        state_idx, static_cast<uint16_t *>(o), B, H, HV, W, P, scale, flags & KDA_DECODE_L2NORM, err, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -155,8 +155,8 @@ __global__ __launch_bounds__(512) void decode_kernel(
     const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float *__restrict__ pool,
-    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV,
-    float scale, int l2norm)
+    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV, int P,
+    float scale, int l2norm, int *__restrict__ err)
 {
     static_assert(K_ == 128 && V_ == 128, "decode kernel is built for K = V = 128");
     constexpr int ROWS = V_ / 32;  // rows per thread
@@ -184,7 +184,8 @@ __global__ __launch_bounds__(512) void decode_kernel(
 
     uint16_t *orow = o + ((size_t)n * HV + hv) * V_;
     const int idx = state_idx[n];
-    if (idx < 0) {  // pad slot: zero output, no state access
+    if (idx < 0 || idx >= P) {  // pad slot (or one past the pool: reported): zero output, no state access
+        if (idx >= P && threadIdx.x == 0) slot_error(err);
         if (threadIdx.x < V_) orow[threadIdx.x] = 0;
         return;
     }
@@ -235,8 +236,8 @@ __global__ __launch_bounds__(512) void extend_kernel(
     const uint16_t *__restrict__ qkv, const uint16_t *__restrict__ a,
     const uint16_t *__restrict__ b, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float *__restrict__ pool,
-    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int T, int H, int HV,
-    float scale, int l2norm)
+    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int T, int H, int HV, int P,
+    float scale, int l2norm, int *__restrict__ err)
 {
     static_assert(K_ == 128 && V_ == 128, "extend kernel is built for K = V = 128");
     constexpr int ROWS = V_ / 32;
@@ -260,7 +261,8 @@ __global__ __launch_bounds__(512) void extend_kernel(
     const size_t tok0 = (size_t)n * T;
 
     const int idx = state_idx[n];
-    if (idx < 0) {  // pad row: zero outputs, no state access
+    if (idx < 0 || idx >= P) {  // pad row (or one past the pool: reported): zero outputs, no state access
+        if (idx >= P && threadIdx.x == 0) slot_error(err);
         for (int i = threadIdx.x; i < T * (V_ / 8); i += 512)
             *reinterpret_cast<uint4 *>(o + ((tok0 + i / (V_ / 8)) * HV + hv) * V_ + 8 * (i % (V_ / 8))) =
                 make_uint4(0, 0, 0, 0);
@@ -416,8 +418,8 @@ __global__ __launch_bounds__(512) void conv_decode_kernel(
     const uint16_t *__restrict__ cw, const uint16_t *__restrict__ cb,
     const uint16_t *__restrict__ a, const uint16_t *__restrict__ b,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float *__restrict__ pool,
-    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV,
-    float scale, int l2norm)
+    const int32_t *__restrict__ state_idx, uint16_t *__restrict__ o, int H, int HV, int P,
+    float scale, int l2norm, int *__restrict__ err)
 {
     static_assert(K_ == 128 && V_ == 128, "conv decode kernel is built for K = V = 128");
     static_assert(W_ >= 2 && W_ <= 4, "conv width 2..4");
@@ -434,7 +436,8 @@ __global__ __launch_bounds__(512) void conv_decode_kernel(
     const int nch = 2 * K_ + G * V_;
 
     const int idx = state_idx[n];
-    if (idx < 0) {  // pad row: zero outputs, no state access
+    if (idx < 0 || idx >= P) {  // pad row (or one past the pool: reported): zero outputs, no state access
+        if (idx >= P && threadIdx.x == 0) slot_error(err);
         for (int i = threadIdx.x; i < G * V_; i += 512) o[((size_t)n * HV + (size_t)hq * G) * V_ + i] = 0;
         return;
     }
@@ -537,44 +540,44 @@ __global__ __launch_bounds__(512) void conv_decode_kernel(
 
 hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
                          const float *A_log, const float *dt_bias, float *pool,
-                         const int32_t *state_idx, uint16_t *o, int B, int H, int HV,
-                         float scale, int l2norm, hipStream_t stream)
+                         const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int P,
+                         float scale, int l2norm, int *err, hipStream_t stream)
 {
     hipLaunchKernelGGL((decode_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(512), 0, stream,
-                       qkv, a, b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+                       qkv, a, b, A_log, dt_bias, pool, state_idx, o, H, HV, P, scale, l2norm, err);
     return hipGetLastError();
 }
 
 hipError_t launch_extend(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
                          const float *A_log, const float *dt_bias, float *pool,
-                         const int32_t *state_idx, uint16_t *o, int B, int T, int H, int HV,
-                         float scale, int l2norm, hipStream_t stream)
+                         const int32_t *state_idx, uint16_t *o, int B, int T, int H, int HV, int P,
+                         float scale, int l2norm, int *err, hipStream_t stream)
 {
     hipLaunchKernelGGL((extend_kernel<128, 128>), dim3((unsigned)(B * HV)), dim3(512), 0, stream,
-                       qkv, a, b, A_log, dt_bias, pool, state_idx, o, T, H, HV, scale, l2norm);
+                       qkv, a, b, A_log, dt_bias, pool, state_idx, o, T, H, HV, P, scale, l2norm, err);
     return hipGetLastError();
 }
 
 hipError_t launch_conv_decode(const uint16_t *x, uint16_t *conv_state, const uint16_t *cw,
                               const uint16_t *cb, const uint16_t *a, const uint16_t *b,
                               const float *A_log, const float *dt_bias, float *pool,
-                              const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int W,
-                              float scale, int l2norm, hipStream_t stream)
+                              const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int W, int P,
+                              float scale, int l2norm, int *err, hipStream_t stream)
 {
     const size_t lds = sizeof(float) * (2 * 128 + (size_t)(HV / H) * 128);
     const dim3 grid((unsigned)(B * H)), block(512);
     switch (W) {
     case 2:
         hipLaunchKernelGGL((conv_decode_kernel<128, 128, 2>), grid, block, lds, stream, x, conv_state, cw, cb, a,
-                           b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+                           b, A_log, dt_bias, pool, state_idx, o, H, HV, P, scale, l2norm, err);
         break;
     case 3:
         hipLaunchKernelGGL((conv_decode_kernel<128, 128, 3>), grid, block, lds, stream, x, conv_state, cw, cb, a,
-                           b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+                           b, A_log, dt_bias, pool, state_idx, o, H, HV, P, scale, l2norm, err);
         break;
     case 4:
         hipLaunchKernelGGL((conv_decode_kernel<128, 128, 4>), grid, block, lds, stream, x, conv_state, cw, cb, a,
-                           b, A_log, dt_bias, pool, state_idx, o, H, HV, scale, l2norm);
+                           b, A_log, dt_bias, pool, state_idx, o, H, HV, P, scale, l2norm, err);
         break;
     default: return hipErrorInvalidValue;
     }

@@ -5,57 +5,51 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Chunk-forward team ring: slots per team, bytes per slot, and the largest
-// number of teams one launch uses.
-#ifndef KDA_RING
-#define KDA_RING 8
-#endif
-#define KDA_RING_SLOT_BYTES 24576   // largest slot; a launch uses its payload's copy size
-#define KDA_MAX_TEAMS 256
-// Per-team flag block (ints): ready[KDA_RING] at 0, used[KDA_RING] at 32, so
-// each array has a cache line to itself and no line is shared between teams
-// (teams run on different XCDs).
-#define KDA_TEAM_FLAG_INTS 64
+// Bits of the per-device error word that kernels set on invalid input found
+// in device memory (sticky until kda_device_check reads and clears them).
+#define KDA_DEVERR_SLOT 1   // a live pool slot index >= P (treated as a pad)
 
 namespace kda {
 
-// Producer workgroups per team of the chunkwise prefill (each builds every
-// fourth chunk of the team's chains).
-constexpr int KDA_PRODUCER_WGS = 4;
+// Report an out-of-range slot: a vector atomic OR into the error word.
+__device__ __forceinline__ void slot_error(int *err) {
+    __hip_atomic_fetch_or(err, KDA_DEVERR_SLOT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
+// Pool-addressed launchers: slots are state_idx[n] in [0, P); a negative
+// index is a pad row, an index >= P is treated as a pad and sets
+// KDA_DEVERR_SLOT in *err.
 hipError_t launch_decode(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
                          const float *A_log, const float *dt_bias, float *pool,
-                         const int32_t *state_idx, uint16_t *o, int B, int H, int HV,
-                         float scale, int l2norm, hipStream_t stream);
+                         const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int P,
+                         float scale, int l2norm, int *err, hipStream_t stream);
 hipError_t launch_extend(const uint16_t *qkv, const uint16_t *a, const uint16_t *b,
                          const float *A_log, const float *dt_bias, float *pool,
-                         const int32_t *state_idx, uint16_t *o, int B, int T, int H, int HV,
-                         float scale, int l2norm, hipStream_t stream);
+                         const int32_t *state_idx, uint16_t *o, int B, int T, int H, int HV, int P,
+                         float scale, int l2norm, int *err, hipStream_t stream);
 
 hipError_t launch_conv_decode(const uint16_t *x, uint16_t *conv_state, const uint16_t *cw,
                               const uint16_t *cb, const uint16_t *a, const uint16_t *b,
                               const float *A_log, const float *dt_bias, float *pool,
-                              const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int W,
-                              float scale, int l2norm, hipStream_t stream);
+                              const int32_t *state_idx, uint16_t *o, int B, int H, int HV, int W, int P,
+                              float scale, int l2norm, int *err, hipStream_t stream);
 
-struct ChunkArgs {
+// Chunkwise prefill (kda_fwd.hip for bf16, kda_fwd_f32.hip for fp32).
+struct FwdArgs {
     const void *q, *k, *v, *g_raw, *beta_raw;
     const float *A_log, *dt_bias, *h0;
-    const int32_t *state_idx;   // NULL: h0 / h_T row = sequence; else row = state_idx[sequence] (< 0: none)
+    const int32_t *state_idx;   // NULL: h0 / h_T row = sequence; else row = state_idx[sequence] (< 0 or >= P: none)
     const int32_t *cu_seqlens;
     void *o;
     float *h_T;
     float *h_chunks;     // NULL, or [N_chunks][H][DV][DK]: the state entering every chunk
     int T, H, n_seq;     // T: per-sequence length for dense input, total tokens if cu_seqlens
+    int P;               // pool slots (state_idx only)
     float scale;
-    // workspace (device memory owned by the library)
-    unsigned char *ring;   // KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES
-    int *flags;            // [KDA_MAX_TEAMS][KDA_TEAM_FLAG_INTS], then err (zeroed per launch)
-    int *err;
-    int n_teams;           // set by the launcher
-    int teams_per_xcd;     // set by the launcher
-    int pair_half;         // workgroups per XCD in the first dispatch round (0: no CU pairing)
+    int *err;            // the device error word
 };
+hipError_t launch_fwd_bf16(const FwdArgs &a, int dk, int dv, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs &a, int dk, int dv, hipStream_t stream);
 
 struct ChunkOArgs {
     const void *q, *k, *v, *g_raw, *beta_raw;
@@ -82,15 +76,5 @@ struct BwdArgs {
 };
 size_t bwd_workspace_bytes(int n_seq, int H, long long tokens);
 hipError_t launch_bwd(const BwdArgs &a, int dtype, hipStream_t stream);
-
-// Bytes of the flag area (team blocks, then a 256-byte block for the error word).
-inline size_t chunk_flag_bytes() { return sizeof(int) * ((size_t)KDA_MAX_TEAMS * KDA_TEAM_FLAG_INTS + 64); }
-// Device bytes of the chunk-forward workspace.
-inline size_t chunk_workspace_bytes() {
-    return (size_t)KDA_MAX_TEAMS * KDA_RING * KDA_RING_SLOT_BYTES + chunk_flag_bytes();
-}
-
-// dtype: 0 = float32, 1 = bfloat16 activations.
-hipError_t launch_chunk_fwd(const ChunkArgs &a, int dtype, int dk, int dv, hipStream_t stream);
 
 }  // namespace kda

@@ -38,7 +38,7 @@ def close_grad(got, ref, what):
 def run(p, seed, with_dhT=True):
     d = to_device(p)
     _, _, hc = kda.chunk_fwd_states(**d, scale=p.scale)
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     do_bits, dhT = synth.cotangents(seed, p.tokens, p.H, p.dv, p.dk, len(p.offsets()) - 1, with_dhT)
     B, T = d["q"].shape[:2]
     do = torch.from_numpy(do_bits.view(np.int16)).view(torch.bfloat16).cuda().reshape(B, T, p.H, p.dv)

@@ -139,7 +139,7 @@ def test_prefill_graph_replay():
     d = to_device(p)
     print("[case] prefill graph replay B2 T300 H4", flush=True)
     o_ref, h_ref = kda.chunk_fwd(**d, scale=p.scale)     # also sets up the library's workspace
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     o, hT = torch.empty_like(o_ref), torch.empty_like(h_ref)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -155,7 +155,7 @@ def test_prefill_graph_replay():
         hT.zero_()
         g.replay()
         torch.cuda.synchronize()
-        kda.chunk_fwd_check()
+        assert kda.device_check() == 0
         assert torch.equal(o, o_ref) and torch.equal(hT, h_ref)
         o2, h2 = kda.chunk_fwd(**d, scale=p.scale)       # eager work between replays
         torch.cuda.synchronize()

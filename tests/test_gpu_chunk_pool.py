@@ -28,7 +28,7 @@ def pool_run(p, pool0, idx):
     d.pop("h0")
     pool = torch.from_numpy(pool0.copy()).cuda()
     o = kda.chunk_fwd_pool(**d, state_pool=pool, state_idx=torch.from_numpy(idx).cuda(), scale=p.scale)
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     return (o.float().cpu().numpy().reshape(p.tokens, p.H, p.dv).astype(np.float64),
             pool.cpu().numpy())
 
@@ -48,7 +48,7 @@ def test_pool_equals_dense_and_oracle(dk, dtype):
     pd = synth.Prefill(**{**p.__dict__, "h0": h0})
     d = to_device(pd)
     o_d, hT_d = kda.chunk_fwd(**d, scale=p.scale)
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     o_d = o_d.float().cpu().numpy().reshape(p.tokens, p.H, p.dv).astype(np.float64)
     hT_d = hT_d.cpu().numpy()
     assert np.array_equal(o_pool, o_d)
@@ -73,7 +73,7 @@ def test_pool_prefill_then_decode_equals_longer_prefill():
     say("pool prefill then decode", "B", B, "T", T)
     full = to_device(p)
     o_full, h_full = kda.chunk_fwd(**{k: v for k, v in full.items() if k != "h0"}, scale=p.scale)
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     o_full = o_full.float().cpu().numpy().astype(np.float64)      # [B, T+1, H, dv]
     h_full = h_full.cpu().numpy()
 
@@ -88,7 +88,7 @@ def test_pool_prefill_then_decode_equals_longer_prefill():
     d.pop("h0")
     idx_dev = torch.from_numpy(idx).cuda()
     kda.chunk_fwd_pool(**d, state_pool=pool, state_idx=idx_dev, scale=p.scale)
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     qkv = np.concatenate([q[:, T].reshape(B, -1), k[:, T].reshape(B, -1), v[:, T].reshape(B, -1)], axis=1)
     o_dec = kda.decode_step(bf16_dev(qkv), bf16_dev(a[:, T].reshape(B, -1)), bf16_dev(b[:, T].reshape(B, -1)),
                             torch.from_numpy(p.A_log).cuda(), torch.from_numpy(p.dt_bias.reshape(-1)).cuda(),

@@ -37,12 +37,12 @@ def check_states(p, heads=None, what=""):
     d = to_device(p)
     o1, hT1 = kda.chunk_fwd(**d, scale=p.scale)
     o2, hT2, hc = kda.chunk_fwd_states(**d, scale=p.scale)
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     assert torch.equal(o1, o2) and torch.equal(hT1, hT2), what + ": outputs differ from kda_chunk_fwd"
     # chunk-parallel output pass from the stored states
     dd = {k_: v_ for k_, v_ in d.items() if k_ != "h0"}
     o3 = kda.chunk_o_from_states(**dd, h_chunks=hc, scale=p.scale)
-    kda.chunk_fwd_check()
+    assert kda.device_check() == 0
     assert torch.equal(o1, o3), what + ": chunk-parallel pass differs"
     if p.dtype == "bf16" and p.dk == 128 and p.dv == 128:
         o4 = kda.chunk_o(**dd, h_chunks=hc, scale=p.scale)
