@@ -44,9 +44,11 @@
  *     results are ready once the caller synchronises the stream.  A kernel
  *     fault surfaces at that synchronisation.
  *   - No entry point allocates memory.  kda_backward takes a caller-owned
- *     workspace (size from kda_backward_workspace_bytes).  Calls on different
- *     streams may overlap: no kernel keeps state between launches or shares
- *     scratch memory with another launch.
+ *     workspace (size from kda_backward_workspace_bytes); the prefill entry
+ *     points take an optional one (size from kda_chunk_fwd_workspace_bytes).
+ *     Calls on different streams may overlap as long as they do not share a
+ *     workspace: no kernel keeps state between launches or shares memory with
+ *     another launch.
  *   - Invalid input that lives in device memory (a pool slot index >= P) is
  *     handled by the kernels as documented per entry point and recorded in a
  *     sticky per-device error word, which kda_device_check() reads and clears.
@@ -90,13 +92,21 @@ typedef enum {
  *   U = INV beta (v - (k e^G) S) = u' - w S with u' = INV beta v, w = INV beta (k e^G),
  *   O = scale ((q e^G) S + Mqk U),
  *   S <- Diag(e^{G_C}) S + (k e^{G_C - G})^T U   (after the output).
- * One workgroup carries one (sequence, head, group of state columns) through
- * the whole sequence; inside it, prep waves build each chunk's
- * state-independent operands (gate, decayed operands, L, Mqk, INV, w, u')
- * three chunks ahead while consumer waves hold the fp32 state columns in MFMA
- * accumulators and run the recurrence.  Workgroups never wait on each other
- * and the launch uses no memory besides its arguments.  Packed sequences are
- * scheduled longest first (up to 128 sequences).
+ * The state-independent part of every chunk ("prep": gate, decayed operands,
+ * L, Mqk, INV, w) is built by prep waves and the recurrence by consumer
+ * waves that hold the fp32 state columns in MFMA accumulators.  Two forms:
+ *   - one pass (no workspace needed): one workgroup carries one (sequence,
+ *     head, group of state columns) through the whole sequence, its prep waves
+ *     three chunks ahead of its consumer waves, hand-over through LDS.  With
+ *     fewer chains than compute units the columns are split over several
+ *     workgroups, each repeating the prep;
+ *   - two passes (when `workspace` holds at least
+ *     kda_chunk_fwd_workspace_bytes() bytes and the (sequence, head) chains are
+ *     fewer than the compute units): a fully parallel pass writes every
+ *     chunk's consumer operands into the workspace, then one wave per
+ *     (sequence, head, 16 state columns) runs the recurrence from them.
+ * Both give the same results up to rounding order.  No workgroup waits on
+ * another.  Packed sequences are scheduled longest first (up to 128).
  *
  * Layout (T_all = B*T for dense input, = T for packed input):
  *   q, k, g_raw : [T_all, H, dk]   activation dtype, q and k expected
@@ -115,6 +125,10 @@ typedef enum {
  *   chunk       : must be 16.
  *   dk, dv      : 64 or 128 each.
  *   scale       : multiplies q (usually dk^-1/2).
+ *   dtype       : KDA_BF16 (dk, dv in {64, 128}) or KDA_F32 (dk = 64).
+ *   workspace   : NULL, or caller-owned device memory of workspace_bytes
+ *                 bytes (contents on entry do not matter; overwritten); see
+ *                 kda_chunk_fwd_workspace_bytes.  Only the bf16 form uses it.
  * A zero-length sequence leaves its outputs untouched and writes h_T = h0
  * (or zeros).  T == 0 is accepted and launches nothing except the h_T copy.
  * Returns KDA_OK or a negative kda_status.
@@ -125,7 +139,17 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v,
                   const float *h0, const int32_t *cu_seqlens, int chunk,
                   void *o, float *h_T,
                   int B, int T, int H, int dk, int dv, int n_seq,
-                  float scale, kda_dtype dtype, hipStream_t stream);
+                  float scale, kda_dtype dtype,
+                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_workspace_bytes -- bytes of workspace that let the prefill
+ * entry points use their two-pass form: 13,824 (dk = 128) or 7,424 (dk = 64)
+ * per chunk row and head, for ceil(T/16) * B chunk rows of dense input
+ * (packed = 0) or ceil(T/16) + n_seq rows of packed input (packed != 0,
+ * an upper bound: the lengths live in device memory).  0 for invalid sizes.
+ */
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n_seq, int packed);
 
 /*
  * kda_chunk_fwd_states -- kda_chunk_fwd that also writes the state entering
@@ -153,7 +177,8 @@ int kda_chunk_fwd_states(const void *q, const void *k, const void *v,
                          const float *h0, const int32_t *cu_seqlens, int chunk,
                          void *o, float *h_T, float *h_chunks,
                          int B, int T, int H, int dk, int dv, int n_seq,
-                         float scale, kda_dtype dtype, hipStream_t stream);
+                         float scale, kda_dtype dtype,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_chunk_o -- the chunk-parallel output pass of the materialised form
@@ -253,7 +278,8 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v,
                        float *state_pool, const int32_t *state_idx,
                        const int32_t *cu_seqlens, int chunk, void *o,
                        int B, int T, int H, int dk, int dv, int n_seq, int P,
-                       float scale, kda_dtype dtype, hipStream_t stream);
+                       float scale, kda_dtype dtype,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_decode_step -- fused T=1 KDA decode over a state pool ([SGL-PR],

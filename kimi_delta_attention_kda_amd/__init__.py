@@ -19,7 +19,8 @@ _lib = None
 KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_pool", "kda_chunk_fwd_states", "kda_device_check", "kda_decode_step",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_pool", "kda_chunk_fwd_states",
+           "kda_device_check", "kda_decode_step",
            "kda_decode_extend", "kda_conv_decode_step", "kda_chunk_o", "kda_backward", "kda_backward_workspace_bytes",
            "kda_status_str")
 
@@ -38,11 +39,14 @@ def load_library(path: str = LIB_PATH):
         raise KDAError(f"{path} is not built; run __graft_entry__.build() first")
     lib = ctypes.CDLL(path)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, F, I, P]
+    Z = ctypes.c_size_t
+    lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     lib.kda_chunk_fwd.restype = I
-    lib.kda_chunk_fwd_pool.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P]
+    lib.kda_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.kda_chunk_fwd_workspace_bytes.restype = Z
+    lib.kda_chunk_fwd_pool.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
     lib.kda_chunk_fwd_pool.restype = I
-    lib.kda_chunk_fwd_states.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, P, I, I, I, I, I, I, F, I, P]
+    lib.kda_chunk_fwd_states.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     lib.kda_chunk_fwd_states.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P]
     lib.kda_decode_step.restype = I
@@ -85,6 +89,39 @@ def _dev(name, t, dtype=None):
         raise KDAError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+_CU_COUNT = {}
+
+
+def chunk_fwd_workspace_bytes(B: int, T: int, H: int, dk: int, dv: int, n_seq: int, packed: bool) -> int:
+    """Workspace bytes for the two-pass prefill (kda_chunk_fwd_workspace_bytes)."""
+    return int(load_library().kda_chunk_fwd_workspace_bytes(B, T, H, dk, dv, n_seq, int(bool(packed))))
+
+
+def _workspace(workspace, act, B, T, H, dk, dv, n_seq, packed, device):
+    """(pointer, bytes) of the prefill workspace.  "auto": allocate one (torch's
+    caching allocator) when the two-pass form applies (bf16, fewer (sequence,
+    head) chains than compute units); None: no workspace (one-pass form); a
+    uint8 GPU tensor: used as given."""
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise KDAError('workspace must be "auto", None or a uint8 GPU tensor')
+        if act != torch.bfloat16:
+            return None, 0
+        idx = device.index if device.index is not None else torch.cuda.current_device()
+        if idx not in _CU_COUNT:
+            _CU_COUNT[idx] = torch.cuda.get_device_properties(idx).multi_processor_count
+        if n_seq * H >= _CU_COUNT[idx]:
+            return None, 0
+        nbytes = chunk_fwd_workspace_bytes(B, T, H, dk, dv, n_seq, packed)
+        if nbytes == 0:
+            return None, 0
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _dev("workspace", workspace, torch.uint8)
+    return _ptr(workspace), workspace.numel()
+
+
 def _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq):
     if o.numel() != B * T * H * dv:
         raise KDAError("o must hold [B, T, H, dv] elements")
@@ -95,13 +132,14 @@ def _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq):
 
 def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
               chunk: int = 16, scale=None, output_final_state: bool = True,
-              o=None, h_T=None, stream=None):
+              o=None, h_T=None, stream=None, workspace="auto"):
     """Chunkwise KDA prefill.
 
     q, k, g_raw: [B, T, H, dk]; v: [B, T, H, dv]; beta_raw: [B, T, H] -- all
     float32 or all bfloat16 (q, k L2-normalised by the caller).
     A_log: [H] float32; dt_bias: [H, dk] float32.
     h0: [N, H, dv, dk] float32 or None.  cu_seqlens: [N+1] int32 (then B == 1).
+    workspace: "auto", None (one-pass form) or a uint8 GPU tensor (see _workspace).
     Returns (o [B, T, H, dv], h_T [N, H, dv, dk] float32 or None)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -126,17 +164,18 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None
         h_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
     _dev("h_T", h_T, torch.float32)
     _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq)
+    wsp, wsb = _workspace(workspace, act, B, T, H, dk, dv, n_seq, cu_seqlens is not None, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(load_library().kda_chunk_fwd(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
         _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), B, T, H, dk, dv, n_seq,
-        float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
+        float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, wsp, wsb, ctypes.c_void_p(stream)))
     return o, h_T
 
 
 def chunk_fwd_pool(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_idx,
-                   cu_seqlens=None, chunk: int = 16, scale=None, o=None, stream=None):
+                   cu_seqlens=None, chunk: int = 16, scale=None, o=None, stream=None, workspace="auto"):
     """Chunkwise KDA prefill with the states in a decode state pool.
 
     As chunk_fwd, but sequence s starts from state_pool[state_idx[s]] and its
@@ -168,13 +207,14 @@ def chunk_fwd_pool(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_i
     if o is None:
         o = torch.empty((B, T, H, dv), dtype=act, device=q.device)
     _dev("o", o, act)
+    wsp, wsb = _workspace(workspace, act, B, T, H, dk, dv, n_seq, cu_seqlens is not None, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(load_library().kda_chunk_fwd_pool(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
         _ptr(state_pool), _ptr(state_idx), _ptr(cu_seqlens), chunk, _ptr(o), B, T, H, dk, dv, n_seq,
         state_pool.shape[0], float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32,
-        ctypes.c_void_p(stream)))
+        wsp, wsb, ctypes.c_void_p(stream)))
     return o
 
 
@@ -318,7 +358,7 @@ def n_chunks(T: int, B: int = 1, cu_seqlens=None, chunk: int = 16) -> int:
 
 def chunk_fwd_states(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
                      chunk: int = 16, scale=None, output_final_state: bool = True, o=None,
-                     h_T=None, h_chunks=None, stream=None):
+                     h_T=None, h_chunks=None, stream=None, workspace="auto"):
     """chunk_fwd that also returns the state entering every chunk.
     Returns (o, h_T, h_chunks [N_chunks, H, dv, dk] float32)."""
     B, T, H, dk = q.shape
@@ -350,12 +390,13 @@ def chunk_fwd_states(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqle
     if h_chunks.numel() != nc * H * dv * dk:
         raise KDAError("h_chunks must hold [N_chunks, H, dv, dk] elements")
     _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq)
+    wsp, wsb = _workspace(workspace, act, B, T, H, dk, dv, n_seq, cu_seqlens is not None, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(load_library().kda_chunk_fwd_states(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
         _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), _ptr(h_chunks), B, T, H, dk, dv, n_seq,
-        float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
+        float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, wsp, wsb, ctypes.c_void_p(stream)))
     return o, h_T, h_chunks
 
 

@@ -40,6 +40,15 @@ hipError_t error_word(int **out)
     return hipSuccess;
 }
 
+// Chunk rows of a prefill (sum over sequences of ceil(len / 16)): exact for
+// dense input, an upper bound for packed input (whose lengths live in device
+// memory): each sequence adds at most one partial chunk.
+long long chunk_rows(int B, int T, int n_seq, bool packed)
+{
+    if (!packed) return (long long)B * ((T + 15) / 16);
+    return (long long)(T + 15) / 16 + n_seq;
+}
+
 }  // namespace
 
 extern "C" {
@@ -64,7 +73,8 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
                           const void *beta_raw, const float *A_log, const float *dt_bias,
                           const float *h0, const int32_t *state_idx, const int32_t *cu_seqlens,
                           int chunk, void *o, float *h_T, float *h_chunks, int B, int T, int H, int dk,
-                          int dv, int n_seq, int P, float scale, kda_dtype dtype, hipStream_t stream)
+                          int dv, int n_seq, int P, float scale, kda_dtype dtype, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream)
 {
     if (chunk != 16) return KDA_ERR_UNSUPPORTED;
     if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -81,7 +91,8 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     if ((long long)n_seq * H * 2 > 0x7fffffffLL) return KDA_ERR_SHAPE;
     if (!A_log || !dt_bias) return KDA_ERR_NULL;
     if (n_seq > 0 && tokens > 0 && (!q || !k || !v || !g_raw || !beta_raw || !o)) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, h_chunks, cu_seqlens, state_idx};
+    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, h_chunks, cu_seqlens, state_idx,
+                          workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
     if (n_seq == 0) return KDA_OK;
@@ -92,38 +103,47 @@ static int chunk_fwd_impl(const void *q, const void *k, const void *v, const voi
     a.A_log = A_log; a.dt_bias = dt_bias; a.h0 = h0; a.state_idx = state_idx; a.cu_seqlens = cu_seqlens;
     a.o = o; a.h_T = h_T; a.h_chunks = h_chunks; a.T = T; a.H = H; a.n_seq = n_seq; a.P = P;
     a.scale = scale;
-    const hipError_t e = dtype == KDA_BF16 ? kda::launch_fwd_bf16(a, dk, dv, stream)
+    const long long rows = chunk_rows(B, T, n_seq, cu_seqlens != nullptr);
+    const hipError_t e = dtype == KDA_BF16 ? kda::launch_fwd_bf16(a, dk, dv, workspace, workspace_bytes, rows, stream)
                                            : kda::launch_fwd_f32(a, dk, dv, stream);
     if (e == hipErrorInvalidValue) return KDA_ERR_UNSUPPORTED;
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n_seq, int packed)
+{
+    if (B < 0 || T < 0 || H <= 0 || n_seq < 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128)) return 0;
+    return kda::fwd_workspace_bytes(dk, chunk_rows(B, T, n_seq, packed != 0), H);
 }
 
 int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw,
                   const void *beta_raw, const float *A_log, const float *dt_bias,
                   const float *h0, const int32_t *cu_seqlens, int chunk, void *o, float *h_T,
                   int B, int T, int H, int dk, int dv, int n_seq, float scale,
-                  kda_dtype dtype, hipStream_t stream)
+                  kda_dtype dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
-                          h_T, nullptr, B, T, H, dk, dv, n_seq, 0, scale, dtype, stream);
+                          h_T, nullptr, B, T, H, dk, dv, n_seq, 0, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 int kda_chunk_fwd_states(const void *q, const void *k, const void *v, const void *g_raw,
                          const void *beta_raw, const float *A_log, const float *dt_bias,
                          const float *h0, const int32_t *cu_seqlens, int chunk, void *o, float *h_T,
                          float *h_chunks, int B, int T, int H, int dk, int dv, int n_seq, float scale,
-                         kda_dtype dtype, hipStream_t stream)
+                         kda_dtype dtype, void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
     if (n_seq > 0 && T > 0 && !h_chunks) return KDA_ERR_NULL;
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
-                          h_T, h_chunks, B, T, H, dk, dv, n_seq, 0, scale, dtype, stream);
+                          h_T, h_chunks, B, T, H, dk, dv, n_seq, 0, scale, dtype, workspace, workspace_bytes,
+                          stream);
 }
 
 int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *g_raw,
                        const void *beta_raw, const float *A_log, const float *dt_bias,
                        float *state_pool, const int32_t *state_idx, const int32_t *cu_seqlens,
                        int chunk, void *o, int B, int T, int H, int dk, int dv, int n_seq, int P,
-                       float scale, kda_dtype dtype, hipStream_t stream)
+                       float scale, kda_dtype dtype, void *workspace, size_t workspace_bytes,
+                       hipStream_t stream)
 {
     if (P <= 0) return KDA_ERR_SHAPE;
     if (n_seq > 0 && (!state_pool || !state_idx)) return KDA_ERR_NULL;
@@ -131,7 +151,8 @@ int kda_chunk_fwd_pool(const void *q, const void *k, const void *v, const void *
     // the slots double as h0 (read when a sequence starts) and h_T (written when it
     // ends); each (sequence, head, slab) is read and written by the same workgroup
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_idx, cu_seqlens,
-                          chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, P, scale, dtype, stream);
+                          chunk, o, state_pool, nullptr, B, T, H, dk, dv, n_seq, P, scale, dtype, workspace,
+                          workspace_bytes, stream);
 }
 
 int kda_chunk_o(const void *q, const void *k, const void *v, const void *g_raw, const void *beta_raw,

@@ -6,10 +6,14 @@
 //             through a sequential chunk loop inside the block: the sequence
 //             axis stays out of the grid), 6.4.1 (split d_v, never d_k),
 //             6.4.2 (the state advances after the chunk's output).
+//   [LA-06]   "06 · linear 路线（一）：kernel trick、RNN 等价与三种计算形式":
+//             chunkwise form (the state-independent per-chunk terms can be
+//             formed for all chunks in parallel ahead of the recurrence).
 //   [FKDA-LM] "FlashKDA 里的 L 矩阵和 Mqk 矩阵是什么": "30秒速览" (U, output and
 //             state advance), "L 矩阵的构造" (strictly lower, rows scaled by
 //             beta), "Mqk 矩阵的构造" (lower including the diagonal), "为什么
-//             CHUNK16" (L^16 = 0; inverse by Neumann squaring), "K2 内核如何消费".
+//             CHUNK16" (L^16 = 0; inverse by Neumann squaring), "K2 内核如何消费"
+//             (a prep step and a recurrence step that consumes its operands).
 //   [SGL-PR]  "SGLang PR #26586 (KDA packed decode)": gate and beta formulas.
 //
 // Per chunk of C = 16 tokens of one (sequence, head), with G the chunk-local
@@ -25,25 +29,33 @@
 // Sign of L: the recurrence gives (I + A) U = u with A_ij = beta_i <k~_i, k_j e^{-G_j}>,
 // so L := -A (the page prints the series both ways).
 //
-// Work split on MI355X.  One workgroup owns one (sequence, head, d_v column
-// group) for the whole sequence: no other workgroup and no device memory
-// besides the inputs and outputs is involved.  Its waves have two roles:
-//   * NPW = d_k / 32 PREP waves build everything that does not depend on the
-//     state, in three pipelined stages, each chunk's stages in successive
-//     iterations of the chunk loop:
-//       A (chunk it+3, all prep waves): gate, cumulative gate, decayed
-//         operands, this wave's 32-channel partials of L, L^T and Mqk^T on the
-//         matrix core, layout transposes of k~, k^r and v (below);
-//       B1 (chunk it+2, wave 0): sums the partials, applies masks and beta,
-//         INV by Neumann squaring, INV beta;
-//       B2 (chunk it+1, the other prep waves): w and u' on the matrix core;
-//   * NCW CONSUMER waves, each owning SPW slabs of 16 state columns in fp32
-//     MFMA accumulators, run the recurrence for chunk it:
-//       W' = w S, Qs^T = S^T q~^T, decay, U = u' - W', O^T = Qs^T + U^T Mqk^T,
-//       S += k^r^T U.
-//   The stages hand over through LDS; one workgroup barrier per chunk.
-//   A chain whose columns are split over G groups repeats the prep in each
-//   group (used when the chains are fewer than the compute units).
+// Everything that does not depend on the state (the "prep") is built by prep
+// waves in three stages per chunk:
+//   A  (NPW = d_k / 32 waves, one 32-channel block each): gate, cumulative gate,
+//      decayed operands, this block's partials of L, L^T and Mqk^T on the
+//      matrix core, layout copies of k~, k^r (and v);
+//   B1 (one wave): sums the partials, masks, beta, INV by Neumann squaring, INV beta;
+//   B2 (stage-A waves 1 ..): w (and u') on the matrix core.
+// The recurrence runs in consumer waves, each owning slabs of 16 state columns
+// in fp32 MFMA accumulators:
+//   W' = w S, Qs^T = S^T q~^T, decay, U = u' - W', O^T = Qs^T + U^T Mqk^T, S += k^r^T U.
+//
+// Two ways to run it (the launcher picks by the number of (sequence, head)
+// chains against the compute units, and by the caller's workspace):
+//   * ONE PASS (fwd_kernel): one workgroup per (sequence, head, column group)
+//     holds prep and consumer waves; the three prep stages of successive
+//     chunks run three iterations ahead of the consumers and hand over through
+//     LDS, one barrier per chunk.  No memory besides the arguments.  A chain
+//     split over G column groups repeats the prep in each group, so this is
+//     the form for many chains.
+//   * TWO PASSES (prep_kernel, then rec_kernel), for chains fewer than the
+//     compute units: every chunk's prep runs once, all chunks in parallel, and
+//     its consumer operands (q~, w, k^r, e^{G_C}, Mqk^T, INV beta; 13.5 KiB
+//     per chunk and head at d_k = 128) go to the caller's workspace; then one
+//     single-wave workgroup per (sequence, head, 16 columns) walks the chunks,
+//     prefetching the next chunk's operands straight into registers, forming
+//     u' = INV beta v from its own columns of v and running the recurrence.
+//     No workgroup waits on another in either pass.
 //
 // Operand layouts.  For a 16 x 16 tile X the "C layout" is the MFMA
 // accumulator layout: lane (lq, ln) = (lane / 16, lane % 16) holds
@@ -143,43 +155,54 @@ __device__ __forceinline__ void lds_barrier() {   // LDS-only barrier: global lo
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+__device__ __forceinline__ void vm_wait_all() {   // all of this wave's global loads have landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
+    asm volatile("" ::: "memory");
+}
 
 // Channel of row 4 lq + i of state tile m (and of the matching rows of every
 // C-layout channel tile): the 8 K values a lane feeds to a 16x16x32 MFMA in K
 // block s are then the 8 consecutive channels 32 s + 8 lq .. +7.
 __device__ __forceinline__ constexpr int chan(int m, int lq, int i) { return 32 * (m >> 1) + 8 * lq + 4 * (m & 1) + i; }
 
+// Consumer operands of one chunk (a workspace row of the two-pass form; the
+// one-pass form keeps the same pieces in LDS): byte offsets.
+template <int DK>
+struct Pay {
+    static constexpr int NKB = DK / 32, NMT = DK / 16;
+    static constexpr int QF = 0;                    // q~ B fragments   [NKB][64] x 16 B
+    static constexpr int WF = QF + NKB * 1024;      // w A fragments    [NKB][64] x 16 B
+    static constexpr int KR = WF + NKB * 1024;      // k^r C tiles      [NMT][64] x 8 B (bf16)
+    static constexpr int EG = KR + NMT * 512;       // e^{G_C}          [DK] fp32
+    static constexpr int MQ = EG + DK * 4;          // Mqk^T C tile     [64] x 8 B (bf16)
+    static constexpr int IB = MQ + 512;             // (INV beta)^T C tile [64] x 8 B (bf16)
+    static constexpr int BYTES = IB + 512;
+};
+
 template <int DK, int DV, int NCW, int SPW>
 struct Lay {
-    static constexpr int NPW = DK / 32;           // prep waves (one 32-channel block each)
+    using P = Pay<DK>;
+    static constexpr int NPW = DK / 32;           // stage-A waves (one 32-channel block each)
     static constexpr int NKB = DK / 32;           // K blocks of the state products
     static constexpr int NMT = DK / 16;           // state row tiles
     static constexpr int NCOL = NCW * SPW * 16;   // columns of the group
     static constexpr int G = DV / NCOL;           // column groups per chain
     static constexpr int NVT = NCOL / 16;         // 16-column tiles of the group
     static constexpr int NVB = (NCOL + 31) / 32;  // 32-column v blocks
-    static constexpr int VPW = (NVB + NPW - 1) / NPW;   // v blocks per prep wave
-    static constexpr int NW = NPW + NCW;
+    static constexpr int VPW = (NVB + NPW - 1) / NPW;   // v blocks per stage-A wave
+    static constexpr int NW = NPW + 1 + NCW;       // stage-A waves, the INV wave, consumers
     static constexpr int NTHR = 64 * NW;
-    // per chunk, read by the consumers (4 buffers: written 3 iterations ahead)
-    static constexpr int QF = 0;                    // q~ B fragments   [NKB][64] x 16 B
-    static constexpr int KR = QF + NKB * 1024;      // k^r C tiles      [NMT][64] x 8 B (bf16)
-    static constexpr int EG = KR + NMT * 512;       // e^{G_C}          [DK] fp32
-    static constexpr int MQ = EG + DK * 4;          // Mqk^T C tile     [64] x 8 B (bf16)
-    static constexpr int QKE = MQ + 512;
-    static constexpr int WF = 0;                    // w A fragments    [NKB][64] x 16 B   (2 buffers)
-    static constexpr int UP = WF + NKB * 1024;      // u' C tiles       [NVT][64] x 16 B (fp32)
-    static constexpr int WUM = UP + NVT * 1024;
-    static constexpr int KT = 0;                    // k~ C tiles       [NMT][64] x 8 B    (3 buffers)
-    static constexpr int VT = KT + NMT * 512;       // v C tiles        [NVT][64] x 8 B
+    static constexpr int PAY = P::BYTES;          // consumer operands (4 buffers: written from 3 iterations ahead)
+    static constexpr int UP = NVT * 1024;         // u' C tiles [NVT][64] x 16 B fp32 (2 buffers)
+    static constexpr int KT = 0;                  // k~ C tiles [NMT][64] x 8 B  (3 buffers)
+    static constexpr int VT = KT + NMT * 512;     // v C tiles  [NVT][64] x 8 B
     static constexpr int KV = VT + NVT * 512;
-    static constexpr int PART = NPW * 3 * 1024;     // per prep wave: L, L^T, Mqk^T partials (2 buffers)
-    static constexpr int O_QKE = 0;
-    static constexpr int O_WUM = O_QKE + 4 * QKE;
-    static constexpr int O_KV = O_WUM + 2 * WUM;
+    static constexpr int PART = NPW * 3 * 1024;   // per stage-A wave: L, L^T, Mqk^T partials (2 buffers)
+    static constexpr int O_PAY = 0;
+    static constexpr int O_UP = O_PAY + 4 * PAY;
+    static constexpr int O_KV = O_UP + 2 * UP;
     static constexpr int O_PART = O_KV + 3 * KV;
-    static constexpr int O_INVB = O_PART + 2 * PART;   // C layout of (INV beta)^T, bf16  (2 buffers)
-    static constexpr int O_BETA = O_INVB + 2 * 512;    // beta [16]                         (2 buffers)
+    static constexpr int O_BETA = O_PART + 2 * PART;   // beta [16] (2 buffers)
     static constexpr int O_SEQ = O_BETA + 2 * 64;      // the sequence this workgroup takes
     static constexpr int BYTES = O_SEQ + 16;
     static_assert(DK == 64 || DK == 128, "d_k");
@@ -190,26 +213,351 @@ struct Lay {
 // Packed sequences with at most this many entries are taken longest first.
 constexpr int LPT_MAX = 128;
 
-// Inputs of one chunk as a prep lane holds them: token t = lane % 16, the
+// Inputs of one chunk as a stage-A lane holds them: token t = lane % 16, the
 // 8 channels 32 w + 8 (lane / 16) .. +7 of q, k, g_raw; v blocks; beta_raw.
 template <int VPW>
 struct In {
     uint4 k, q, a;
-    uint4 v[VPW];
+    uint4 v[VPW > 0 ? VPW : 1];
     uint16_t b;
 };
+
+// ------------------------------------------------------------------ prep
+// One stage-A wave: its 32-channel block, its constants, its loads and stage A.
+template <int DK, int VPW>
+struct Prep {
+    static constexpr int NPW = DK / 32;
+    int w, t, r, lane, ln, lq;
+    float A_exp, dtl[8];
+    bf16x8 sel_c[2], sel_v[2];
+
+    __device__ __forceinline__ void init(const FwdArgs &a, int head, int wave, int lane_) {
+        w = wave;
+        lane = lane_;
+        ln = lane & 15;
+        lq = lane >> 4;
+        t = ln;
+        r = lq;
+        A_exp = expf(a.A_log[head]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dtl[e] = a.dt_bias[(size_t)head * DK + 32 * w + 8 * r + e] * kLog2e;
+        // 0/1 selectors: C-layout copies of row-loaded tiles (the channels of
+        // state tile 2w + h; columns 16 (2 vb + h) .. + 15 of a v block)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sel_c[h][e] = static_cast<__bf16>((lq == (ln >> 2) && e == 4 * h + (ln & 3)) ? 1.f : 0.f);
+                sel_v[h][e] = static_cast<__bf16>((lq == 2 * h + (ln >> 3) && e == (ln & 7)) ? 1.f : 0.f);
+            }
+    }
+
+    // Loads of chunk x of the sequence starting at token bos with len tokens
+    // (x < ceil(len / 16)); v blocks vb = w, w + NPW, ... (< nvb) of the
+    // columns col0 .. col0 + ncol of a row of dv columns.
+    __device__ __forceinline__ void load(In<VPW> &in, const FwdArgs &a, size_t bos, int len, int x, int head,
+                                         int dv, int col0, int ncol, int nvb) const {
+        const size_t H = a.H;
+        const int rem = min(CH, len - x * CH);
+        const size_t tok = bos + (size_t)x * CH + min(t, rem - 1);   // rows past the end repeat the last live row
+        const size_t off = (tok * H + head) * DK + 32 * w + 8 * r;
+        in.k = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + off);
+        in.q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + off);
+        in.a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.g_raw) + off);
+#pragma unroll
+        for (int i = 0; i < VPW; ++i) {
+            const int vb = w + NPW * i;
+            if (vb < nvb && 32 * vb + 8 * r < ncol)
+                in.v[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) +
+                                                           (tok * H + head) * dv + col0 + 32 * vb + 8 * r);
+            else
+                in.v[i] = uint4{0u, 0u, 0u, 0u};
+        }
+        in.b = (w == 0) ? static_cast<const uint16_t *>(a.beta_raw)[tok * H + head] : (uint16_t)0;
+    }
+
+    // Stage A of a chunk with `rem` live tokens.  Writes q~ fragments (qf),
+    // e^{G_C} (eg), k^r C tiles (kr), k~ C tiles (kt), v C tiles (vt, nvt
+    // tiles of nvb blocks; none if vt is NULL), this wave's L / L^T / Mqk^T
+    // partials (part) and, from wave 0, beta (beta).
+    __device__ __forceinline__ void stage_a(const In<VPW> &in, int rem, unsigned char *qf, float *eg,
+                                            unsigned char *kr, unsigned char *kt, unsigned char *vt, int nvb, int nvt,
+                                            f32x4 *part, float *beta) const {
+        const bool live = t < rem;
+        const float nA = live ? -A_exp : 0.f;
+        float kf[8], qfv[8], gv[8], Gm[8], GC[8], e1[8], kd[8], qd[8], krv[8];
+        const uint32_t kw[4] = {in.k.x, in.k.y, in.k.z, in.k.w};
+        const uint32_t qw[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
+        const uint32_t aw[4] = {in.a.x, in.a.y, in.a.z, in.a.w};
+        bool deep = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int sh = (e & 1) ? 0 : 16;
+            const uint32_t mk = (e & 1) ? 0xffff0000u : 0xffffffffu;
+            kf[e] = live ? __builtin_bit_cast(float, (kw[e >> 1] << sh) & mk) : 0.f;
+            qfv[e] = live ? __builtin_bit_cast(float, (qw[e >> 1] << sh) & mk) : 0.f;
+            const float af = __builtin_bit_cast(float, (aw[e >> 1] << sh) & mk);
+            const float y = __builtin_fmaf(af, kLog2e, dtl[e]);        // (a + dt_bias) log2 e
+            const float sp = y > 20.0f * kLog2e ? y : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(y));
+            gv[e] = nA * sp;                                            // gate, log2 units; pads do not decay
+            Gm[e] = scan16(gv[e]);
+            GC[e] = row_bcast<15>(Gm[e]);
+            deep |= GC[e] < -100.f;
+            e1[e] = __builtin_amdgcn_exp2f(Gm[e]);
+            kd[e] = kf[e] * e1[e];
+            qd[e] = qfv[e] * e1[e];
+        }
+        const bf16x8 bkd = pack8(kd), bqd = pack8(qd);
+        f32x4 pL, pLT, pMT;
+        if (__ballot(deep) == 0) {
+            // mild: rows k~ (<= 1), columns k 2^-G (<= 2^100); k^r = k 2^-G 2^{G_C}
+            float kh[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                kh[e] = kf[e] * __builtin_amdgcn_exp2f(-Gm[e]);
+                krv[e] = kh[e] * row_bcast<15>(e1[e]);
+            }
+            const bf16x8 bkh = pack8(kh);
+            pL = mma32(bkd, bkh, Z4);
+            pLT = mma32(bkh, bkd, Z4);
+            pMT = mma32(bkh, bqd, Z4);
+        } else {
+            // strong: two 8-token row blocks, each token's decay clipped at 2^-12
+            constexpr float CLIP = 12.f;
+            float Gp[8], Bf1[8], R[8], Rq[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                krv[e] = kf[e] * __builtin_amdgcn_exp2f(GC[e] - Gm[e]);
+                Gp[e] = scan16(fmaxf(gv[e], -CLIP));
+                Bf1[e] = row_bcast<7>(Gp[e]);
+                const float f = __builtin_amdgcn_exp2f(Gp[e] - (t >= 8 ? Bf1[e] : 0.f));   // <= 1
+                R[e] = kf[e] * f;
+                Rq[e] = qfv[e] * f;
+            }
+            const bf16x8 bR = pack8(R), bRq = pack8(Rq);
+            pL = pLT = pMT = Z4;
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                float Cc[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    Cc[e] = t < 8 * (bb + 1) ? kf[e] * __builtin_amdgcn_exp2f((bb ? Bf1[e] : 0.f) - Gp[e]) : 0.f;
+                const bf16x8 bC = pack8(Cc);
+                const f32x4 Lb = mma32(bR, bC, Z4), LTb = mma32(bC, bR, Z4), MTb = mma32(bC, bRq, Z4);
+                if ((4 * r) / 8 == bb) pL = Lb;          // C-layout rows 4r .. 4r+3 of L lie in block bb
+                if (t / 8 == bb) { pLT = LTb; pMT = MTb; }   // row t of L (as column t of L^T), of Mqk
+            }
+        }
+        const bf16x8 bkr = pack8(krv);
+        *reinterpret_cast<bf16x8 *>(qf + (w * 64 + lane) * 16) = bqd;
+        if (t == CH - 1) {
+            float *egw = eg + 32 * w + 8 * r;
+            *reinterpret_cast<f32x4 *>(egw) = f32x4{e1[0], e1[1], e1[2], e1[3]};
+            *reinterpret_cast<f32x4 *>(egw + 4) = f32x4{e1[4], e1[5], e1[6], e1[7]};
+        }
+        f32x4 *pp = part + (w * 3) * 64 + lane;
+        pp[0] = pL;
+        pp[64] = pLT;
+        pp[128] = pMT;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int m = 2 * w + h;
+            *reinterpret_cast<bf16x4 *>(kt + (m * 64 + lane) * 8) = pack4(mma32(bkd, sel_c[h], Z4));
+            *reinterpret_cast<bf16x4 *>(kr + (m * 64 + lane) * 8) = pack4(mma32(bkr, sel_c[h], Z4));
+        }
+        if (vt) {
+#pragma unroll
+            for (int i = 0; i < VPW; ++i) {
+                const int vb = w + NPW * i;
+                if (vb < nvb) {
+                    const bf16x8 bv = __builtin_bit_cast(bf16x8, in.v[i]);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int n = 2 * vb + h;
+                        if (n < nvt)
+                            *reinterpret_cast<bf16x4 *>(vt + (n * 64 + lane) * 8) = pack4(mma32(bv, sel_v[h], Z4));
+                    }
+                }
+            }
+        }
+        if (w == 0 && r == 0) beta[t] = live ? sigmoid_f(bf16_to_f32(in.b)) : 0.f;
+    }
+};
+
+// Stage B1 (one wave): L, L^T, Mqk^T from the NPW partials; INV; writes the
+// C layout of (INV beta)^T (bf16) to ib and of Mqk^T (bf16) to mq.
+template <int NPW>
+__device__ __forceinline__ void stage_b1(const f32x4 *part, const float *beta, unsigned char *ib, unsigned char *mq,
+                                         int lane) {
+    const int ln = lane & 15, lq = lane >> 4;
+    const f32x4 *pp = part + lane;
+    f32x4 Lm = Z4, LT = Z4, MT = Z4;
+#pragma unroll
+    for (int ww = 0; ww < NPW; ++ww) {
+        Lm += pp[ww * 192];
+        LT += pp[ww * 192 + 64];
+        MT += pp[ww * 192 + 128];
+    }
+    const f32x4 brow = *reinterpret_cast<const f32x4 *>(beta + 4 * lq);
+    const float bcol = beta[ln];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * lq + i;
+        Lm[i] = row > ln ? -brow[i] * Lm[i] : 0.f;   // L[row][ln], strictly lower
+        LT[i] = ln > row ? -bcol * LT[i] : 0.f;      // L[ln][row]
+        MT[i] = ln >= row ? MT[i] : 0.f;             // Mqk[ln][row], lower including the diagonal
+    }
+    const f32x4 L2 = prod(LT, Lm), L2T = prod(Lm, LT);
+    const f32x4 L4 = prod(L2T, L2), L4T = prod(L2, L2T);
+    const f32x4 L8 = prod(L4T, L4);
+    // P1^T = ((I + L)(I + L^2))^T,  P2 = (I + L^4)(I + L^8),  INV^T = P2^T P1^T
+    const f32x4 P1T = prod(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
+    const f32x4 P2 = prod(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
+    const f32x4 IT = prod(P2, P1T);
+    *reinterpret_cast<bf16x4 *>(ib + lane * 8) = pack4(IT * brow);
+    *reinterpret_cast<bf16x4 *>(mq + lane * 8) = pack4(MT);
+}
+
+// w = INV beta k~ for K block s: the A fragment of W' = w S (from the C tiles
+// 2s, 2s+1 of k~ and the C layout of (INV beta)^T).
+__device__ __forceinline__ bf16x8 w_frag(const unsigned char *kt, bf16x4 ib, int s, int lane) {
+    const bf16x4 k0 = *reinterpret_cast<const bf16x4 *>(kt + ((2 * s) * 64 + lane) * 8);
+    const bf16x4 k1 = *reinterpret_cast<const bf16x4 *>(kt + ((2 * s + 1) * 64 + lane) * 8);
+    return cat4(pack4(mma16(k0, ib, Z4)), pack4(mma16(k1, ib, Z4)));
+}
+
+// One chunk of the recurrence for SPW slabs of 16 columns: S holds the state
+// entering the chunk and leaves with the state after it; O gets O^T / scale.
+template <int NKB, int NMT, int SPW>
+__device__ __forceinline__ void rec_step(f32x4 (&S)[SPW][NMT], const bf16x8 (&qf)[NKB], const bf16x8 (&wf)[NKB],
+                                         const bf16x4 (&kr)[NMT], const f32x4 (&eg)[NMT], bf16x4 mq,
+                                         const f32x4 (&up)[SPW], f32x4 (&O)[SPW]) {
+    // the state entering the chunk, as bf16 K fragments (B of W' = w S, A of Qs^T = S^T q~^T)
+    bf16x8 bS[SPW][NKB];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int s = 0; s < NKB; ++s) bS[j][s] = cat4(pack4(S[j][2 * s]), pack4(S[j][2 * s + 1]));
+    f32x4 W[SPW], Qs[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) { W[j] = Z4; Qs[j] = Z4; }
+#pragma unroll
+    for (int s = 0; s < NKB; ++s)
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            W[j] = mma32(wf[s], bS[j][s], W[j]);
+            Qs[j] = mma32(bS[j][s], qf[s], Qs[j]);
+        }
+    // decay the fp32 state: S <- Diag(e^{G_C}) S
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) S[j][m] *= eg[m];
+    const bf16x8 bmq = cat4(mq, mq);
+    bf16x8 bU[SPW];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j) {
+        bU[j] = hilo(up[j] - W[j]);            // U = u' - w S as [hi | lo]
+        O[j] = mma32(bU[j], bmq, Qs[j]);       // O^T = Qs^T + U^T Mqk^T
+    }
+    // S += k^r^T U (the k^r values repeated for the hi and lo halves of U)
+#pragma unroll
+    for (int m = 0; m < NMT; ++m) {
+        const bf16x8 bkr = cat4(kr[m], kr[m]);
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) S[j][m] = mma32(bkr, bU[j], S[j][m]);
+    }
+}
+
+// O^T in C layout: lane (lq, ln) holds columns 4 lq .. +3 of token ln.
+__device__ __forceinline__ void store_o(void *o, size_t row, size_t H, int head, int dv, int col, f32x4 O,
+                                        float scale) {
+    uint2 v2;
+    v2.x = pack_bf16x2(scale * O[0], scale * O[1]);
+    v2.y = pack_bf16x2(scale * O[2], scale * O[3]);
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(o) + (row * H + head) * dv + col) = v2;
+}
 
 struct Chain {
     size_t bos;
     int len, nch, seq, head, hrow;
 };
+// Sequence `seq`, head `head`: token range, chunk count and state row (a
+// pool slot >= P is reported and treated as none).
+__device__ __forceinline__ Chain chain_of(const FwdArgs &a, int seq, int head, bool report) {
+    Chain c;
+    c.seq = seq;
+    c.head = head;
+    if (a.cu_seqlens) {
+        c.bos = (size_t)a.cu_seqlens[seq];
+        c.len = a.cu_seqlens[seq + 1] - a.cu_seqlens[seq];
+    } else {
+        c.bos = (size_t)seq * a.T;
+        c.len = a.T;
+    }
+    c.nch = (c.len + CH - 1) / CH;
+    c.hrow = a.state_idx ? a.state_idx[seq] : seq;
+    if (a.state_idx && c.hrow >= a.P) {
+        if (report) slot_error(a.err);
+        c.hrow = -1;
+    }
+    return c;
+}
+// Chunks of the sequences before `seq` (the row of its first chunk in the
+// chunk-indexed arrays).
+__device__ __forceinline__ size_t chunk_base(const FwdArgs &a, int seq) {
+    if (!a.cu_seqlens) return (size_t)seq * ((a.T + CH - 1) / CH);
+    size_t b = 0;
+    for (int s2 = 0; s2 < seq; ++s2) b += (size_t)((a.cu_seqlens[s2 + 1] - a.cu_seqlens[s2] + CH - 1) / CH);
+    return b;
+}
+
+// Chunk row `row` of the concatenated chunk rows (sequence 0's chunks, then
+// sequence 1's, ...): its sequence, chunk, first token and length; seq =
+// n_seq past the last row.
+struct RowPos {
+    size_t bos;
+    int seq, x, len;
+};
+__device__ __forceinline__ RowPos row_pos(const FwdArgs &a, long long row) {
+    RowPos p;
+    p.x = 0;
+    p.bos = 0;
+    p.len = 0;
+    if (!a.cu_seqlens) {
+        const int nch = (a.T + CH - 1) / CH;
+        p.seq = nch > 0 ? (int)(row / nch) : a.n_seq;
+        if (p.seq < a.n_seq) {
+            p.x = (int)(row - (long long)p.seq * nch);
+            p.bos = (size_t)p.seq * a.T;
+            p.len = a.T;
+        } else {
+            p.seq = a.n_seq;
+        }
+        return p;
+    }
+    for (p.seq = 0; p.seq < a.n_seq; ++p.seq) {
+        const int len = a.cu_seqlens[p.seq + 1] - a.cu_seqlens[p.seq];
+        const int nch = (len + CH - 1) / CH;
+        if (row < nch) {
+            p.x = (int)row;
+            p.bos = (size_t)a.cu_seqlens[p.seq];
+            p.len = len;
+            return p;
+        }
+        row -= nch;
+    }
+    return p;
+}
 
 }  // namespace
 
+// =========================================================== one pass
 template <int DK, int DV, int NCW, int SPW, bool SNAP>
-__global__ __launch_bounds__(64 * (DK / 32 + NCW)) void fwd_kernel(FwdArgs a)
+__global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a)
 {
     using L = Lay<DK, DV, NCW, SPW>;
+    using P = Pay<DK>;
     constexpr int NPW = L::NPW, NKB = L::NKB, NMT = L::NMT, NVT = L::NVT, NVB = L::NVB, VPW = L::VPW;
     __shared__ __attribute__((aligned(16))) unsigned char lds[L::BYTES];
 
@@ -221,38 +569,23 @@ __global__ __launch_bounds__(64 * (DK / 32 + NCW)) void fwd_kernel(FwdArgs a)
     const int col0 = group * L::NCOL;
 
     // ---- which (sequence, head): heads inner; packed sequences longest first
-    Chain c;
-    c.head = slot % a.H;
     const int rank = slot / a.H;
+    int seq = rank;
     if (a.cu_seqlens && a.n_seq <= LPT_MAX) {
         int *sseq = reinterpret_cast<int *>(lds + L::O_SEQ);
         for (int s = tid; s < a.n_seq; s += L::NTHR) {
             const int ls = a.cu_seqlens[s + 1] - a.cu_seqlens[s];
-            int r = 0;
+            int rk = 0;
             for (int s2 = 0; s2 < a.n_seq; ++s2) {
                 const int l2 = a.cu_seqlens[s2 + 1] - a.cu_seqlens[s2];
-                r += (l2 > ls) || (l2 == ls && s2 < s);
+                rk += (l2 > ls) || (l2 == ls && s2 < s);
             }
-            if (r == rank) *sseq = s;
+            if (rk == rank) *sseq = s;
         }
         lds_barrier();
-        c.seq = __builtin_amdgcn_readfirstlane(*sseq);
-    } else {
-        c.seq = rank;
+        seq = __builtin_amdgcn_readfirstlane(*sseq);
     }
-    if (a.cu_seqlens) {
-        c.bos = (size_t)a.cu_seqlens[c.seq];
-        c.len = a.cu_seqlens[c.seq + 1] - a.cu_seqlens[c.seq];
-    } else {
-        c.bos = (size_t)c.seq * a.T;
-        c.len = a.T;
-    }
-    c.nch = (c.len + CH - 1) / CH;
-    c.hrow = a.state_idx ? a.state_idx[c.seq] : c.seq;
-    if (a.state_idx && c.hrow >= a.P) {   // out-of-range slot: start from zero, keep no state, report
-        if (tid == 0) slot_error(a.err);
-        c.hrow = -1;
-    }
+    const Chain c = chain_of(a, seq, slot % a.H, tid == 0);
     const size_t H = a.H;
     const size_t hbase = (((size_t)(c.hrow < 0 ? 0 : c.hrow) * H + c.head) * DV + col0) * DK;
 
@@ -263,9 +596,9 @@ __global__ __launch_bounds__(64 * (DK / 32 + NCW)) void fwd_kernel(FwdArgs a)
         return;
     }
 
-    if (wv >= NPW) {
+    if (wv > NPW) {
         // ======================================================= consumer
-        const int cw = wv - NPW;
+        const int cw = wv - NPW - 1;
         f32x4 S[SPW][NMT];
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
@@ -278,27 +611,12 @@ __global__ __launch_bounds__(64 * (DK / 32 + NCW)) void fwd_kernel(FwdArgs a)
                     S[j][m] = Z4;
             }
         }
-        size_t cbase = 0;   // h_chunks row of the sequence's first chunk
-        if (SNAP) {
-            if (a.cu_seqlens) {
-                for (int s2 = 0; s2 < c.seq; ++s2)
-                    cbase += (size_t)((a.cu_seqlens[s2 + 1] - a.cu_seqlens[s2] + CH - 1) / CH);
-            } else {
-                cbase = (size_t)c.seq * ((a.T + CH - 1) / CH);
-            }
-        }
-        const float scale = a.scale;
+        const size_t cbase = SNAP ? chunk_base(a, c.seq) : 0;
         for (int it = -3; it < c.nch; ++it) {
             if (it >= 0) {
                 const int x = it;
-                const unsigned char *qke = lds + L::O_QKE + (x & 3) * L::QKE;
-                const unsigned char *wum = lds + L::O_WUM + (x & 1) * L::WUM;
-                // the state entering the chunk, as bf16 K fragments (B of W' = w S, A of Qs^T = S^T q~^T)
-                bf16x8 bS[SPW][NKB];
-#pragma unroll
-                for (int j = 0; j < SPW; ++j)
-#pragma unroll
-                    for (int s = 0; s < NKB; ++s) bS[j][s] = cat4(pack4(S[j][2 * s]), pack4(S[j][2 * s + 1]));
+                const unsigned char *pay = lds + L::O_PAY + (x & 3) * L::PAY;
+                const unsigned char *ups = lds + L::O_UP + (x & 1) * L::UP;
                 if constexpr (SNAP) {
                     const size_t at = (((cbase + x) * H + c.head) * DV + col0) * DK;
 #pragma unroll
@@ -310,52 +628,30 @@ __global__ __launch_bounds__(64 * (DK / 32 + NCW)) void fwd_kernel(FwdArgs a)
                                 a.h_chunks + at + (size_t)(16 * n + ln) * DK + chan(m, lq, 0)));
                     }
                 }
-                f32x4 W[SPW], Qs[SPW];
-#pragma unroll
-                for (int j = 0; j < SPW; ++j) { W[j] = Z4; Qs[j] = Z4; }
+                bf16x8 qf[NKB], wf[NKB];
+                bf16x4 kr[NMT];
+                f32x4 eg[NMT], up[SPW], O[SPW];
 #pragma unroll
                 for (int s = 0; s < NKB; ++s) {
-                    const bf16x8 wf = *reinterpret_cast<const bf16x8 *>(wum + L::WF + (s * 64 + lane) * 16);
-                    const bf16x8 qf = *reinterpret_cast<const bf16x8 *>(qke + L::QF + (s * 64 + lane) * 16);
-#pragma unroll
-                    for (int j = 0; j < SPW; ++j) {
-                        W[j] = mma32(wf, bS[j][s], W[j]);
-                        Qs[j] = mma32(bS[j][s], qf, Qs[j]);
-                    }
+                    wf[s] = *reinterpret_cast<const bf16x8 *>(pay + P::WF + (s * 64 + lane) * 16);
+                    qf[s] = *reinterpret_cast<const bf16x8 *>(pay + P::QF + (s * 64 + lane) * 16);
                 }
-                // decay the fp32 state: S <- Diag(e^{G_C}) S
 #pragma unroll
                 for (int m = 0; m < NMT; ++m) {
-                    const f32x4 eg = *reinterpret_cast<const f32x4 *>(qke + L::EG + chan(m, lq, 0) * 4);
-#pragma unroll
-                    for (int j = 0; j < SPW; ++j) S[j][m] *= eg;
+                    eg[m] = *reinterpret_cast<const f32x4 *>(pay + P::EG + chan(m, lq, 0) * 4);
+                    kr[m] = *reinterpret_cast<const bf16x4 *>(pay + P::KR + (m * 64 + lane) * 8);
                 }
-                const bf16x4 mq = *reinterpret_cast<const bf16x4 *>(qke + L::MQ + lane * 8);
-                const bf16x8 bmq = cat4(mq, mq);
+                const bf16x4 mq = *reinterpret_cast<const bf16x4 *>(pay + P::MQ + lane * 8);
+#pragma unroll
+                for (int j = 0; j < SPW; ++j)
+                    up[j] = *reinterpret_cast<const f32x4 *>(ups + ((cw * SPW + j) * 64 + lane) * 16);
+                rec_step<NKB, NMT, SPW>(S, qf, wf, kr, eg, mq, up, O);
                 const int rem = min(CH, c.len - x * CH);
-                bf16x8 bU[SPW];
+                if (ln < rem) {
 #pragma unroll
-                for (int j = 0; j < SPW; ++j) {
-                    const int n = cw * SPW + j;
-                    const f32x4 up = *reinterpret_cast<const f32x4 *>(wum + L::UP + (n * 64 + lane) * 16);
-                    bU[j] = hilo(up - W[j]);   // U = u' - w S as [hi | lo]
-                    // O^T = Qs^T + U^T Mqk^T; lane: 4 consecutive columns of token ln
-                    const f32x4 O = mma32(bU[j], bmq, Qs[j]);
-                    if (ln < rem) {
-                        uint2 v2;
-                        v2.x = pack_bf16x2(scale * O[0], scale * O[1]);
-                        v2.y = pack_bf16x2(scale * O[2], scale * O[3]);
-                        const size_t at = ((c.bos + (size_t)x * CH + ln) * H + c.head) * DV + col0 + 16 * n + 4 * lq;
-                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.o) + at) = v2;
-                    }
-                }
-                // S += k^r^T U (the k^r values repeated for the hi and lo halves of U)
-#pragma unroll
-                for (int m = 0; m < NMT; ++m) {
-                    const bf16x4 kr = *reinterpret_cast<const bf16x4 *>(qke + L::KR + (m * 64 + lane) * 8);
-                    const bf16x8 bkr = cat4(kr, kr);
-#pragma unroll
-                    for (int j = 0; j < SPW; ++j) S[j][m] = mma32(bkr, bU[j], S[j][m]);
+                    for (int j = 0; j < SPW; ++j)
+                        store_o(a.o, c.bos + (size_t)x * CH + ln, H, c.head, DV, col0 + 16 * (cw * SPW + j) + 4 * lq,
+                                O[j], a.scale);
                 }
             }
             lds_barrier();
@@ -373,216 +669,250 @@ __global__ __launch_bounds__(64 * (DK / 32 + NCW)) void fwd_kernel(FwdArgs a)
     }
 
     // =========================================================== prep
-    const int w = wv;
-    const int t = ln, r = lq;                 // token, 8-channel unit within the wave's 32 channels
-    const float A_exp = expf(a.A_log[c.head]);
-    float dtl[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dtl[e] = a.dt_bias[(size_t)c.head * DK + 32 * w + 8 * r + e] * kLog2e;
-    // 0/1 selectors: C-layout copies of row-loaded tiles (the channels of
-    // state tile 2w + h; columns 16 (2 vb + h) .. + 15 of a v block)
-    bf16x8 sel_c[2], sel_v[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sel_c[h][e] = static_cast<__bf16>((lq == (ln >> 2) && e == 4 * h + (ln & 3)) ? 1.f : 0.f);
-            sel_v[h][e] = static_cast<__bf16>((lq == 2 * h + (ln >> 3) && e == (ln & 7)) ? 1.f : 0.f);
+    auto part = [&](int x) { return reinterpret_cast<f32x4 *>(lds + L::O_PART + (x & 1) * L::PART); };
+    auto beta = [&](int x) { return reinterpret_cast<float *>(lds + L::O_BETA + (x & 1) * 64); };
+    auto pay = [&](int x) { return lds + L::O_PAY + (x & 3) * L::PAY; };
+    auto kv = [&](int x) { return lds + L::O_KV + (x % 3) * L::KV; };
+    if (wv == NPW) {
+        // the INV wave: stage B1 of chunk it + 2 in iteration it
+        for (int it = -3; it < c.nch; ++it) {
+            const int x = it + 2;
+            if (x >= 0 && x < c.nch) stage_b1<NPW>(part(x), beta(x), pay(x) + P::IB, pay(x) + P::MQ, lane);
+            lds_barrier();
         }
-
-    auto load = [&](In<VPW> &in, int x) {
-        const int rem = min(CH, c.len - x * CH);
-        const size_t tok = c.bos + (size_t)x * CH + min(t, rem - 1);   // rows past the end repeat the last live row
-        const size_t off = (tok * H + c.head) * DK + 32 * w + 8 * r;
-        in.k = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.k) + off);
-        in.q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + off);
-        in.a = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.g_raw) + off);
-#pragma unroll
-        for (int i = 0; i < VPW; ++i) {
-            const int vb = w + NPW * i;
-            if (vb < NVB && 32 * vb + 8 * r < L::NCOL)
-                in.v[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) +
-                                                           (tok * H + c.head) * DV + col0 + 32 * vb + 8 * r);
-            else
-                in.v[i] = uint4{0u, 0u, 0u, 0u};
-        }
-        in.b = (w == 0) ? static_cast<const uint16_t *>(a.beta_raw)[tok * H + c.head] : (uint16_t)0;
-    };
-
-    // ---- stage A: chunk x from the inputs in `in`
-    auto stage_a = [&](const In<VPW> &in, int x) {
-        const int rem = min(CH, c.len - x * CH);
-        const bool live = t < rem;
-        const float nA = live ? -A_exp : 0.f;
-        unsigned char *qke = lds + L::O_QKE + (x & 3) * L::QKE;
-        unsigned char *kv = lds + L::O_KV + (x % 3) * L::KV;
-        float kf[8], qf[8], gv[8], Gm[8], GC[8], e1[8], kd[8], qd[8], kr[8];
-        const uint32_t kw[4] = {in.k.x, in.k.y, in.k.z, in.k.w};
-        const uint32_t qw[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
-        const uint32_t aw[4] = {in.a.x, in.a.y, in.a.z, in.a.w};
-        bool deep = false;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int sh = (e & 1) ? 0 : 16;
-            const uint32_t mk = (e & 1) ? 0xffff0000u : 0xffffffffu;
-            kf[e] = live ? __builtin_bit_cast(float, (kw[e >> 1] << sh) & mk) : 0.f;
-            qf[e] = live ? __builtin_bit_cast(float, (qw[e >> 1] << sh) & mk) : 0.f;
-            const float af = __builtin_bit_cast(float, (aw[e >> 1] << sh) & mk);
-            const float y = __builtin_fmaf(af, kLog2e, dtl[e]);        // (a + dt_bias) log2 e
-            const float sp = y > 20.0f * kLog2e ? y : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(y));
-            gv[e] = nA * sp;                                            // gate, log2 units; pads do not decay
-            Gm[e] = scan16(gv[e]);
-            GC[e] = row_bcast<15>(Gm[e]);
-            deep |= GC[e] < -100.f;
-            e1[e] = __builtin_amdgcn_exp2f(Gm[e]);
-            kd[e] = kf[e] * e1[e];
-            qd[e] = qf[e] * e1[e];
-        }
-        const bf16x8 bkd = pack8(kd), bqd = pack8(qd);
-        f32x4 pL, pLT, pMT;
-        if (__ballot(deep) == 0) {
-            // mild: rows k~ (<= 1), columns k 2^-G (<= 2^100); k^r = k 2^-G 2^{G_C}
-            float kh[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kh[e] = kf[e] * __builtin_amdgcn_exp2f(-Gm[e]);
-                kr[e] = kh[e] * row_bcast<15>(e1[e]);
-            }
-            const bf16x8 bkh = pack8(kh);
-            pL = mma32(bkd, bkh, Z4);
-            pLT = mma32(bkh, bkd, Z4);
-            pMT = mma32(bkh, bqd, Z4);
-        } else {
-            // strong: two 8-token row blocks, each token's decay clipped at 2^-12
-            constexpr float CLIP = 12.f;
-            float Gp[8], Bf1[8], R[8], Rq[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                kr[e] = kf[e] * __builtin_amdgcn_exp2f(GC[e] - Gm[e]);
-                Gp[e] = scan16(fmaxf(gv[e], -CLIP));
-                Bf1[e] = row_bcast<7>(Gp[e]);
-                const float f = __builtin_amdgcn_exp2f(Gp[e] - (t >= 8 ? Bf1[e] : 0.f));   // <= 1
-                R[e] = kf[e] * f;
-                Rq[e] = qf[e] * f;
-            }
-            const bf16x8 bR = pack8(R), bRq = pack8(Rq);
-            pL = pLT = pMT = Z4;
-#pragma unroll
-            for (int bb = 0; bb < 2; ++bb) {
-                float Cc[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    Cc[e] = t < 8 * (bb + 1) ? kf[e] * __builtin_amdgcn_exp2f((bb ? Bf1[e] : 0.f) - Gp[e]) : 0.f;
-                const bf16x8 bC = pack8(Cc);
-                const f32x4 Lb = mma32(bR, bC, Z4), LTb = mma32(bC, bR, Z4), MTb = mma32(bC, bRq, Z4);
-                if ((4 * r) / 8 == bb) pL = Lb;          // C-layout rows 4r .. 4r+3 of L lie in block bb
-                if (t / 8 == bb) { pLT = LTb; pMT = MTb; }   // row t of L (as column t of L^T), of Mqk
-            }
-        }
-        const bf16x8 bkr = pack8(kr);
-        // payload of the consumers: q~ fragments, e^{G_C}, k^r C tiles
-        *reinterpret_cast<bf16x8 *>(qke + L::QF + (w * 64 + lane) * 16) = bqd;
-        if (t == CH - 1) {
-            float *eg = reinterpret_cast<float *>(qke + L::EG) + 32 * w + 8 * r;
-            *reinterpret_cast<f32x4 *>(eg) = f32x4{e1[0], e1[1], e1[2], e1[3]};
-            *reinterpret_cast<f32x4 *>(eg + 4) = f32x4{e1[4], e1[5], e1[6], e1[7]};
-        }
-        f32x4 *pp = reinterpret_cast<f32x4 *>(lds + L::O_PART + (x & 1) * L::PART) + (w * 3) * 64 + lane;
-        pp[0] = pL;
-        pp[64] = pLT;
-        pp[128] = pMT;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int m = 2 * w + h;
-            *reinterpret_cast<bf16x4 *>(kv + L::KT + (m * 64 + lane) * 8) = pack4(mma32(bkd, sel_c[h], Z4));
-            *reinterpret_cast<bf16x4 *>(qke + L::KR + (m * 64 + lane) * 8) = pack4(mma32(bkr, sel_c[h], Z4));
-        }
-#pragma unroll
-        for (int i = 0; i < VPW; ++i) {
-            const int vb = w + NPW * i;
-            if (vb < NVB) {
-                const bf16x8 bv = __builtin_bit_cast(bf16x8, in.v[i]);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int n = 2 * vb + h;
-                    if (n < NVT)
-                        *reinterpret_cast<bf16x4 *>(kv + L::VT + (n * 64 + lane) * 8) = pack4(mma32(bv, sel_v[h], Z4));
-                }
-            }
-        }
-        if (w == 0 && r == 0) {
-            float *bs = reinterpret_cast<float *>(lds + L::O_BETA + (x & 1) * 64);
-            bs[t] = live ? sigmoid_f(bf16_to_f32(in.b)) : 0.f;
-        }
-    };
-
-    // ---- stage B1 (wave 0): L, L^T, Mqk^T from the partials; INV; (INV beta)^T
-    auto stage_b1 = [&](int x) {
-        const f32x4 *pp = reinterpret_cast<const f32x4 *>(lds + L::O_PART + (x & 1) * L::PART) + lane;
-        f32x4 Lm = Z4, LT = Z4, MT = Z4;
-#pragma unroll
-        for (int ww = 0; ww < NPW; ++ww) {
-            Lm += pp[ww * 192];
-            LT += pp[ww * 192 + 64];
-            MT += pp[ww * 192 + 128];
-        }
-        const float *bs = reinterpret_cast<const float *>(lds + L::O_BETA + (x & 1) * 64);
-        const f32x4 brow = *reinterpret_cast<const f32x4 *>(bs + 4 * lq);
-        const float bcol = bs[ln];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 4 * lq + i;
-            Lm[i] = row > ln ? -brow[i] * Lm[i] : 0.f;   // L[row][ln], strictly lower
-            LT[i] = ln > row ? -bcol * LT[i] : 0.f;      // L[ln][row]
-            MT[i] = ln >= row ? MT[i] : 0.f;             // Mqk[ln][row], lower including the diagonal
-        }
-        const f32x4 L2 = prod(LT, Lm), L2T = prod(Lm, LT);
-        const f32x4 L4 = prod(L2T, L2), L4T = prod(L2, L2T);
-        const f32x4 L8 = prod(L4T, L4);
-        // P1^T = ((I + L)(I + L^2))^T,  P2 = (I + L^4)(I + L^8),  INV^T = P2^T P1^T
-        const f32x4 P1T = prod(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
-        const f32x4 P2 = prod(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
-        const f32x4 IT = prod(P2, P1T);
-        *reinterpret_cast<bf16x4 *>(lds + L::O_INVB + (x & 1) * 512 + lane * 8) = pack4(IT * brow);
-        *reinterpret_cast<bf16x4 *>(lds + L::O_QKE + (x & 3) * L::QKE + L::MQ + lane * 8) = pack4(MT);
-    };
-
-    // ---- stage B2 (prep waves 1 ..): w = INV beta k~ (as C tiles of w^T) and u' = INV beta v
-    auto stage_b2 = [&](int x) {
-        const bf16x4 ib = *reinterpret_cast<const bf16x4 *>(lds + L::O_INVB + (x & 1) * 512 + lane * 8);
-        const unsigned char *kv = lds + L::O_KV + (x % 3) * L::KV;
-        unsigned char *wum = lds + L::O_WUM + (x & 1) * L::WUM;
-        for (int job = w - 1; job < NKB + NVT; job += NPW - 1) {
-            if (job < NKB) {
-                const bf16x4 k0 = *reinterpret_cast<const bf16x4 *>(kv + L::KT + ((2 * job) * 64 + lane) * 8);
-                const bf16x4 k1 = *reinterpret_cast<const bf16x4 *>(kv + L::KT + ((2 * job + 1) * 64 + lane) * 8);
-                *reinterpret_cast<bf16x8 *>(wum + L::WF + (job * 64 + lane) * 16) =
-                    cat4(pack4(mma16(k0, ib, Z4)), pack4(mma16(k1, ib, Z4)));
-            } else {
-                const int n = job - NKB;
-                const bf16x4 vt = *reinterpret_cast<const bf16x4 *>(kv + L::VT + (n * 64 + lane) * 8);
-                *reinterpret_cast<f32x4 *>(wum + L::UP + (n * 64 + lane) * 16) = mma16(ib, vt, Z4);
-            }
-        }
-    };
-
+        return;
+    }
+    Prep<DK, VPW> pr;
+    pr.init(a, c.head, wv, lane);
     In<VPW> in0, in1;
-    load(in0, 0);
+    pr.load(in0, a, c.bos, c.len, 0, c.head, DV, col0, L::NCOL, NVB);
     // chunk x's inputs sit in in[x & 1], loaded one iteration before stage A uses them
     auto body = [&](int it, In<VPW> &use, In<VPW> &fill) {
         // the only loads in flight here are `use`'s, issued an iteration ago: wait
         // for them now, so that no later wait covers the loads issued next
-        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        asm volatile("" ::: "memory");
-        if (it + 4 < c.nch) load(fill, it + 4);
-        if (w == 0 && it + 2 >= 0 && it + 2 < c.nch) stage_b1(it + 2);
-        if (it + 3 < c.nch) stage_a(use, it + 3);
-        if (w > 0 && it + 1 >= 0 && it + 1 < c.nch) stage_b2(it + 1);
+        vm_wait_all();
+        if (it + 4 < c.nch) pr.load(fill, a, c.bos, c.len, it + 4, c.head, DV, col0, L::NCOL, NVB);
+        const int xa = it + 3;
+        if (xa < c.nch) {
+            unsigned char *p = pay(xa);
+            pr.stage_a(use, min(CH, c.len - xa * CH), p + P::QF, reinterpret_cast<float *>(p + P::EG), p + P::KR,
+                       kv(xa) + L::KT, kv(xa) + L::VT, NVB, NVT, part(xa), beta(xa));
+        }
+        const int xb = it + 1;
+        if (wv > 0 && xb >= 0 && xb < c.nch) {
+            // stage B2: w fragments into the chunk's operands, u' tiles
+            const bf16x4 ib = *reinterpret_cast<const bf16x4 *>(pay(xb) + P::IB + lane * 8);
+            const unsigned char *kvb = kv(xb);
+            unsigned char *ups = lds + L::O_UP + (xb & 1) * L::UP;
+            for (int job = wv - 1; job < NKB + NVT; job += NPW - 1) {
+                if (job < NKB) {
+                    *reinterpret_cast<bf16x8 *>(pay(xb) + P::WF + (job * 64 + lane) * 16) =
+                        w_frag(kvb + L::KT, ib, job, lane);
+                } else {
+                    const int n = job - NKB;
+                    const bf16x4 vt = *reinterpret_cast<const bf16x4 *>(kvb + L::VT + (n * 64 + lane) * 8);
+                    *reinterpret_cast<f32x4 *>(ups + (n * 64 + lane) * 16) = mma16(ib, vt, Z4);
+                }
+            }
+        }
         lds_barrier();
     };
     for (int it = -3; it < c.nch; it += 2) {
         body(it, in0, in1);
         if (it + 1 < c.nch) body(it + 1, in1, in0);
+    }
+}
+
+// =========================================================== two passes
+// Pass 1: the prep of NBC consecutive chunk rows (sequence 0's chunks, then
+// sequence 1's, ...) of one head per workgroup; consumer operands go to the
+// workspace, at row (chunk row) * H + head.  Stages A, B1, B2 of successive
+// rows are pipelined as in the one-pass form.
+constexpr int NBC = 16;
+
+template <int DK>
+__global__ __launch_bounds__(64 * (DK / 32 + 1)) void prep_kernel(FwdArgs a, unsigned char *ws, long long n_rows)
+{
+    constexpr int NPW = DK / 32, NMT = DK / 16, NKB = DK / 32;
+    using P = Pay<DK>;
+    constexpr int KT = NMT * 512, PART = NPW * 3 * 1024;
+    // LDS: k~ C tiles (3 buffers), partials (2), beta (2), (INV beta)^T (2)
+    __shared__ __attribute__((aligned(16))) unsigned char lds[3 * KT + 2 * PART + 2 * 64 + 2 * 512];
+    unsigned char *l_kt = lds;
+    f32x4 *l_part = reinterpret_cast<f32x4 *>(lds + 3 * KT);
+    float *l_beta = reinterpret_cast<float *>(lds + 3 * KT + 2 * PART);
+    unsigned char *l_ib = lds + 3 * KT + 2 * PART + 2 * 64;
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int head = blockIdx.x % a.H;
+    const long long row0 = (long long)(blockIdx.x / a.H) * NBC;
+    // live rows of this workgroup (the host's row count is an upper bound for packed input)
+    int nr = 0;
+    while (nr < NBC && row0 + nr < n_rows && row_pos(a, row0 + nr).seq < a.n_seq) ++nr;
+    if (nr == 0) return;
+    auto prow = [&](int i) { return ws + (size_t)((row0 + i) * a.H + head) * P::BYTES; };
+
+    if (wv == NPW) {
+        // the INV wave: stage B1 of row it + 1 in iteration it
+        for (int it = -2; it < nr; ++it) {
+            const int i = it + 1;
+            if (i >= 0 && i < nr)
+                stage_b1<NPW>(l_part + (i & 1) * (PART / 16), l_beta + (i & 1) * 16, l_ib + (i & 1) * 512,
+                              prow(i) + P::MQ, lane);
+            lds_barrier();
+        }
+        return;
+    }
+    Prep<DK, 0> pr;
+    pr.init(a, head, wv, lane);
+    auto load = [&](In<0> &in, int i) {
+        const RowPos p = row_pos(a, row0 + i);
+        pr.load(in, a, p.bos, p.len, p.x, head, 0, 0, 0, 0);
+    };
+    In<0> in0, in1;
+    load(in0, 0);
+    // row i's inputs sit in in[i & 1]; stage A of row it + 2, B2 of row it in iteration it
+    auto body = [&](int it, In<0> &use, In<0> &fill) {
+        vm_wait_all();
+        if (it + 3 < nr) load(fill, it + 3);
+        const int ia = it + 2;
+        if (ia < nr) {
+            const RowPos p = row_pos(a, row0 + ia);
+            unsigned char *pw = prow(ia);
+            pr.stage_a(use, min(CH, p.len - p.x * CH), pw + P::QF, reinterpret_cast<float *>(pw + P::EG), pw + P::KR,
+                       l_kt + (ia % 3) * KT, nullptr, 0, 0, l_part + (ia & 1) * (PART / 16), l_beta + (ia & 1) * 16);
+        }
+        const int ib = it;
+        if (wv > 0 && ib >= 0 && ib < nr) {
+            const bf16x4 ibv = *reinterpret_cast<const bf16x4 *>(l_ib + (ib & 1) * 512 + lane * 8);
+            unsigned char *pw = prow(ib);
+            for (int s = wv - 1; s < NKB; s += NPW - 1)
+                *reinterpret_cast<bf16x8 *>(pw + P::WF + (s * 64 + lane) * 16) =
+                    w_frag(l_kt + (ib % 3) * KT, ibv, s, lane);
+            if (wv == 1) *reinterpret_cast<bf16x4 *>(pw + P::IB + lane * 8) = ibv;
+        }
+        lds_barrier();
+    };
+    for (int it = -2; it < nr; it += 2) {
+        body(it, in0, in1);
+        if (it + 1 < nr) body(it + 1, in1, in0);
+    }
+}
+
+// Pass 2: one wave per (sequence, head, SPW slabs of 16 columns).  Workgroup
+// b takes chain 8 (b / 8 / NSG) + b % 8 and slab group (b / 8) % NSG, so that
+// the slab groups of a chain share blockIdx % 8 (the XCD, whose L2 then serves
+// the chain's operands to all of them; placement only affects speed).
+template <int DK, int DV, int SPW, bool SNAP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void rec_kernel(FwdArgs a, const unsigned char *ws)
+{
+    constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * SPW);
+    constexpr int NVB = (SPW + 1) / 2;   // 32-column v blocks of the slab group
+    using P = Pay<DK>;
+    const int lane = threadIdx.x, ln = lane & 15, lq = lane >> 4;
+    const int b8 = blockIdx.x / 8;
+    const int chain = 8 * (b8 / NSG) + blockIdx.x % 8;
+    const int sg = b8 % NSG;
+    if (chain >= a.n_seq * a.H) return;
+    const Chain c = chain_of(a, chain / a.H, chain % a.H, lane == 0 && sg == 0);
+    const size_t H = a.H;
+    const int col0 = sg * SPW * 16;
+    const size_t hbase = (((size_t)(c.hrow < 0 ? 0 : c.hrow) * H + c.head) * DV + col0) * DK;
+    f32x4 S[SPW][NMT];
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+            S[j][m] = (a.h0 && c.hrow >= 0)
+                          ? *reinterpret_cast<const f32x4 *>(a.h0 + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0))
+                          : Z4;
+    const size_t cbase = chunk_base(a, c.seq);
+    // 0/1 selectors for the C layout of v: columns 16 h .. +15 of a 32-column block
+    bf16x8 sel_v[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            sel_v[h][e] = static_cast<__bf16>((lq == 2 * h + (ln >> 3) && e == (ln & 7)) ? 1.f : 0.f);
+    struct Ops {
+        bf16x8 qf[NKB], wf[NKB];
+        bf16x4 kr[NMT], mq, ib;
+        f32x4 eg[NMT];
+        uint4 v[NVB];
+    };
+    auto load = [&](Ops &op, int x) {
+        const unsigned char *row = ws + ((cbase + x) * H + c.head) * P::BYTES;
+#pragma unroll
+        for (int s = 0; s < NKB; ++s) {
+            op.qf[s] = *reinterpret_cast<const bf16x8 *>(row + P::QF + (s * 64 + lane) * 16);
+            op.wf[s] = *reinterpret_cast<const bf16x8 *>(row + P::WF + (s * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) {
+            op.kr[m] = *reinterpret_cast<const bf16x4 *>(row + P::KR + (m * 64 + lane) * 8);
+            op.eg[m] = *reinterpret_cast<const f32x4 *>(row + P::EG + chan(m, lq, 0) * 4);
+        }
+        op.mq = *reinterpret_cast<const bf16x4 *>(row + P::MQ + lane * 8);
+        op.ib = *reinterpret_cast<const bf16x4 *>(row + P::IB + lane * 8);
+        // v: lane (lq, ln) takes token ln and columns 8 lq .. +7 of each 32-column block
+        const int rem = min(CH, c.len - x * CH);
+        const size_t tok = c.bos + (size_t)x * CH + min(ln, rem - 1);
+#pragma unroll
+        for (int vb = 0; vb < NVB; ++vb) {
+            const int cofs = 32 * vb + 8 * lq;
+            op.v[vb] = cofs < SPW * 16
+                           ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) +
+                                                              (tok * H + c.head) * DV + col0 + cofs)
+                           : uint4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto step = [&](const Ops &op, int x) {
+        if constexpr (SNAP) {
+            const size_t at = (((cbase + x) * H + c.head) * DV + col0) * DK;
+#pragma unroll
+            for (int j = 0; j < SPW; ++j)
+#pragma unroll
+                for (int m = 0; m < NMT; ++m)
+                    __builtin_nontemporal_store(S[j][m], reinterpret_cast<f32x4 *>(
+                        a.h_chunks + at + (size_t)(16 * j + ln) * DK + chan(m, lq, 0)));
+        }
+        f32x4 up[SPW], O[SPW];
+#pragma unroll
+        for (int j = 0; j < SPW; ++j) {
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, op.v[j / 2]);
+            up[j] = mma16(op.ib, pack4(mma32(bv, sel_v[j & 1], Z4)), Z4);   // u' = INV beta v
+        }
+        rec_step<NKB, NMT, SPW>(S, op.qf, op.wf, op.kr, op.eg, op.mq, up, O);
+        const int rem = min(CH, c.len - x * CH);
+        if (ln < rem) {
+#pragma unroll
+            for (int j = 0; j < SPW; ++j)
+                store_o(a.o, c.bos + (size_t)x * CH + ln, H, c.head, DV, col0 + 16 * j + 4 * lq, O[j], a.scale);
+        }
+    };
+    if (c.nch > 0) {
+        // chunk x's operands sit in op[x & 1], loaded one chunk ahead
+        Ops op0, op1;
+        load(op0, 0);
+        for (int x = 0; x < c.nch; x += 2) {
+            vm_wait_all();
+            if (x + 1 < c.nch) load(op1, x + 1);
+            step(op0, x);
+            if (x + 1 < c.nch) {
+                vm_wait_all();
+                if (x + 2 < c.nch) load(op0, x + 2);
+                step(op1, x + 1);
+            }
+        }
+    }
+    if (a.h_T && c.hrow >= 0) {
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+#pragma unroll
+            for (int m = 0; m < NMT; ++m)
+                *reinterpret_cast<f32x4 *>(a.h_T + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0)) = S[j][m];
     }
 }
 
@@ -599,10 +929,10 @@ hipError_t launch_t(const FwdArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Column groups per chain: the fewest that give at least one workgroup per
-// compute unit (the prep is repeated in every group of a chain).
+// One pass: column groups per chain, the fewest that give at least one
+// workgroup per compute unit (the prep is repeated in every group of a chain).
 template <int DK, int DV, bool SNAP>
-hipError_t launch_dims(const FwdArgs &a, int n_cu, hipStream_t stream)
+hipError_t launch_one_pass(const FwdArgs &a, int n_cu, hipStream_t stream)
 {
     const long long chains = (long long)a.n_seq * a.H;
     int G = 1;
@@ -623,19 +953,55 @@ hipError_t launch_dims(const FwdArgs &a, int n_cu, hipStream_t stream)
     }
 }
 
+template <int DK, int DV, bool SNAP>
+hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows, hipStream_t stream)
+{
+    const long long wgs1 = ((n_rows + NBC - 1) / NBC) * a.H;
+    if (wgs1 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (wgs1 > 0) {
+        hipLaunchKernelGGL((prep_kernel<DK>), dim3((unsigned)wgs1), dim3(64 * (DK / 32 + 1)), 0, stream, a, ws,
+                           n_rows);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    constexpr int SPW = 1, NSG = DV / 16;
+    const long long chains = (long long)a.n_seq * a.H;
+    const long long wgs2 = 8 * NSG * ((chains + 7) / 8);
+    if (wgs2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((rec_kernel<DK, DV, SPW, SNAP>), dim3((unsigned)wgs2), dim3(64), 0, stream, a,
+                       (const unsigned char *)ws);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t launch_dims(const FwdArgs &a, int n_cu, void *ws, size_t ws_bytes, long long n_rows, hipStream_t stream)
+{
+    const long long chains = (long long)a.n_seq * a.H;
+    const bool two = ws && chains < n_cu && ws_bytes >= fwd_workspace_bytes(DK, n_rows, a.H);
+    if (two)
+        return a.h_chunks ? launch_two_pass<DK, DV, true>(a, static_cast<unsigned char *>(ws), n_rows, stream)
+                          : launch_two_pass<DK, DV, false>(a, static_cast<unsigned char *>(ws), n_rows, stream);
+    return a.h_chunks ? launch_one_pass<DK, DV, true>(a, n_cu, stream) : launch_one_pass<DK, DV, false>(a, n_cu, stream);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs &a, int dk, int dv, hipStream_t stream)
+size_t fwd_workspace_bytes(int dk, long long n_rows, int H)
+{
+    const size_t per = dk == 128 ? (size_t)Pay<128>::BYTES : (size_t)Pay<64>::BYTES;
+    return per * (size_t)(n_rows < 0 ? 0 : n_rows) * (size_t)(H < 0 ? 0 : H);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs &a, int dk, int dv, void *ws, size_t ws_bytes, long long n_rows,
+                           hipStream_t stream)
 {
     int dev = 0, n_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-#define KDA_FWD(DKV, DVV)                                                                  \
-    if (dk == DKV && dv == DVV)                                                            \
-        return a.h_chunks ? launch_dims<DKV, DVV, true>(a, n_cu, stream)                   \
-                          : launch_dims<DKV, DVV, false>(a, n_cu, stream);
+#define KDA_FWD(DKV, DVV) \
+    if (dk == DKV && dv == DVV) return launch_dims<DKV, DVV>(a, n_cu, ws, ws_bytes, n_rows, stream);
     KDA_FWD(128, 128)
     KDA_FWD(128, 64)
     KDA_FWD(64, 128)

@@ -48,7 +48,11 @@ struct FwdArgs {
     float scale;
     int *err;            // the device error word
 };
-hipError_t launch_fwd_bf16(const FwdArgs &a, int dk, int dv, hipStream_t stream);
+// bf16: one pass, or (with a workspace of at least fwd_workspace_bytes for
+// n_rows chunk rows, and chains fewer than the compute units) two passes.
+size_t fwd_workspace_bytes(int dk, long long n_rows, int H);
+hipError_t launch_fwd_bf16(const FwdArgs &a, int dk, int dv, void *ws, size_t ws_bytes, long long n_rows,
+                           hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs &a, int dk, int dv, hipStream_t stream);
 
 struct ChunkOArgs {

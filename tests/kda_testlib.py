@@ -32,9 +32,9 @@ def to_device(p: synth.Prefill, dev="cuda"):
         cu_seqlens=None if p.cu_seqlens is None else torch.from_numpy(p.cu_seqlens).to(dev))
 
 
-def run_gpu(p: synth.Prefill, dev="cuda"):
+def run_gpu(p: synth.Prefill, dev="cuda", workspace="auto"):
     d = to_device(p, dev)
-    o, hT = kda.chunk_fwd(**d, scale=p.scale)
+    o, hT = kda.chunk_fwd(**d, scale=p.scale, workspace=workspace)
     assert kda.device_check() == 0   # synchronises; no slot index out of range
     return (o.float().cpu().numpy().reshape(p.tokens, p.H, p.dv).astype(np.float64),
             hT.cpu().numpy().astype(np.float64))

@@ -46,12 +46,13 @@ MIS = ctypes.c_void_p(0x20004)
 
 def chunk(lib, **kw):
     args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, h0=None, cu=None, chunk=16, o=A,
-                hT=None, B=1, T=16, H=1, dk=128, dv=128, n_seq=1, scale=0.1, dtype=1)
+                hT=None, B=1, T=16, H=1, dk=128, dv=128, n_seq=1, scale=0.1, dtype=1, ws=None, wsb=0)
     args.update(kw)
     return lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["b"],
                              args["A_log"], args["dt"], args["h0"], args["cu"], args["chunk"],
                              args["o"], args["hT"], args["B"], args["T"], args["H"], args["dk"],
-                             args["dv"], args["n_seq"], args["scale"], args["dtype"], None)
+                             args["dv"], args["n_seq"], args["scale"], args["dtype"], args["ws"], args["wsb"],
+                             None)
 
 
 def test_chunk_validation(lib):
@@ -65,7 +66,19 @@ def test_chunk_validation(lib):
     assert chunk(lib, A_log=None) == -1
     assert chunk(lib, q=None) == -1
     assert chunk(lib, o=MIS) == -4
+    assert chunk(lib, ws=MIS, wsb=1 << 20) == -4    # a workspace must be aligned too
     assert chunk(lib, n_seq=0, B=0) == 0            # nothing to do, no launch
+
+
+def test_chunk_workspace_bytes(lib):
+    """13,824 bytes per chunk row and head at dk = 128 (7,424 at dk = 64):
+    B * ceil(T/16) rows for dense input, ceil(T/16) + n_seq for packed."""
+    f = lib.kda_chunk_fwd_workspace_bytes
+    assert f(4, 4096, 16, 128, 128, 4, 0) == 13824 * 4 * 256 * 16
+    assert f(1, 17, 2, 64, 64, 1, 0) == 7424 * 2 * 2
+    assert f(1, 129830, 32, 128, 128, 32, 1) == 13824 * 32 * ((129830 + 15) // 16 + 32)
+    assert f(1, 16, 0, 128, 128, 1, 0) == 0
+    assert f(1, 16, 1, 96, 128, 1, 0) == 0
 
 
 def chunk_states(lib, **kw):
@@ -76,7 +89,7 @@ def chunk_states(lib, **kw):
                                     args["A_log"], args["dt"], args["h0"], args["cu"], args["chunk"],
                                     args["o"], args["hT"], args["hc"], args["B"], args["T"], args["H"],
                                     args["dk"], args["dv"], args["n_seq"], args["scale"], args["dtype"],
-                                    None)
+                                    None, 0, None)
 
 
 def test_chunk_states_validation(lib):
@@ -94,7 +107,7 @@ def chunk_pool(lib, **kw):
                                   args["A_log"], args["dt"], args["pool"], args["idx"], args["cu"],
                                   args["chunk"], args["o"], args["B"], args["T"], args["H"],
                                   args["dk"], args["dv"], args["n_seq"], args["P"], args["scale"],
-                                  args["dtype"], None)
+                                  args["dtype"], None, 0, None)
 
 
 def test_chunk_pool_validation(lib):

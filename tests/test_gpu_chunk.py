@@ -19,9 +19,9 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def check(p, heads=None, seqs=None, what=""):
+def check(p, heads=None, seqs=None, what="", workspace="auto"):
     say(what or p.name, "shapes", p.tokens, p.H, p.dk, p.dv, p.dtype)
-    o, hT = run_gpu(p)
+    o, hT = run_gpu(p, workspace=workspace)
     ro, rh = run_oracle(p, heads, seqs)
     if heads is not None:
         o, hT = o[:, heads], hT[:, heads]
@@ -67,6 +67,23 @@ def test_many_short_sequences(dtype, dk, dv, H):
     lengths = [int(x) for x in np.random.default_rng(7).integers(0, 41, size=24)]
     p = synth.prefill(400, B=1, T=0, H=H, dk=dk, dv=dv, dtype=dtype, lengths=lengths, with_h0=True)
     check(p, what=f"many-short {dtype} d{dk}x{dv} H{H}")
+
+
+@pytest.mark.parametrize("form", ["one-pass", "two-pass"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
+def test_both_prefill_forms(form, dk, dv):
+    """The one-pass kernel (no workspace) and the prep + recurrence pair (a
+    workspace, fewer chains than compute units) each match the oracle, on a
+    ragged packed batch that spans several 16-row prep blocks."""
+    p = synth.prefill(500 + dk + dv, B=1, T=0, H=3, dk=dk, dv=dv, dtype="bf16",
+                      lengths=[300, 1, 0, 47, 129], with_h0=True)
+    if form == "one-pass":
+        ws = None
+    else:
+        n = kda.chunk_fwd_workspace_bytes(1, p.tokens, p.H, dk, dv, p.n_seq, True)
+        assert n > 0
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    check(p, what=f"{form} d{dk}x{dv}", workspace=ws)
 
 
 def test_workload1_full():
