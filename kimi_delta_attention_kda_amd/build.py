@@ -18,6 +18,9 @@ SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_fwd.hip", "kda_fwd_f32.hip", "k
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: no copies between the AGPR and VGPR files
+         # around the fp32 elementwise work done on accumulated state
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I" + os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-result"]
 
 

@@ -747,10 +747,22 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1)) void prep_kernel(FwdArgs a, uns
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int head = blockIdx.x % a.H;
     const long long row0 = (long long)(blockIdx.x / a.H) * NBC;
-    // live rows of this workgroup (the host's row count is an upper bound for packed input)
-    int nr = 0;
-    while (nr < NBC && row0 + nr < n_rows && row_pos(a, row0 + nr).seq < a.n_seq) ++nr;
+    // lane i < NBC holds the position of row row0 + i; the live rows are a
+    // prefix (the host's row count is an upper bound for packed input)
+    const RowPos mine = row_pos(a, row0 + (lane < NBC ? lane : 0));
+    const bool live_row = lane < NBC && row0 + lane < n_rows && mine.seq < a.n_seq;
+    const int nr = __builtin_popcountll(__ballot(live_row));
     if (nr == 0) return;
+    auto pos = [&](int i) {   // row row0 + i (uniform i < NBC), read from lane i
+        RowPos p;
+        const uint64_t bos = mine.bos;
+        p.bos = ((uint64_t)(unsigned)__builtin_amdgcn_readlane((unsigned)(bos >> 32), i) << 32) |
+                (unsigned)__builtin_amdgcn_readlane((unsigned)bos, i);
+        p.x = __builtin_amdgcn_readlane(mine.x, i);
+        p.len = __builtin_amdgcn_readlane(mine.len, i);
+        p.seq = __builtin_amdgcn_readlane(mine.seq, i);
+        return p;
+    };
     auto prow = [&](int i) { return ws + (size_t)((row0 + i) * a.H + head) * P::BYTES; };
 
     if (wv == NPW) {
@@ -767,7 +779,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1)) void prep_kernel(FwdArgs a, uns
     Prep<DK, 0> pr;
     pr.init(a, head, wv, lane);
     auto load = [&](In<0> &in, int i) {
-        const RowPos p = row_pos(a, row0 + i);
+        const RowPos p = pos(i);
         pr.load(in, a, p.bos, p.len, p.x, head, 0, 0, 0, 0);
     };
     In<0> in0, in1;
@@ -778,7 +790,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1)) void prep_kernel(FwdArgs a, uns
         if (it + 3 < nr) load(fill, it + 3);
         const int ia = it + 2;
         if (ia < nr) {
-            const RowPos p = row_pos(a, row0 + ia);
+            const RowPos p = pos(ia);
             unsigned char *pw = prow(ia);
             pr.stage_a(use, min(CH, p.len - p.x * CH), pw + P::QF, reinterpret_cast<float *>(pw + P::EG), pw + P::KR,
                        l_kt + (ia % 3) * KT, nullptr, 0, 0, l_part + (ia & 1) * (PART / 16), l_beta + (ia & 1) * 16);
@@ -804,13 +816,110 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1)) void prep_kernel(FwdArgs a, uns
 // b takes chain 8 (b / 8 / NSG) + b % 8 and slab group (b / 8) % NSG, so that
 // the slab groups of a chain share blockIdx % 8 (the XCD, whose L2 then serves
 // the chain's operands to all of them; placement only affects speed).
+//
+// A chunk's operands (its workspace row, padded to whole KiB, and the wave's
+// 16 x 16 SPW bf16 tile of v) reach LDS by direct global-to-LDS loads, RING
+// chunks ahead, so the recurrence never waits on memory latency.  The loads
+// are issued from inline assembly: the compiler would otherwise wait for all
+// of them before every LDS read.  Each is counted in this wave's vmcnt, which
+// drains in issue order, so waiting until at most n loads remain outstanding,
+// n = the loads issued after chunk x's, guarantees chunk x has landed.
+namespace {
+constexpr int RING = 5;
+
+// Direct global-to-LDS loads of 16 bytes per lane: load i of a group reads
+// base + voff + 1024 i (the last one voff_last + 1024 i) into LDS bytes
+// lds + 1024 i + 16 lane .. (the instruction offset moves both addresses; m0,
+// the LDS address register, is set for the group and then restored).
+template <int N>
+__device__ __forceinline__ void dma_group(const void *base, unsigned voff, unsigned voff_last, unsigned lds) {
+    static_assert(N >= 1 && N <= 4, "one 4 KiB group");
+    // wave-uniform operands, made explicit for the scalar-register constraints
+    lds = __builtin_amdgcn_readfirstlane(lds);
+    const uint64_t b64 = reinterpret_cast<uint64_t>(base);
+    base = reinterpret_cast<const void *>(
+        ((uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((unsigned)(b64 >> 32)) << 32) |
+        (unsigned)__builtin_amdgcn_readfirstlane((unsigned)b64));
+    unsigned keep;
+    if constexpr (N == 4)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, %3\n\t"
+                     "global_load_lds_dwordx4 %1, %3 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %1, %3 offset:2048\n\t"
+                     "global_load_lds_dwordx4 %2, %3 offset:3072\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(keep) : "v"(voff), "v"(voff_last), "s"(base), "s"(lds) : "memory");
+    else if constexpr (N == 3)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, %3\n\t"
+                     "global_load_lds_dwordx4 %1, %3 offset:1024\n\t"
+                     "global_load_lds_dwordx4 %2, %3 offset:2048\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(keep) : "v"(voff), "v"(voff_last), "s"(base), "s"(lds) : "memory");
+    else if constexpr (N == 2)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, %3\n\t"
+                     "global_load_lds_dwordx4 %2, %3 offset:1024\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(keep) : "v"(voff), "v"(voff_last), "s"(base), "s"(lds) : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                     "global_load_lds_dwordx4 %1, %2\n\t"
+                     "s_mov_b32 m0, %0"
+                     : "=&s"(keep) : "v"(voff_last), "s"(base), "s"(lds) : "memory");
+}
+// NB bytes (a multiple of 16) from base into LDS at lds, in 1 KiB loads; the
+// lanes of the last load that would pass the end re-read its last 16 bytes
+// (landing in LDS padding past NB).
+template <int NB>
+__device__ __forceinline__ void dma_bytes(const unsigned char *base, unsigned lds, int lane) {
+    constexpr int NL = (NB + 1023) / 1024;
+#pragma unroll
+    for (int g = 0; g < (NL + 3) / 4; ++g) {
+        const int first = 4 * g;
+        const unsigned voff = 4096u * g + 16u * lane;
+        if (first + 4 < NL) {
+            dma_group<4>(base, voff, voff, lds + 4096u * g);
+        } else {
+            // the group holding the last load: its clamped offset, relative to the load's instruction offset
+            const unsigned last = (unsigned)min((NL - 1) * 1024 + 16 * lane, NB - 16) - 1024u * (NL - 1 - first);
+            switch (NL - first) {
+            case 4: dma_group<4>(base, voff, last, lds + 4096u * g); break;
+            case 3: dma_group<3>(base, voff, last, lds + 4096u * g); break;
+            case 2: dma_group<2>(base, voff, last, lds + 4096u * g); break;
+            default: dma_group<1>(base, voff, last, lds + 4096u * g); break;
+            }
+        }
+    }
+}
+// Wait until at most n of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait_le() {
+    static_assert(N >= 0 && N <= 63, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+template <int ND, int K = RING - 1>
+__device__ __forceinline__ void vm_wait_chunks(int k) {   // at most k chunks of ND loads outstanding
+    if constexpr (K == 0) {
+        vm_wait_le<0>();
+    } else {
+        if (k >= K) vm_wait_le<K * ND>();
+        else vm_wait_chunks<ND, K - 1>(k);
+    }
+}
+}  // namespace
+
 template <int DK, int DV, int SPW, bool SNAP>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void rec_kernel(FwdArgs a, const unsigned char *ws)
+__global__ __launch_bounds__(64) void rec_kernel(FwdArgs a, const unsigned char *ws)
 {
     constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * SPW);
-    constexpr int NVB = (SPW + 1) / 2;   // 32-column v blocks of the slab group
     using P = Pay<DK>;
+    constexpr int NPAY = (P::BYTES + 1023) / 1024;   // 1 KiB loads of a workspace row
+    constexpr int ND = NPAY + 1;                     // and one for the v tile
+    constexpr int SLOT = ND * 1024, VT = NPAY * 1024;
+    static_assert((RING - 1) * ND <= 63, "loads in flight exceed the vmcnt field");
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[RING * SLOT];
     const int lane = threadIdx.x, ln = lane & 15, lq = lane >> 4;
     const int b8 = blockIdx.x / 8;
     const int chain = 8 * (b8 / NSG) + blockIdx.x % 8;
@@ -829,46 +938,24 @@ void rec_kernel(FwdArgs a, const unsigned char *ws)
                           ? *reinterpret_cast<const f32x4 *>(a.h0 + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0))
                           : Z4;
     const size_t cbase = chunk_base(a, c.seq);
-    // 0/1 selectors for the C layout of v: columns 16 h .. +15 of a 32-column block
-    bf16x8 sel_v[2];
+    // identity as a K = 16 B operand: the product of a row-loaded 16 x 16 tile with it is its C layout
+    bf16x4 eye;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            sel_v[h][e] = static_cast<__bf16>((lq == 2 * h + (ln >> 3) && e == (ln & 7)) ? 1.f : 0.f);
-    struct Ops {
-        bf16x8 qf[NKB], wf[NKB];
-        bf16x4 kr[NMT], mq, ib;
-        f32x4 eg[NMT];
-        uint4 v[NVB];
-    };
-    auto load = [&](Ops &op, int x) {
-        const unsigned char *row = ws + ((cbase + x) * H + c.head) * P::BYTES;
-#pragma unroll
-        for (int s = 0; s < NKB; ++s) {
-            op.qf[s] = *reinterpret_cast<const bf16x8 *>(row + P::QF + (s * 64 + lane) * 16);
-            op.wf[s] = *reinterpret_cast<const bf16x8 *>(row + P::WF + (s * 64 + lane) * 16);
-        }
-#pragma unroll
-        for (int m = 0; m < NMT; ++m) {
-            op.kr[m] = *reinterpret_cast<const bf16x4 *>(row + P::KR + (m * 64 + lane) * 8);
-            op.eg[m] = *reinterpret_cast<const f32x4 *>(row + P::EG + chan(m, lq, 0) * 4);
-        }
-        op.mq = *reinterpret_cast<const bf16x4 *>(row + P::MQ + lane * 8);
-        op.ib = *reinterpret_cast<const bf16x4 *>(row + P::IB + lane * 8);
-        // v: lane (lq, ln) takes token ln and columns 8 lq .. +7 of each 32-column block
+    for (int e = 0; e < 4; ++e) eye[e] = static_cast<__bf16>(4 * lq + e == ln ? 1.f : 0.f);
+    const unsigned ring_lds =
+        __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) unsigned char *)ring);
+    // v tile in LDS: token t at t * 32 SPW bytes, 8 columns per lane; for SPW = 1
+    // lanes 32 .. 63 repeat lanes 0 .. 31 into the unused upper half.
+    const int vt_tok = (lane & 63) / (2 * SPW) % 16, vt_col = 8 * ((lane & 63) % (2 * SPW));
+    auto issue = [&](int x) {   // chunk x's loads into ring slot x % RING
+        const unsigned slot = ring_lds + (unsigned)((x % RING) * SLOT);
+        dma_bytes<P::BYTES>(ws + ((cbase + x) * H + c.head) * P::BYTES, slot, lane);
         const int rem = min(CH, c.len - x * CH);
-        const size_t tok = c.bos + (size_t)x * CH + min(ln, rem - 1);
-#pragma unroll
-        for (int vb = 0; vb < NVB; ++vb) {
-            const int cofs = 32 * vb + 8 * lq;
-            op.v[vb] = cofs < SPW * 16
-                           ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.v) +
-                                                              (tok * H + c.head) * DV + col0 + cofs)
-                           : uint4{0u, 0u, 0u, 0u};
-        }
+        const uint16_t *v0 = static_cast<const uint16_t *>(a.v) + ((c.bos + (size_t)x * CH) * H + c.head) * DV + col0;
+        dma_group<1>(v0, 0u, (unsigned)(((size_t)min(vt_tok, rem - 1) * H * DV + vt_col) * 2), slot + VT);
     };
-    auto step = [&](const Ops &op, int x) {
+    auto step = [&](int x) {
+        const unsigned char *row = ring + (x % RING) * SLOT;
         if constexpr (SNAP) {
             const size_t at = (((cbase + x) * H + c.head) * DV + col0) * DK;
 #pragma unroll
@@ -878,13 +965,30 @@ void rec_kernel(FwdArgs a, const unsigned char *ws)
                     __builtin_nontemporal_store(S[j][m], reinterpret_cast<f32x4 *>(
                         a.h_chunks + at + (size_t)(16 * j + ln) * DK + chan(m, lq, 0)));
         }
+        // operands from the ring slot, in the order the chunk consumes them:
+        // v as lane (lq, ln) = token ln, columns 4 lq .. +3 of each 16-column slab
+        bf16x4 vv[SPW];
+#pragma unroll
+        for (int j = 0; j < SPW; ++j)
+            vv[j] = *reinterpret_cast<const bf16x4 *>(row + VT + ln * 32 * SPW + (16 * j + 4 * lq) * 2);
+        const bf16x4 ib = *reinterpret_cast<const bf16x4 *>(row + P::IB + lane * 8);
+        bf16x8 qf[NKB], wf[NKB];
+        bf16x4 kr[NMT];
+        f32x4 eg[NMT];
+#pragma unroll
+        for (int s = 0; s < NKB; ++s) wf[s] = *reinterpret_cast<const bf16x8 *>(row + P::WF + (s * 64 + lane) * 16);
+#pragma unroll
+        for (int s = 0; s < NKB; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(row + P::QF + (s * 64 + lane) * 16);
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) eg[m] = *reinterpret_cast<const f32x4 *>(row + P::EG + chan(m, lq, 0) * 4);
+        const bf16x4 mq = *reinterpret_cast<const bf16x4 *>(row + P::MQ + lane * 8);
+#pragma unroll
+        for (int m = 0; m < NMT; ++m) kr[m] = *reinterpret_cast<const bf16x4 *>(row + P::KR + (m * 64 + lane) * 8);
         f32x4 up[SPW], O[SPW];
 #pragma unroll
-        for (int j = 0; j < SPW; ++j) {
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, op.v[j / 2]);
-            up[j] = mma16(op.ib, pack4(mma32(bv, sel_v[j & 1], Z4)), Z4);   // u' = INV beta v
-        }
-        rec_step<NKB, NMT, SPW>(S, op.qf, op.wf, op.kr, op.eg, op.mq, up, O);
+        for (int j = 0; j < SPW; ++j)   // u' = INV beta v (v in C layout by an identity product)
+            up[j] = mma16(ib, pack4(mma16(vv[j], eye, Z4)), Z4);
+        rec_step<NKB, NMT, SPW>(S, qf, wf, kr, eg, mq, up, O);
         const int rem = min(CH, c.len - x * CH);
         if (ln < rem) {
 #pragma unroll
@@ -892,20 +996,13 @@ void rec_kernel(FwdArgs a, const unsigned char *ws)
                 store_o(a.o, c.bos + (size_t)x * CH + ln, H, c.head, DV, col0 + 16 * j + 4 * lq, O[j], a.scale);
         }
     };
-    if (c.nch > 0) {
-        // chunk x's operands sit in op[x & 1], loaded one chunk ahead
-        Ops op0, op1;
-        load(op0, 0);
-        for (int x = 0; x < c.nch; x += 2) {
-            vm_wait_all();
-            if (x + 1 < c.nch) load(op1, x + 1);
-            step(op0, x);
-            if (x + 1 < c.nch) {
-                vm_wait_all();
-                if (x + 2 < c.nch) load(op0, x + 2);
-                step(op1, x + 1);
-            }
-        }
+    for (int x = 0; x < min(RING - 1, c.nch); ++x) issue(x);
+    for (int x = 0; x < c.nch; ++x) {
+        // slot (x + RING - 1) % RING held chunk x - 1, whose LDS reads are done
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        if (x + RING - 1 < c.nch) issue(x + RING - 1);
+        vm_wait_chunks<ND>(min(RING - 1, c.nch - 1 - x));   // chunks x + 1 .. x + RING - 1 may still fly
+        step(x);
     }
     if (a.h_T && c.hrow >= 0) {
 #pragma unroll
@@ -915,6 +1012,10 @@ void rec_kernel(FwdArgs a, const unsigned char *ws)
                 *reinterpret_cast<f32x4 *>(a.h_T + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0)) = S[j][m];
     }
 }
+
+#ifndef KDA_REC_SPW
+#define KDA_REC_SPW 1
+#endif
 
 namespace {
 
@@ -964,7 +1065,7 @@ hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    constexpr int SPW = 1, NSG = DV / 16;
+    constexpr int SPW = KDA_REC_SPW, NSG = DV / (16 * SPW);
     const long long chains = (long long)a.n_seq * a.H;
     const long long wgs2 = 8 * NSG * ((chains + 7) / 8);
     if (wgs2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
