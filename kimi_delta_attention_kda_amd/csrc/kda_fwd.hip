@@ -276,16 +276,19 @@ struct Prep {
         in.b = (w == 0) ? static_cast<const uint16_t *>(a.beta_raw)[tok * H + head] : (uint16_t)0;
     }
 
-    // Stage A of a chunk with `rem` live tokens.  Writes q~ fragments (qf),
-    // e^{G_C} (eg), k^r C tiles (kr), k~ C tiles (kt), v C tiles (vt, nvt
-    // tiles of nvb blocks; none if vt is NULL), this wave's L / L^T / Mqk^T
-    // partials (part) and, from wave 0, beta (beta).
-    __device__ __forceinline__ void stage_a(const In<VPW> &in, int rem, unsigned char *qf, float *eg,
-                                            unsigned char *kr, unsigned char *kt, unsigned char *vt, int nvb, int nvt,
-                                            f32x4 *part, float *beta) const {
+    // Stage A of a chunk with `rem` live tokens, the arithmetic: q~ and k~ (bf16
+    // K fragments of this block's 32 channels), k^r, e^G of each token and
+    // channel (e1; the chunk's e^{G_C} in the lanes of token 15), this block's
+    // partials of L, L^T and Mqk^T (before masks and beta).
+    struct Out {
+        bf16x8 bqd, bkd, bkr;
+        float e1[8];
+        f32x4 pL, pLT, pMT;
+    };
+    __device__ __forceinline__ void stage_a_core(const In<VPW> &in, int rem, Out &o) const {
         const bool live = t < rem;
         const float nA = live ? -A_exp : 0.f;
-        float kf[8], qfv[8], gv[8], Gm[8], GC[8], e1[8], kd[8], qd[8], krv[8];
+        float kf[8], qfv[8], gv[8], Gm[8], GC[8], kd[8], qd[8], krv[8];
         const uint32_t kw[4] = {in.k.x, in.k.y, in.k.z, in.k.w};
         const uint32_t qw[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
         const uint32_t aw[4] = {in.a.x, in.a.y, in.a.z, in.a.w};
@@ -303,24 +306,24 @@ struct Prep {
             Gm[e] = scan16(gv[e]);
             GC[e] = row_bcast<15>(Gm[e]);
             deep |= GC[e] < -100.f;
-            e1[e] = __builtin_amdgcn_exp2f(Gm[e]);
-            kd[e] = kf[e] * e1[e];
-            qd[e] = qfv[e] * e1[e];
+            o.e1[e] = __builtin_amdgcn_exp2f(Gm[e]);
+            kd[e] = kf[e] * o.e1[e];
+            qd[e] = qfv[e] * o.e1[e];
         }
-        const bf16x8 bkd = pack8(kd), bqd = pack8(qd);
-        f32x4 pL, pLT, pMT;
+        o.bkd = pack8(kd);
+        o.bqd = pack8(qd);
         if (__ballot(deep) == 0) {
             // mild: rows k~ (<= 1), columns k 2^-G (<= 2^100); k^r = k 2^-G 2^{G_C}
             float kh[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 kh[e] = kf[e] * __builtin_amdgcn_exp2f(-Gm[e]);
-                krv[e] = kh[e] * row_bcast<15>(e1[e]);
+                krv[e] = kh[e] * row_bcast<15>(o.e1[e]);
             }
             const bf16x8 bkh = pack8(kh);
-            pL = mma32(bkd, bkh, Z4);
-            pLT = mma32(bkh, bkd, Z4);
-            pMT = mma32(bkh, bqd, Z4);
+            o.pL = mma32(o.bkd, bkh, Z4);
+            o.pLT = mma32(bkh, o.bkd, Z4);
+            o.pMT = mma32(bkh, o.bqd, Z4);
         } else {
             // strong: two 8-token row blocks, each token's decay clipped at 2^-12
             constexpr float CLIP = 12.f;
@@ -335,7 +338,7 @@ struct Prep {
                 Rq[e] = qfv[e] * f;
             }
             const bf16x8 bR = pack8(R), bRq = pack8(Rq);
-            pL = pLT = pMT = Z4;
+            o.pL = o.pLT = o.pMT = Z4;
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 float Cc[8];
@@ -344,26 +347,43 @@ struct Prep {
                     Cc[e] = t < 8 * (bb + 1) ? kf[e] * __builtin_amdgcn_exp2f((bb ? Bf1[e] : 0.f) - Gp[e]) : 0.f;
                 const bf16x8 bC = pack8(Cc);
                 const f32x4 Lb = mma32(bR, bC, Z4), LTb = mma32(bC, bR, Z4), MTb = mma32(bC, bRq, Z4);
-                if ((4 * r) / 8 == bb) pL = Lb;          // C-layout rows 4r .. 4r+3 of L lie in block bb
-                if (t / 8 == bb) { pLT = LTb; pMT = MTb; }   // row t of L (as column t of L^T), of Mqk
+                if ((4 * r) / 8 == bb) o.pL = Lb;          // C-layout rows 4r .. 4r+3 of L lie in block bb
+                if (t / 8 == bb) { o.pLT = LTb; o.pMT = MTb; }   // row t of L (as column t of L^T), of Mqk
             }
         }
-        const bf16x8 bkr = pack8(krv);
-        *reinterpret_cast<bf16x8 *>(qf + (w * 64 + lane) * 16) = bqd;
+        o.bkr = pack8(krv);
+    }
+    // e^{G_C} of this block's channels from the lanes of token 15
+    __device__ __forceinline__ void store_eg(const Out &o, float *eg) const {
         if (t == CH - 1) {
             float *egw = eg + 32 * w + 8 * r;
-            *reinterpret_cast<f32x4 *>(egw) = f32x4{e1[0], e1[1], e1[2], e1[3]};
-            *reinterpret_cast<f32x4 *>(egw + 4) = f32x4{e1[4], e1[5], e1[6], e1[7]};
+            *reinterpret_cast<f32x4 *>(egw) = f32x4{o.e1[0], o.e1[1], o.e1[2], o.e1[3]};
+            *reinterpret_cast<f32x4 *>(egw + 4) = f32x4{o.e1[4], o.e1[5], o.e1[6], o.e1[7]};
         }
+    }
+    // C tiles 2w + h of a row-loaded channel block (one selector MFMA each)
+    __device__ __forceinline__ bf16x4 ctile(bf16x8 x, int h) const { return pack4(mma32(x, sel_c[h], Z4)); }
+
+    // Stage A of a chunk with `rem` live tokens.  Writes q~ fragments (qf),
+    // e^{G_C} (eg), k^r C tiles (kr), k~ C tiles (kt), v C tiles (vt, nvt
+    // tiles of nvb blocks; none if vt is NULL), this wave's L / L^T / Mqk^T
+    // partials (part) and, from wave 0, beta (beta).
+    __device__ __forceinline__ void stage_a(const In<VPW> &in, int rem, unsigned char *qf, float *eg,
+                                            unsigned char *kr, unsigned char *kt, unsigned char *vt, int nvb, int nvt,
+                                            f32x4 *part, float *beta) const {
+        Out o;
+        stage_a_core(in, rem, o);
+        *reinterpret_cast<bf16x8 *>(qf + (w * 64 + lane) * 16) = o.bqd;
+        store_eg(o, eg);
         f32x4 *pp = part + (w * 3) * 64 + lane;
-        pp[0] = pL;
-        pp[64] = pLT;
-        pp[128] = pMT;
+        pp[0] = o.pL;
+        pp[64] = o.pLT;
+        pp[128] = o.pMT;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int m = 2 * w + h;
-            *reinterpret_cast<bf16x4 *>(kt + (m * 64 + lane) * 8) = pack4(mma32(bkd, sel_c[h], Z4));
-            *reinterpret_cast<bf16x4 *>(kr + (m * 64 + lane) * 8) = pack4(mma32(bkr, sel_c[h], Z4));
+            *reinterpret_cast<bf16x4 *>(kt + (m * 64 + lane) * 8) = ctile(o.bkd, h);
+            *reinterpret_cast<bf16x4 *>(kr + (m * 64 + lane) * 8) = ctile(o.bkr, h);
         }
         if (vt) {
 #pragma unroll
@@ -380,9 +400,33 @@ struct Prep {
                 }
             }
         }
-        if (w == 0 && r == 0) beta[t] = live ? sigmoid_f(bf16_to_f32(in.b)) : 0.f;
+        if (w == 0 && r == 0) beta[t] = t < rem ? sigmoid_f(bf16_to_f32(in.b)) : 0.f;
     }
 };
+
+// Stage B1 from the summed partials of L, L^T, Mqk^T and beta (brow: tokens
+// 4 lq .. +3 of this lane, bcol: token ln): masks, beta, INV by Neumann
+// squaring.  Returns the C layouts of (INV beta)^T and Mqk^T, in bf16.
+__device__ __forceinline__ void b1_core(f32x4 Lm, f32x4 LT, f32x4 MT, f32x4 brow, float bcol, int lane, bf16x4 &ib,
+                                        bf16x4 &mq) {
+    const int ln = lane & 15, lq = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 4 * lq + i;
+        Lm[i] = row > ln ? -brow[i] * Lm[i] : 0.f;   // L[row][ln], strictly lower
+        LT[i] = ln > row ? -bcol * LT[i] : 0.f;      // L[ln][row]
+        MT[i] = ln >= row ? MT[i] : 0.f;             // Mqk[ln][row], lower including the diagonal
+    }
+    const f32x4 L2 = prod(LT, Lm), L2T = prod(Lm, LT);
+    const f32x4 L4 = prod(L2T, L2), L4T = prod(L2, L2T);
+    const f32x4 L8 = prod(L4T, L4);
+    // P1^T = ((I + L)(I + L^2))^T,  P2 = (I + L^4)(I + L^8),  INV^T = P2^T P1^T
+    const f32x4 P1T = prod(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
+    const f32x4 P2 = prod(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
+    const f32x4 IT = prod(P2, P1T);
+    ib = pack4(IT * brow);
+    mq = pack4(MT);
+}
 
 // Stage B1 (one wave): L, L^T, Mqk^T from the NPW partials; INV; writes the
 // C layout of (INV beta)^T (bf16) to ib and of Mqk^T (bf16) to mq.
@@ -398,32 +442,20 @@ __device__ __forceinline__ void stage_b1(const f32x4 *part, const float *beta, u
         LT += pp[ww * 192 + 64];
         MT += pp[ww * 192 + 128];
     }
-    const f32x4 brow = *reinterpret_cast<const f32x4 *>(beta + 4 * lq);
-    const float bcol = beta[ln];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 4 * lq + i;
-        Lm[i] = row > ln ? -brow[i] * Lm[i] : 0.f;   // L[row][ln], strictly lower
-        LT[i] = ln > row ? -bcol * LT[i] : 0.f;      // L[ln][row]
-        MT[i] = ln >= row ? MT[i] : 0.f;             // Mqk[ln][row], lower including the diagonal
-    }
-    const f32x4 L2 = prod(LT, Lm), L2T = prod(Lm, LT);
-    const f32x4 L4 = prod(L2T, L2), L4T = prod(L2, L2T);
-    const f32x4 L8 = prod(L4T, L4);
-    // P1^T = ((I + L)(I + L^2))^T,  P2 = (I + L^4)(I + L^8),  INV^T = P2^T P1^T
-    const f32x4 P1T = prod(plus_eye(L2, ln, lq), plus_eye(LT, ln, lq));
-    const f32x4 P2 = prod(plus_eye(L4T, ln, lq), plus_eye(L8, ln, lq));
-    const f32x4 IT = prod(P2, P1T);
-    *reinterpret_cast<bf16x4 *>(ib + lane * 8) = pack4(IT * brow);
-    *reinterpret_cast<bf16x4 *>(mq + lane * 8) = pack4(MT);
+    bf16x4 ibv, mqv;
+    b1_core(Lm, LT, MT, *reinterpret_cast<const f32x4 *>(beta + 4 * lq), beta[ln], lane, ibv, mqv);
+    *reinterpret_cast<bf16x4 *>(ib + lane * 8) = ibv;
+    *reinterpret_cast<bf16x4 *>(mq + lane * 8) = mqv;
 }
 
 // w = INV beta k~ for K block s: the A fragment of W' = w S (from the C tiles
 // 2s, 2s+1 of k~ and the C layout of (INV beta)^T).
-__device__ __forceinline__ bf16x8 w_frag(const unsigned char *kt, bf16x4 ib, int s, int lane) {
-    const bf16x4 k0 = *reinterpret_cast<const bf16x4 *>(kt + ((2 * s) * 64 + lane) * 8);
-    const bf16x4 k1 = *reinterpret_cast<const bf16x4 *>(kt + ((2 * s + 1) * 64 + lane) * 8);
+__device__ __forceinline__ bf16x8 w_frag2(bf16x4 k0, bf16x4 k1, bf16x4 ib) {
     return cat4(pack4(mma16(k0, ib, Z4)), pack4(mma16(k1, ib, Z4)));
+}
+__device__ __forceinline__ bf16x8 w_frag(const unsigned char *kt, bf16x4 ib, int s, int lane) {
+    return w_frag2(*reinterpret_cast<const bf16x4 *>(kt + ((2 * s) * 64 + lane) * 8),
+                   *reinterpret_cast<const bf16x4 *>(kt + ((2 * s + 1) * 64 + lane) * 8), ib);
 }
 
 // One chunk of the recurrence for SPW slabs of 16 columns: S holds the state
@@ -724,92 +756,67 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a
 }
 
 // =========================================================== two passes
-// Pass 1: the prep of NBC consecutive chunk rows (sequence 0's chunks, then
-// sequence 1's, ...) of one head per workgroup; consumer operands go to the
-// workspace, at row (chunk row) * H + head.  Stages A, B1, B2 of successive
-// rows are pipelined as in the one-pass form.
-constexpr int NBC = 16;
+// Pass 1: one wave per (chunk row, head), independent of every other wave:
+// stage A over the d_k / 32 channel blocks in turn (the partials of L, L^T,
+// Mqk^T summed in registers), then B1 and B2, writing the chunk's consumer
+// operands to its workspace row (chunk row) * H + head.  Chunk rows run over
+// sequence 0's chunks, then sequence 1's, ...
+constexpr int PREP_WAVES = 4;
+#ifndef KDA_PREP_OCC
+#define KDA_PREP_OCC
+#endif
 
 template <int DK>
-__global__ __launch_bounds__(64 * (DK / 32 + 1)) void prep_kernel(FwdArgs a, unsigned char *ws, long long n_rows)
+__global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdArgs a, unsigned char *ws, long long n_rows)
 {
     constexpr int NPW = DK / 32, NMT = DK / 16, NKB = DK / 32;
     using P = Pay<DK>;
-    constexpr int KT = NMT * 512, PART = NPW * 3 * 1024;
-    // LDS: k~ C tiles (3 buffers), partials (2), beta (2), (INV beta)^T (2)
-    __shared__ __attribute__((aligned(16))) unsigned char lds[3 * KT + 2 * PART + 2 * 64 + 2 * 512];
-    unsigned char *l_kt = lds;
-    f32x4 *l_part = reinterpret_cast<f32x4 *>(lds + 3 * KT);
-    float *l_beta = reinterpret_cast<float *>(lds + 3 * KT + 2 * PART);
-    unsigned char *l_ib = lds + 3 * KT + 2 * PART + 2 * 64;
-
-    const int lane = threadIdx.x & 63;
+    __shared__ float l_beta[PREP_WAVES][CH];
+    const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int head = blockIdx.x % a.H;
-    const long long row0 = (long long)(blockIdx.x / a.H) * NBC;
-    // lane i < NBC holds the position of row row0 + i; the live rows are a
-    // prefix (the host's row count is an upper bound for packed input)
-    const RowPos mine = row_pos(a, row0 + (lane < NBC ? lane : 0));
-    const bool live_row = lane < NBC && row0 + lane < n_rows && mine.seq < a.n_seq;
-    const int nr = __builtin_popcountll(__ballot(live_row));
-    if (nr == 0) return;
-    auto pos = [&](int i) {   // row row0 + i (uniform i < NBC), read from lane i
-        RowPos p;
-        const uint64_t bos = mine.bos;
-        p.bos = ((uint64_t)(unsigned)__builtin_amdgcn_readlane((unsigned)(bos >> 32), i) << 32) |
-                (unsigned)__builtin_amdgcn_readlane((unsigned)bos, i);
-        p.x = __builtin_amdgcn_readlane(mine.x, i);
-        p.len = __builtin_amdgcn_readlane(mine.len, i);
-        p.seq = __builtin_amdgcn_readlane(mine.seq, i);
-        return p;
-    };
-    auto prow = [&](int i) { return ws + (size_t)((row0 + i) * a.H + head) * P::BYTES; };
-
-    if (wv == NPW) {
-        // the INV wave: stage B1 of row it + 1 in iteration it
-        for (int it = -2; it < nr; ++it) {
-            const int i = it + 1;
-            if (i >= 0 && i < nr)
-                stage_b1<NPW>(l_part + (i & 1) * (PART / 16), l_beta + (i & 1) * 16, l_ib + (i & 1) * 512,
-                              prow(i) + P::MQ, lane);
-            lds_barrier();
-        }
-        return;
-    }
-    Prep<DK, 0> pr;
-    pr.init(a, head, wv, lane);
-    auto load = [&](In<0> &in, int i) {
-        const RowPos p = pos(i);
+    const long long item = (long long)blockIdx.x * PREP_WAVES + wv;
+    const long long row = item / a.H;
+    const int head = (int)(item - row * a.H);
+    if (row >= n_rows) return;
+    const RowPos p = row_pos(a, row);   // the host's row count is an upper bound for packed input
+    if (p.seq >= a.n_seq) return;
+    unsigned char *pw = ws + (size_t)(row * a.H + head) * P::BYTES;
+    const int rem = min(CH, p.len - p.x * CH);
+    f32x4 Lm = Z4, LT = Z4, MT = Z4;
+    bf16x4 kt[NMT];
+    float beta = 0.f;
+#pragma unroll
+    for (int w = 0; w < NPW; ++w) {
+        Prep<DK, 0> pr;
+        pr.init(a, head, w, lane);
+        In<0> in;
         pr.load(in, a, p.bos, p.len, p.x, head, 0, 0, 0, 0);
-    };
-    In<0> in0, in1;
-    load(in0, 0);
-    // row i's inputs sit in in[i & 1]; stage A of row it + 2, B2 of row it in iteration it
-    auto body = [&](int it, In<0> &use, In<0> &fill) {
-        vm_wait_all();
-        if (it + 3 < nr) load(fill, it + 3);
-        const int ia = it + 2;
-        if (ia < nr) {
-            const RowPos p = pos(ia);
-            unsigned char *pw = prow(ia);
-            pr.stage_a(use, min(CH, p.len - p.x * CH), pw + P::QF, reinterpret_cast<float *>(pw + P::EG), pw + P::KR,
-                       l_kt + (ia % 3) * KT, nullptr, 0, 0, l_part + (ia & 1) * (PART / 16), l_beta + (ia & 1) * 16);
+        typename Prep<DK, 0>::Out o;
+        pr.stage_a_core(in, rem, o);
+        *reinterpret_cast<bf16x8 *>(pw + P::QF + (w * 64 + lane) * 16) = o.bqd;
+        pr.store_eg(o, reinterpret_cast<float *>(pw + P::EG));
+        Lm += o.pL;
+        LT += o.pLT;
+        MT += o.pMT;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            kt[2 * w + h] = pr.ctile(o.bkd, h);
+            *reinterpret_cast<bf16x4 *>(pw + P::KR + ((2 * w + h) * 64 + lane) * 8) = pr.ctile(o.bkr, h);
         }
-        const int ib = it;
-        if (wv > 0 && ib >= 0 && ib < nr) {
-            const bf16x4 ibv = *reinterpret_cast<const bf16x4 *>(l_ib + (ib & 1) * 512 + lane * 8);
-            unsigned char *pw = prow(ib);
-            for (int s = wv - 1; s < NKB; s += NPW - 1)
-                *reinterpret_cast<bf16x8 *>(pw + P::WF + (s * 64 + lane) * 16) =
-                    w_frag(l_kt + (ib % 3) * KT, ibv, s, lane);
-            if (wv == 1) *reinterpret_cast<bf16x4 *>(pw + P::IB + lane * 8) = ibv;
-        }
-        lds_barrier();
-    };
-    for (int it = -2; it < nr; it += 2) {
-        body(it, in0, in1);
-        if (it + 1 < nr) body(it + 1, in1, in0);
+        if (w == 0) beta = ln < rem ? sigmoid_f(bf16_to_f32(in.b)) : 0.f;
     }
+    // beta of tokens 4 lq .. +3 and of token ln, through this wave's LDS row
+    if (lq == 0) l_beta[wv][ln] = beta;
+    __builtin_amdgcn_wave_barrier();
+    const f32x4 brow = *reinterpret_cast<const f32x4 *>(&l_beta[wv][4 * lq]);
+    const float bcol = l_beta[wv][ln];
+    bf16x4 ib, mq;
+    b1_core(Lm, LT, MT, brow, bcol, lane, ib, mq);
+    *reinterpret_cast<bf16x4 *>(pw + P::MQ + lane * 8) = mq;
+    *reinterpret_cast<bf16x4 *>(pw + P::IB + lane * 8) = ib;
+#pragma unroll
+    for (int s2 = 0; s2 < NKB; ++s2)
+        *reinterpret_cast<bf16x8 *>(pw + P::WF + (s2 * 64 + lane) * 16) = w_frag2(kt[2 * s2], kt[2 * s2 + 1], ib);
 }
 
 // Pass 2: one wave per (sequence, head, SPW slabs of 16 columns).  Workgroup
@@ -1057,11 +1064,10 @@ hipError_t launch_one_pass(const FwdArgs &a, int n_cu, hipStream_t stream)
 template <int DK, int DV, bool SNAP>
 hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows, hipStream_t stream)
 {
-    const long long wgs1 = ((n_rows + NBC - 1) / NBC) * a.H;
+    const long long wgs1 = (n_rows * a.H + PREP_WAVES - 1) / PREP_WAVES;
     if (wgs1 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (wgs1 > 0) {
-        hipLaunchKernelGGL((prep_kernel<DK>), dim3((unsigned)wgs1), dim3(64 * (DK / 32 + 1)), 0, stream, a, ws,
-                           n_rows);
+        hipLaunchKernelGGL((prep_kernel<DK>), dim3((unsigned)wgs1), dim3(64 * PREP_WAVES), 0, stream, a, ws, n_rows);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
