@@ -67,3 +67,47 @@ def assert_close(got, ref, dtype, what=""):
     if tol["rel_rmse"] is not None:
         assert m["rel_rmse"] <= tol["rel_rmse"], msg
     return m
+
+
+class ErrAcc:
+    """Error metrics accumulated over batches: the same max-abs and RMSE/RMS
+    as metrics() over the concatenation of every batch."""
+
+    def __init__(self):
+        self.max_abs, self.sq_err, self.sq_ref, self.finite, self.n = 0.0, 0.0, 0.0, True, 0
+
+    def add(self, got, ref):
+        got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+        err = got - ref
+        if err.size:
+            self.max_abs = max(self.max_abs, float(np.max(np.abs(err))))
+        self.sq_err += float(np.sum(err * err))
+        self.sq_ref += float(np.sum(ref * ref))
+        self.finite &= bool(np.isfinite(got).all())
+        self.n += err.size
+
+    def check(self, dtype, what=""):
+        m = dict(max_abs=self.max_abs, rel_rmse=float(np.sqrt(self.sq_err / self.sq_ref)) if self.sq_ref > 0 else 0.0,
+                 finite=self.finite, elements=self.n)
+        tol = TOL[dtype]
+        msg = f"{what}: {m} tol {tol}"
+        assert m["finite"], msg
+        assert m["max_abs"] <= tol["max_abs"], msg
+        if tol["rel_rmse"] is not None:
+            assert m["rel_rmse"] <= tol["rel_rmse"], msg
+        return m
+
+
+def full_parity(p: synth.Prefill, o, hT, batch: int):
+    """Every element of the device outputs o ([B, T, H, dv] or [1, tokens, H,
+    dv]) and final states hT ([n_seq, H, dv, dk]) against the oracle, which
+    runs over `batch` heads at a time to bound host memory."""
+    eo, eh = ErrAcc(), ErrAcc()
+    o3 = o.reshape(p.tokens, p.H, p.dv)
+    for h0 in range(0, p.H, batch):
+        heads = list(range(h0, min(p.H, h0 + batch)))
+        ro, rh = run_oracle(p, heads)
+        eo.add(o3[:, heads].float().cpu().numpy(), ro)
+        eh.add(hT[:, heads].cpu().numpy(), rh)
+        del ro, rh
+    return eo, eh

@@ -10,7 +10,7 @@ import torch
 
 import kimi_delta_attention_kda_amd as kda
 import synth
-from kda_testlib import assert_close, metrics, run_gpu, run_oracle, to_device
+from kda_testlib import assert_close, full_parity, metrics, run_gpu, run_oracle, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -90,20 +90,26 @@ def test_workload1_full():
     check(synth.prefill_workload(1), what="prefill-bf16 B4 H16 T4096")
 
 
-@pytest.fixture(scope="module")
-def w2():
-    return synth.prefill_workload(2)
+def check_full(w, batch):
+    """A whole workload, every output element and final state against the
+    oracle (run in head batches), in the launch configuration the benchmark
+    times (default workspace)."""
+    p = synth.prefill_workload(w)
+    say(p.name, "tokens", p.tokens, "H", p.H, "full parity, oracle batches of", batch, "heads")
+    d = to_device(p)
+    o, hT = kda.chunk_fwd(**d, scale=p.scale)
+    assert kda.device_check() == 0
+    eo, eh = full_parity(p, o, hT, batch)
+    mo, mh = eo.check(p.dtype, p.name + " o"), eh.check(p.dtype, p.name + " h_T")
+    say("  o", mo, " h_T", mh)
 
 
-def test_workload2_sampled(w2):
-    lengths = np.diff(w2.offsets())
-    seqs = sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), 5, 17})
-    check(w2, heads=[0, 19], seqs=seqs, what="varlen-bf16 32 seqs (2 heads x 4 seqs sampled)")
+def test_workload2_full():
+    check_full(2, batch=8)
 
 
-def test_workload3_sampled():
-    p = synth.prefill_workload(3)
-    check(p, heads=[0, 13, 31], what="long-bf16 T131072 (3 heads sampled)")
+def test_workload3_full():
+    check_full(3, batch=16)
 
 
 def test_deterministic_and_continuation():
