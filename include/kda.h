@@ -72,7 +72,8 @@ typedef enum {
     KDA_ERR_UNSUPPORTED = -3, /* valid but not built (head dim, chunk size, dtype) */
     KDA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
     KDA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
-    KDA_ERR_SLOT = -6         /* a kernel met a pool slot index >= P (see kda_device_check) */
+    KDA_ERR_SLOT = -6,        /* a kernel met a pool slot index >= P (see kda_device_check) */
+    KDA_ERR_SCRATCH = -7      /* kda_chunk_fwd_noalloc: more workspace needed than its scratch holds */
 } kda_status;
 
 typedef enum {
@@ -150,6 +151,33 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v,
  * an upper bound: the lengths live in device memory).  0 for invalid sizes.
  */
 size_t kda_chunk_fwd_workspace_bytes(int B, int T, int H, int dk, int dv, int n_seq, int packed);
+
+/*
+ * kda_chunk_fwd_noalloc -- kda_chunk_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, layouts and results as kda_chunk_fwd
+ * (bitwise: it launches the same kernels), without a workspace argument.
+ * Where kda_chunk_fwd would take its two-pass form, this entry point uses a
+ * fixed device array of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) as the workspace,
+ * and nothing else: no allocation, no library routine that allocates.  Each
+ * GPU the library runs on holds one such array until the process ends; the
+ * first call on a device looks up its address.  All calls on one GPU share
+ * that array, so calls that overlap on one GPU (two streams, two threads)
+ * race and must be serialised by the caller.  The array needs no clearing:
+ * every workspace byte a call reads was written earlier in the same call.
+ * Returns KDA_ERR_SCRATCH, launching nothing, when the two-pass form would
+ * need more than the array (kda_chunk_fwd_workspace_bytes() above
+ * KDA_NOALLOC_SCRATCH_BYTES: at d_k = 128, 4,854 chunk rows x heads); else as
+ * kda_chunk_fwd.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                          const void *g_raw, const void *beta_raw,
+                          const float *A_log, const float *dt_bias,
+                          const float *h0, const int32_t *cu_seqlens, int chunk,
+                          void *o, float *h_T,
+                          int B, int T, int H, int dk, int dv, int n_seq,
+                          float scale, kda_dtype dtype, hipStream_t stream);
 
 /*
  * kda_chunk_fwd_states -- kda_chunk_fwd that also writes the state entering

@@ -19,7 +19,7 @@ _lib = None
 KDA_F32, KDA_BF16 = 0, 1
 KDA_DECODE_L2NORM = 1
 
-EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_pool", "kda_chunk_fwd_states",
+EXPORTS = ("kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd_pool", "kda_chunk_fwd_states",
            "kda_device_check", "kda_decode_step",
            "kda_decode_extend", "kda_conv_decode_step", "kda_chunk_o", "kda_backward", "kda_backward_workspace_bytes",
            "kda_status_str")
@@ -42,6 +42,8 @@ def load_library(path: str = LIB_PATH):
     Z = ctypes.c_size_t
     lib.kda_chunk_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, F, I, P, Z, P]
     lib.kda_chunk_fwd.restype = I
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, P, P, I, I, I, I, I, I, F, I, P]
+    lib.kda_chunk_fwd_noalloc.restype = I
     lib.kda_chunk_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.kda_chunk_fwd_workspace_bytes.restype = Z
     lib.kda_chunk_fwd_pool.argtypes = [P, P, P, P, P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, Z, P]
@@ -130,17 +132,9 @@ def _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq):
             raise KDAError(f"{name} must hold [N, H, dv, dk] elements")
 
 
-def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
-              chunk: int = 16, scale=None, output_final_state: bool = True,
-              o=None, h_T=None, stream=None, workspace="auto"):
-    """Chunkwise KDA prefill.
-
-    q, k, g_raw: [B, T, H, dk]; v: [B, T, H, dv]; beta_raw: [B, T, H] -- all
-    float32 or all bfloat16 (q, k L2-normalised by the caller).
-    A_log: [H] float32; dt_bias: [H, dk] float32.
-    h0: [N, H, dv, dk] float32 or None.  cu_seqlens: [N+1] int32 (then B == 1).
-    workspace: "auto", None (one-pass form) or a uint8 GPU tensor (see _workspace).
-    Returns (o [B, T, H, dv], h_T [N, H, dv, dk] float32 or None)."""
+def _prefill_outputs(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, cu_seqlens, scale, output_final_state, o, h_T):
+    """Shared argument checks of the prefill entry points: returns
+    (B, T, H, dk, dv, n_seq, act, scale, o, h_T) with o / h_T allocated if None."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     act = q.dtype
@@ -164,6 +158,22 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None
         h_T = torch.empty((n_seq, H, dv, dk), dtype=torch.float32, device=q.device)
     _dev("h_T", h_T, torch.float32)
     _state_shapes(o, h0, h_T, B, T, H, dk, dv, n_seq)
+    return B, T, H, dk, dv, n_seq, act, scale, o, h_T
+
+
+def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
+              chunk: int = 16, scale=None, output_final_state: bool = True,
+              o=None, h_T=None, stream=None, workspace="auto"):
+    """Chunkwise KDA prefill.
+
+    q, k, g_raw: [B, T, H, dk]; v: [B, T, H, dv]; beta_raw: [B, T, H] -- all
+    float32 or all bfloat16 (q, k L2-normalised by the caller).
+    A_log: [H] float32; dt_bias: [H, dk] float32.
+    h0: [N, H, dv, dk] float32 or None.  cu_seqlens: [N+1] int32 (then B == 1).
+    workspace: "auto", None (one-pass form) or a uint8 GPU tensor (see _workspace).
+    Returns (o [B, T, H, dv], h_T [N, H, dv, dk] float32 or None)."""
+    B, T, H, dk, dv, n_seq, act, scale, o, h_T = _prefill_outputs(
+        q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, cu_seqlens, scale, output_final_state, o, h_T)
     wsp, wsb = _workspace(workspace, act, B, T, H, dk, dv, n_seq, cu_seqlens is not None, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -171,6 +181,27 @@ def chunk_fwd(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None
         _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
         _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), B, T, H, dk, dv, n_seq,
         float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, wsp, wsb, ctypes.c_void_p(stream)))
+    return o, h_T
+
+
+def chunk_fwd_noalloc(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0=None, cu_seqlens=None,
+                      chunk: int = 16, scale=None, o=None, h_T=None, stream=None):
+    """kda_chunk_fwd_noalloc: chunk_fwd with its workspace taken from the
+    library's fixed device array (NOALLOC_SCRATCH_BYTES per GPU) instead of an
+    allocation.  o and h_T must be passed (this call allocates nothing); h_T may
+    be None only if the final states are not wanted.  Calls that overlap on one
+    GPU race.  Raises KDAError (KDA_ERR_SCRATCH) when the two-pass form would
+    need more than the array."""
+    if o is None:
+        raise KDAError("chunk_fwd_noalloc allocates nothing: pass o (and h_T)")
+    B, T, H, dk, dv, n_seq, act, scale, o, h_T = _prefill_outputs(
+        q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, cu_seqlens, scale, False, o, h_T)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(load_library().kda_chunk_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_raw), _ptr(A_log), _ptr(dt_bias),
+        _ptr(h0), _ptr(cu_seqlens), chunk, _ptr(o), _ptr(h_T), B, T, H, dk, dv, n_seq,
+        float(scale), KDA_BF16 if act == torch.bfloat16 else KDA_F32, ctypes.c_void_p(stream)))
     return o, h_T
 
 
@@ -219,6 +250,8 @@ def chunk_fwd_pool(q, k, v, g_raw, beta_raw, A_log, dt_bias, state_pool, state_i
 
 
 KDA_ERR_SLOT = -6
+KDA_ERR_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 
 
 def device_check(stream=None) -> int:

@@ -1,9 +1,10 @@
 // kda_api.hip -- extern "C" entry points of libkda (see include/kda.h):
 // argument validation on the host, then kernel launches on the caller's
-// stream.  No device allocation and no synchronisation.  The one piece of
-// library state is a per-device error word in device memory, which kernels
-// set when they meet an invalid slot index in device memory and which
-// kda_device_check reads and clears.
+// stream.  No device allocation and no synchronisation.  Library state lives
+// in two device-memory variables, each existing once per GPU: the error word
+// (kernels set it when they meet an invalid slot index in device memory;
+// kda_device_check reads and clears it) and the static scratch array that
+// kda_chunk_fwd_noalloc uses as its workspace.
 #include <stdint.h>
 
 #include <mutex>
@@ -40,6 +41,32 @@ hipError_t error_word(int **out)
     return hipSuccess;
 }
 
+// The workspace of kda_chunk_fwd_noalloc: a fixed array in device memory, one
+// per GPU the library runs on, held until the process ends.  Host code never
+// uses the array's name as an address (on the host it names a stand-in): it
+// takes each device's address once, with hipGetSymbolAddress, and passes that.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_ptr(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 // Chunk rows of a prefill (sum over sequences of ceil(len / 16)): exact for
 // dense input, an upper bound for packed input (whose lengths live in device
 // memory): each sequence adds at most one partial chunk.
@@ -63,6 +90,7 @@ const char *kda_status_str(int status)
     case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case KDA_ERR_HIP: return "HIP launch error";
     case KDA_ERR_SLOT: return "a kernel met a pool slot index >= P (treated as a pad row)";
+    case KDA_ERR_SCRATCH: return "the call needs more workspace than the static scratch (KDA_NOALLOC_SCRATCH_BYTES) holds";
     default: return "unknown status";
     }
 }
@@ -124,6 +152,36 @@ int kda_chunk_fwd(const void *q, const void *k, const void *v, const void *g_raw
 {
     return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
                           h_T, nullptr, B, T, H, dk, dv, n_seq, 0, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+int kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const void *g_raw,
+                          const void *beta_raw, const float *A_log, const float *dt_bias,
+                          const float *h0, const int32_t *cu_seqlens, int chunk, void *o, float *h_T,
+                          int B, int T, int H, int dk, int dv, int n_seq, float scale,
+                          kda_dtype dtype, hipStream_t stream)
+{
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    // the bf16 form takes its workspace from the static scratch when it would run
+    // in two passes; invalid sizes fall through to kda_chunk_fwd's own checks
+    bool sane = chunk == 16 && dtype == KDA_BF16 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128) &&
+                B >= 0 && T >= 0 && H > 0 && n_seq > 0 && (long long)n_seq * H * 2 <= 0x7fffffffLL &&
+                (cu_seqlens ? B == 1 : n_seq == B) &&
+                q && k && v && g_raw && beta_raw && o && A_log && dt_bias;
+    const void *ptrs[] = {q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, o, h_T, cu_seqlens};
+    for (const void *p : ptrs) sane = sane && (!p || aligned16(p));
+    if (sane) {
+        bool two = false;
+        if (kda::fwd_two_pass_eligible((long long)n_seq * H, &two) != hipSuccess) return KDA_ERR_HIP;
+        if (two) {
+            const size_t need = kda::fwd_workspace_bytes(dk, chunk_rows(B, T, n_seq, cu_seqlens != nullptr), H);
+            if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+            if (scratch_ptr(&ws) != hipSuccess) return KDA_ERR_HIP;
+            ws_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+        }
+    }
+    return chunk_fwd_impl(q, k, v, g_raw, beta_raw, A_log, dt_bias, h0, nullptr, cu_seqlens, chunk, o,
+                          h_T, nullptr, B, T, H, dk, dv, n_seq, 0, scale, dtype, ws, ws_bytes, stream);
 }
 
 int kda_chunk_fwd_states(const void *q, const void *k, const void *v, const void *g_raw,

@@ -1099,6 +1099,17 @@ size_t fwd_workspace_bytes(int dk, long long n_rows, int H)
     return per * (size_t)(n_rows < 0 ? 0 : n_rows) * (size_t)(H < 0 ? 0 : H);
 }
 
+hipError_t fwd_two_pass_eligible(long long chains, bool *two)
+{
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    *two = chains < n_cu;
+    return hipSuccess;
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs &a, int dk, int dv, void *ws, size_t ws_bytes, long long n_rows,
                            hipStream_t stream)
 {

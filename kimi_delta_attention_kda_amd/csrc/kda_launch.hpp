@@ -50,6 +50,9 @@ struct FwdArgs {
 };
 // bf16: one pass, or (with a workspace of at least fwd_workspace_bytes for
 // n_rows chunk rows, and chains fewer than the compute units) two passes.
+// Whether the bf16 prefill takes its two-pass form for this many (sequence,
+// head) chains on the current device (given a large enough workspace).
+hipError_t fwd_two_pass_eligible(long long chains, bool *two);
 size_t fwd_workspace_bytes(int dk, long long n_rows, int H);
 hipError_t launch_fwd_bf16(const FwdArgs &a, int dk, int dv, void *ws, size_t ws_bytes, long long n_rows,
                            hipStream_t stream);

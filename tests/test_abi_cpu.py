@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.kda_status_str(code)
     assert lib.kda_status_str(0) == b"ok"
 
@@ -68,6 +68,27 @@ def test_chunk_validation(lib):
     assert chunk(lib, o=MIS) == -4
     assert chunk(lib, ws=MIS, wsb=1 << 20) == -4    # a workspace must be aligned too
     assert chunk(lib, n_seq=0, B=0) == 0            # nothing to do, no launch
+
+
+def chunk_noalloc(lib, **kw):
+    args = dict(q=A, k=A, v=A, g=A, b=A, A_log=B, dt=B, h0=None, cu=None, chunk=16, o=A,
+                hT=None, B=1, T=16, H=1, dk=128, dv=128, n_seq=1, scale=0.1, dtype=1)
+    args.update(kw)
+    return lib.kda_chunk_fwd_noalloc(*(args[k_] for k_ in ("q", "k", "v", "g", "b", "A_log", "dt", "h0", "cu",
+                                                          "chunk", "o", "hT", "B", "T", "H", "dk", "dv", "n_seq",
+                                                          "scale", "dtype")), None)
+
+
+def test_chunk_noalloc_validation(lib):
+    """The allocation-free variant rejects what kda_chunk_fwd rejects, before
+    it touches the GPU (its scratch-size check needs the device)."""
+    assert chunk_noalloc(lib, chunk=32) == -3
+    assert chunk_noalloc(lib, dk=96) == -3
+    assert chunk_noalloc(lib, H=0) == -2
+    assert chunk_noalloc(lib, n_seq=2) == -2
+    assert chunk_noalloc(lib, q=None) == -1
+    assert chunk_noalloc(lib, o=MIS) == -4
+    assert chunk_noalloc(lib, n_seq=0, B=0) == 0
 
 
 def test_chunk_workspace_bytes(lib):
