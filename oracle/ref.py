@@ -229,65 +229,89 @@ def chunkwise(q, k, v, a, b, A_log, dt_bias, h0=None, cu_seqlens=None, scale=Non
 
 
 # ----------------------------------------------------------------------------
-# Level-1 references (no gate, no delta: S <- S + k v^T, o = q^T S) from
-# [TL-KDA] section 3.  Shapes [B, N, H, D] as on the page.
+# Level-1 references: the ungated accumulation S_t = S_{t-1} + k_t v_t^T with
+# o_t = S_t^T q_t ([TL-KDA] section 2.1), in three structures whose agreement
+# is the check of section 3.4.  Its chunk identity: with S_prev the sum of
+# k v^T over every token before chunk c,
+#     O_c = Q_c S_prev + tril(Q_c K_c^T) V_c.
+# Inputs [B, N, H, D] (values [B, N, H, DV]); each head is handled alone.
 # ----------------------------------------------------------------------------
-def level1_recurrent(Q, K, V):
-    """Reference A: double token loop."""
+def _each_head(fn, Q, K, V, *extra):
+    """Apply fn(q [N, D], k [N, D], v [N, DV], *extra) -> [N, DV] to every
+    (batch, head) and reassemble [B, N, H, DV]."""
     Q, K, V = (np.asarray(x, F64) for x in (Q, K, V))
-    B, N, H, D = Q.shape
-    O = np.zeros((B, N, H, V.shape[-1]))
-    for bb in range(B):
-        for h in range(H):
-            S = np.zeros((D, V.shape[-1]))
-            for t in range(N):
-                S += np.outer(K[bb, t, h], V[bb, t, h])
-                O[bb, t, h] = Q[bb, t, h] @ S
-    return O
+    out = np.empty(Q.shape[:-1] + (V.shape[-1],))
+    for bb, h in np.ndindex(Q.shape[0], Q.shape[2]):
+        out[bb, :, h] = fn(Q[bb, :, h], K[bb, :, h], V[bb, :, h], *extra)
+    return out
+
+
+def _tokens(q, k, v):
+    state = np.zeros((k.shape[1], v.shape[1]))
+    res = np.empty((q.shape[0], v.shape[1]))
+    for t in range(q.shape[0]):
+        state += np.outer(k[t], v[t])
+        res[t] = state.T @ q[t]
+    return res
+
+
+def level1_recurrent(Q, K, V):
+    """Token by token: accumulate k_t v_t^T, then read with q_t."""
+    return _each_head(_tokens, Q, K, V)
+
+
+def _chunk_identity(q, k, v, C, inclusive):
+    n = q.shape[0]
+    starts = range(0, n, C)
+    # every chunk's own contribution K_c^T V_c, then the state each chunk sees:
+    # the sum over the chunks before it (inclusive=True also adds its own,
+    # the off-by-one-chunk mistake: the chunk's keys are then counted twice)
+    incr = [k[c0:c0 + C].T @ v[c0:c0 + C] for c0 in starts]
+    seen, running = [], np.zeros((k.shape[1], v.shape[1]))
+    for dS in incr:
+        if inclusive:
+            running = running + dS
+            seen.append(running)
+        else:
+            seen.append(running)
+            running = running + dS
+    res = np.empty((n, v.shape[1]))
+    for c0, S_prev in zip(starts, seen):
+        qc, kc, vc = q[c0:c0 + C], k[c0:c0 + C], v[c0:c0 + C]
+        res[c0:c0 + C] = qc @ S_prev + np.tril(qc @ kc.T) @ vc
+    return res
 
 
 def level1_chunked(Q, K, V, BC, right_shift=True):
-    """Reference B: per-chunk K^T V, prefix sums by cumsum, then a right shift
-    by one chunk so chunk c sees only chunks < c.  right_shift=False is the
-    deliberate bug of [TL-KDA] section 3.4."""
-    Q, K, V = (np.asarray(x, F64) for x in (Q, K, V))
-    B, N, H, D = Q.shape
-    NC = N // BC
-    Qc = Q.transpose(0, 2, 1, 3).reshape(B, H, NC, BC, D)
-    Kc = K.transpose(0, 2, 1, 3).reshape(B, H, NC, BC, D)
-    Vc = V.transpose(0, 2, 1, 3).reshape(B, H, NC, BC, -1)
-    outer = np.einsum("bhcnd,bhcnv->bhcdv", Kc, Vc)
-    states = np.cumsum(outer, axis=2)
-    if right_shift:
-        states = np.concatenate([np.zeros_like(states[:, :, :1]), states[:, :, :-1]], axis=2)
-    inter = np.einsum("bhcnd,bhcdv->bhcnv", Qc, states)
-    A = np.einsum("bhcnd,bhcmd->bhcnm", Qc, Kc) * np.tril(np.ones((BC, BC)))
-    intra = np.einsum("bhcnm,bhcmv->bhcnv", A, Vc)
-    return (inter + intra).reshape(B, H, N, -1).transpose(0, 2, 1, 3)
+    """The chunk identity with every chunk's entering state taken as the sum of
+    the contributions of the chunks before it (all contributions formed
+    first).  right_shift=False includes the chunk's own contribution too: the
+    structural mistake whose error is O(1)."""
+    return _each_head(_chunk_identity, Q, K, V, BC, not right_shift)
+
+
+def _slab_walk(q, k, v, C, slab, read_first):
+    n, dv = q.shape[0], v.shape[1]
+    res = np.empty((n, dv))
+    for j0 in range(0, dv, slab):                      # each slab of value columns alone
+        cols = slice(j0, min(dv, j0 + slab))
+        S = np.zeros((k.shape[1], cols.stop - cols.start))
+        for c0 in range(0, n, C):                      # sequential walk over the chunks
+            qc, kc, vc = q[c0:c0 + C], k[c0:c0 + C], v[c0:c0 + C, cols]
+            if not read_first:                         # the mistake: advance before reading
+                S = S + kc.T @ vc
+            res[c0:c0 + C, cols] = qc @ S + np.tril(qc @ kc.T) @ vc
+            if read_first:
+                S = S + kc.T @ vc
+    return res
 
 
 def level1_dv_slab(Q, K, V, BC, block_dv, update_after_write=True):
-    """Reference D: grid over (b, h, dv-slab), sequential chunk loop carrying
-    the state slab; the state update follows the output write-back.
-    update_after_write=False is the deliberate bug of [TL-KDA] section 3.4."""
-    Q, K, V = (np.asarray(x, F64) for x in (Q, K, V))
-    B, N, H, D = Q.shape
-    DV = V.shape[-1]
-    O = np.zeros((B, N, H, DV))
-    mask = np.tril(np.ones((BC, BC)))
-    for bb in range(B):
-        for h in range(H):
-            for v0 in range(0, DV, block_dv):
-                S = np.zeros((D, min(block_dv, DV - v0)))
-                for c0 in range(0, N, BC):
-                    Qb, Kb = Q[bb, c0:c0 + BC, h], K[bb, c0:c0 + BC, h]
-                    Vb = V[bb, c0:c0 + BC, h, v0:v0 + block_dv]
-                    if not update_after_write:
-                        S = S + Kb.T @ Vb
-                    O[bb, c0:c0 + BC, h, v0:v0 + block_dv] = Qb @ S + ((Qb @ Kb.T) * mask) @ Vb
-                    if update_after_write:
-                        S = S + Kb.T @ Vb
-    return O
+    """The chunk identity walked chunk by chunk, each slab of block_dv value
+    columns carrying its own slice of the state; the chunk's output is read
+    before the state advances.  update_after_write=False advances first: the
+    structural mistake whose error is O(1)."""
+    return _each_head(_slab_walk, Q, K, V, BC, block_dv, update_after_write)
 
 
 def parallel_form(Q, K, V, scale=1.0):
