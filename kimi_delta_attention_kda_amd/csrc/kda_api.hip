@@ -280,7 +280,7 @@ int kda_backward(const void *q, const void *k, const void *v, const void *g_raw,
     a.A_log = A_log; a.dt_bias = dt_bias; a.h_chunks = h_chunks; a.dh_T = dh_T; a.cu_seqlens = cu_seqlens;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg_raw = dg_raw; a.dbeta_raw = dbeta_raw;
     a.dA_log = dA_log; a.ddt_bias = ddt_bias; a.dh0 = dh0;
-    a.work = static_cast<float *>(workspace); a.part = a.part_beta = a.params = nullptr;
+    a.work = workspace;
     a.T = T; a.H = H; a.n_seq = n_seq; a.T_all = tokens; a.scale = scale;
     const hipError_t e = kda::launch_bwd(a, dtype == KDA_BF16 ? 1 : 0, stream);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;

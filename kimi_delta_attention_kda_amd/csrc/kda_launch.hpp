@@ -75,12 +75,24 @@ struct BwdArgs {
     const int32_t *cu_seqlens;
     void *dq, *dk, *dv, *dg_raw, *dbeta_raw;
     float *dA_log, *ddt_bias, *dh0;
-    float *work;          // caller's workspace: the partial sums below
-    float *part, *part_beta, *params;   // set by the launcher (inside work)
+    void *work;           // caller's workspace (bwd_workspace_bytes)
     int T, H, n_seq;      // T: per-sequence length for dense input, total tokens if cu_seqlens
     long long T_all;      // total tokens
     float scale;
 };
+// The chunkwise backward (kda_fwd.hip), bf16 and d = 128: the reverse
+// chain's operands for every chunk, the reverse chain over the chunks of each
+// (sequence, head) (dh0 and a gradient row per chunk), then every chunk's
+// gradients in parallel and its parameter sums (at BwdWs::part, [n_rows][H][129]),
+// which the reduction (kda_backward.hip) sums in BWD_SPLIT slices of rows (at
+// BwdWs::red) and then over the slices.  n_rows bounds the chunk rows (rows
+// past the sequences' chunks get zero sums).
+constexpr int BWD_SPLIT = 64;
+struct BwdWs {
+    size_t pay, grow, part, red, bytes;
+};
+BwdWs bwd_ws_layout(long long n_rows, int H);
+hipError_t launch_bwd_chunkwise(const BwdArgs &b, long long n_rows, hipStream_t stream);
 size_t bwd_workspace_bytes(int n_seq, int H, long long tokens);
 hipError_t launch_bwd(const BwdArgs &a, int dtype, hipStream_t stream);
 

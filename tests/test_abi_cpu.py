@@ -230,8 +230,13 @@ def backward(lib, **kw):
 
 
 def test_backward_validation(lib):
-    # quarter column sums and beta terms per (token, head), block sums per 16 tokens
-    assert lib.kda_backward_workspace_bytes(2, 3, 128, 128, 100) == 4 * (4 * 100 * 3 * (3 * 128 + 1) + 7 * 3 * 129)
+    # per (chunk row, head), for ceil(100 / 16) + 2 rows (at most one partial chunk per
+    # sequence): the chunk's operands (14,336 bytes, rounded up to 256 in all), a
+    # gradient row (40,960 bytes) and the parameter sums (129 floats); per head, 64
+    # slices of those sums
+    items = (7 + 2) * 3
+    assert lib.kda_backward_workspace_bytes(2, 3, 128, 128, 100) == \
+        ((items * 14336 + 255) // 256) * 256 + items * 40960 + items * 129 * 4 + 3 * 64 * 129 * 4
     assert lib.kda_backward_workspace_bytes(2, 3, 64, 128, 100) == 0
     assert backward(lib, dtype=0) == -3               # float32 activations: no d = 128 forward to pair with
     assert backward(lib, dk_=64) == -3
