@@ -59,7 +59,7 @@
 //
 // Operand layouts.  For a 16 x 16 tile X the "C layout" is the MFMA
 // accumulator layout: lane (lq, ln) = (lane / 16, lane % 16) holds
-// X[4 lq + i][ln], i = 0..3.  A K = 16 product X Y on v_mfma_f32_16x16x16_bf16
+// X[4 lq + i][ln], i = 0..3.  A K = 16 product X Y in the 16x16x16 bf16 layout
 // takes the C layout of X^T as its A operand and the C layout of Y as its B
 // operand, so chained 16 x 16 products need no data movement.  A K = 32
 // operand of v_mfma_f32_16x16x32_bf16 holds 8 K values per lane; the state
@@ -91,14 +91,28 @@ namespace kda {
 namespace {
 
 constexpr int CH = 16;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
 __device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// A K = 16 product (the v_mfma_f32_16x16x16_bf16 operand layout: lane (lq, ln)
+// holds A[ln][4 lq .. +3] and B[4 lq .. +3][ln]) issued as v_mfma_f32_16x16x32_bf16
+// with the upper four K values of every lane zero: the same sum, and on gfx950
+// the same issue rate.  The 16x16x16 instruction itself gave wrong results in
+// some instruction sequences here (a 16x16 product of selector copies came out
+// wrong in its second channel tile while the same code built on the K = 32
+// instruction was exact to fp32 rounding), so no kernel uses it.
 __device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
-                                                     c, 0, 0, 0);
+    const bf16x4 z = {};
+    bf16x8 a8, b8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a8[i] = a[i];
+        a8[4 + i] = z[i];
+        b8[i] = b[i];
+        b8[4 + i] = z[i];
+    }
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, c, 0, 0, 0);
 }
 constexpr f32x4 Z4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -1271,6 +1285,21 @@ __device__ __forceinline__ float gate2(float z, float A, bool live) {
     return live ? -A * sp2 : 0.f;
 }
 
+// x = hi + lo with hi = RNE(x), lo = RNE(x - hi), both bf16 (~2^-16 relative).
+__device__ __forceinline__ void split_bf16(float x, __bf16 &hi, __bf16 &lo) {
+    hi = static_cast<__bf16>(x);
+    lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8 &hi, bf16x8 &lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        __bf16 h, l;
+        split_bf16(x[e], h, l);
+        hi[e] = h;
+        lo[e] = l;
+    }
+}
+
 struct BwdOut {
     void *dq, *dk, *dv, *dg, *db;
     float *part;    // [chunk row][H][DK + 1]: the chunk's sums of d dt_bias (DK channels) and d A_log
@@ -1302,12 +1331,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
                                                          const unsigned char *grows, const void *dO, BwdOut out)
 {
     static_assert(DK == 128 && DV == 128, "d = 128");
-    constexpr int NVT = DV / 16, LDR = DK + 4, LDB = DK + 8;
+    constexpr int NVT = DV / 16;
     using P = BPay<DK>;
-    __shared__ __attribute__((aligned(16))) float Dr[CH][LDR];
-    __shared__ __attribute__((aligned(16))) uint16_t Kr[CH][LDB], Qr[CH][LDB];
     __shared__ float LA[CH][CH + 1], PP[CH][CH + 1], QQ[CH][CH + 1];
     __shared__ float bs[CH], dbp[4][CH], red[4];
+    __shared__ __attribute__((aligned(16))) float RF[4][4][32];   // per wave: block references of its channels
     // one region, two lives (a barrier between): the per-wave partials of W,
     // then U^T, (beta dy)^T and the per-wave 16 x 16 partials
     __shared__ __attribute__((aligned(16))) unsigned char big[4 * NVT * 64 * 16];
@@ -1357,27 +1385,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     float z[8], G2[8];
     bool deep = false;
     {
-        const uint32_t ka[4] = {kw.x, kw.y, kw.z, kw.w}, qa[4] = {qw.x, qw.y, qw.z, qw.w},
-                       aa[4] = {aw.x, aw.y, aw.z, aw.w};
-        float dd[8];
-        (void)ka;
-        (void)qa;
+        const uint32_t aa[4] = {aw.x, aw.y, aw.z, aw.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int sh = 16 * (e & 1);
             z[e] = bf16_to_f32((uint16_t)(aa[e >> 1] >> sh)) + a.dt_bias[(size_t)head * DK + c0 + e];
-            const float g2 = gate2(z[e], A, live);
-            dd[e] = __builtin_amdgcn_exp2f(g2);
-            G2[e] = scan16(g2);
-            deep |= row_bcast<15>(G2[e]) < -100.f;
+            G2[e] = scan16(gate2(z[e], A, live));
+            deep |= row_bcast<0>(G2[e]) - row_bcast<15>(G2[e]) > 200.f;
         }
-        deep = __ballot(deep) != 0;   // wave-uniform: the factored form would leave the fp32 range
-        if (deep) {
-            *reinterpret_cast<f32x4 *>(&Dr[t][c0]) = f32x4{dd[0], dd[1], dd[2], dd[3]};
-            *reinterpret_cast<f32x4 *>(&Dr[t][c0 + 4]) = f32x4{dd[4], dd[5], dd[6], dd[7]};
-            *reinterpret_cast<uint4 *>(&Kr[t][c0]) = kl;
-            *reinterpret_cast<uint4 *>(&Qr[t][c0]) = ql;
-        }
+        deep = __ballot(deep) != 0;   // wave-uniform: a single reference would leave the fp32 range
     }
     if (tid < CH) bs[tid] = tid < nt ? sigmoid_f(bf16_to_f32(braw)) : 0.f;
     if (w == 0) {
@@ -1535,35 +1551,69 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     }
 
     // ---- pair terms: RP, RM, CC as above and pG, their share of dG,
-    // k (R^P - C^P) + q R^M - k C^M
+    // k (R^P - C^P) + q R^M - k C^M.  E_ij = 2^{l_i - r} 2^{r - l_j} is split
+    // at a reference r into a row and a column factor, so the sums are 16 x 16
+    // products over tokens (transposed: they land in this lane's token and
+    // channels).  Where no channel of the wave decays by more than 2^-200 in
+    // the chunk, l = G and r is the midpoint of G over the chunk: every factor
+    // within 2^100, exact.  Otherwise l is the cumulative decay with each
+    // token's decay clipped at 2^-24 and the tokens form four blocks of 4,
+    // block b with r_b = l at the end of the previous block (0 for the first):
+    // rows of block b take r_b, columns up to the end of block b take r_b,
+    // every factor within 2^96.  A pair whose true decay gap exceeds 2^-24 is
+    // then taken as at most 2^-24 instead of its smaller true value.
+    // Factors, P and Q enter the products as hi + lo bf16 pairs (to ~2^-16).
+    // Every pair adds +X to one token's dG and -X to another's, which cancel
+    // in the cumulative sum over the chunk, so pG takes both sides from the
+    // same factors.  Q's diagonal (whose dG terms cancel exactly) stays out of
+    // the products and is added to dq and dk exactly.
     float RP[8], RM[8], CC[8], pG[8];
-    const float qii = QQ[t][t];
-    if (!deep) {
-        // factored: with kh = k e^-G, R^P = e^G (P kh), R^M = e^G (Q kh) and
-        // C = e^-G (P^T k~ + Q^T q~), all from bf16 kh, k~, q~; transposed
-        // products land in this lane's token and channels.  Every pair adds
-        // +X to one token's dG and -X to another's, which cancel in the
-        // cumulative sum over the chunk, so pG takes both sides from the same
-        // rounded operands: pG = k~ (P kh) + q~ (Q kh) - kh (P^T k~ + Q^T q~).
-        // Q's diagonal (whose dG terms cancel exactly) stays out of the
-        // products and is added to dq and dk exactly.
-        float kh[8], kt[8], qt[8];
+    {
+        const float qii = QQ[t][t];
+        const int bt = deep ? t / 4 : 0;   // this token's block
+        // block references of this lane's channels (the midpoint of G for a
+        // single block, else l at the end of block bb - 1, 0 for the first),
+        // through LDS so that the block loop need not be unrolled
+        float gl[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float eg = __builtin_amdgcn_exp2f(G2[e]);
-            kh[e] = kf(e) * __builtin_amdgcn_exp2f(-G2[e]);
-            kt[e] = kf(e) * eg;
-            qt[e] = qf(e) * eg;
+            gl[e] = deep ? scan16(fmaxf(gate2(z[e], A, live), -24.f)) : G2[e];
+            const float r0 = deep ? 0.f : 0.5f * (row_bcast<0>(G2[e]) + row_bcast<15>(G2[e]));
+            const float r1 = row_bcast<3>(gl[e]), r2 = row_bcast<7>(gl[e]), r3 = row_bcast<11>(gl[e]);
+            // every lane of the row stores the same values: the row broadcasts
+            // must run with the whole row active (a store under a lane test
+            // would let them sink into it and read inactive lanes)
+            RF[w][0][8 * lq + e] = r0;
+            RF[w][1][8 * lq + e] = r1;
+            RF[w][2][8 * lq + e] = r2;
+            RF[w][3][8 * lq + e] = r3;
+            RP[e] = 0.f;
+            RM[e] = qii * kf(e);
+            CC[e] = qii * qf(e);
+            pG[e] = 0.f;
         }
-        bf16x4 cP, cPT, cQ, cQT;   // C(P), C(P^T), C(Q), C(Q^T), Q without its diagonal
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_wave_barrier();
+        // C(P), C(P^T), C(Q), C(Q^T) (Q without its diagonal) as hi + lo bf16
+        bf16x4 cPh, cPl, cPTh, cPTl, cQh, cQl, cQTh, cQTl;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const bool dg = 4 * lq + r == ln;
-            cP[r] = static_cast<__bf16>(PP[4 * lq + r][ln]);
-            cPT[r] = static_cast<__bf16>(PP[ln][4 * lq + r]);
-            cQ[r] = static_cast<__bf16>(dg ? 0.f : QQ[4 * lq + r][ln]);
-            cQT[r] = static_cast<__bf16>(dg ? 0.f : QQ[ln][4 * lq + r]);
+            __bf16 h, l;
+            split_bf16(PP[4 * lq + r][ln], h, l);
+            cPh[r] = h;
+            cPl[r] = l;
+            split_bf16(PP[ln][4 * lq + r], h, l);
+            cPTh[r] = h;
+            cPTl[r] = l;
+            split_bf16(dg ? 0.f : QQ[4 * lq + r][ln], h, l);
+            cQh[r] = h;
+            cQl[r] = l;
+            split_bf16(dg ? 0.f : QQ[ln][4 * lq + r], h, l);
+            cQTh[r] = h;
+            cQTl[r] = l;
         }
+        const bf16x8 bPT = cat4(cPTh, cPTh), bQT = cat4(cQTh, cQTh), bP = cat4(cPh, cPh), bQ = cat4(cQh, cQh);
         // selector: C tile h of a row fragment (rows: tokens; columns: channels
         // c0 + 4 h + i as 4 lq + i of the transposed products)
         bf16x8 sel[2];
@@ -1572,67 +1622,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 sel[h][e] = static_cast<__bf16>((lq == (ln >> 2) && e == 4 * h + (ln & 3)) ? 1.f : 0.f);
-        const bf16x8 bkh = pack8(kh), bkt = pack8(kt), bqt = pack8(qt);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const bf16x4 ckh = pack4(mma32(bkh, sel[h], Z4)), ckt = pack4(mma32(bkt, sel[h], Z4)),
-                         cqt = pack4(mma32(bqt, sel[h], Z4));
-            const f32x4 rp = mma16(ckh, cPT, Z4);                    // (P kh)^T
-            const f32x4 rm = mma16(ckh, cQT, Z4);                    // (Q kh)^T
-            const f32x4 cc = mma16(cqt, cQ, mma16(ckt, cP, Z4));     // (P^T k~ + Q^T q~)^T
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = 4 * h + i;
-                const float eg = __builtin_amdgcn_exp2f(G2[e]);
-                RP[e] = eg * rp[i];
-                RM[e] = __builtin_fmaf(eg, rm[i], qii * kf(e));
-                CC[e] = __builtin_fmaf(__builtin_amdgcn_exp2f(-G2[e]), cc[i], qii * qf(e));
-                pG[e] = static_cast<float>(bkt[e]) * rp[i] + static_cast<float>(bqt[e]) * rm[i] -
-                        static_cast<float>(bkh[e]) * cc[i];
-            }
-        }
-    } else {
-        // running products: row pass (lane = token i, j = i - 1, i - 2, ..) and
-        // column pass (lane = token j, i = j + 1, ..), E extended one decay at a time
-        float rr[8], rc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            rr[e] = rc[e] = 1.f;
-            RP[e] = 0.f;
-            RM[e] = qii * kf(e);
-            CC[e] = qii * qf(e);
-        }
+        const int nb = deep ? 4 : 1;
 #pragma unroll 1
-        for (int dl = 1; dl < CH; ++dl) {
-            const int j = max(t - dl, 0);
-            const bool okr = t - dl >= 0;
-            const float pr = okr ? PP[t][j] : 0.f, qr = okr ? QQ[t][j] : 0.f;
-            const f32x4 dj0 = *reinterpret_cast<const f32x4 *>(&Dr[j + 1][c0]), dj1 = *reinterpret_cast<const f32x4 *>(&Dr[j + 1][c0 + 4]);
-            const uint4 kjw = *reinterpret_cast<const uint4 *>(&Kr[j][c0]);
-            const float dj[8] = {dj0[0], dj0[1], dj0[2], dj0[3], dj1[0], dj1[1], dj1[2], dj1[3]};
-            const int i = min(t + dl, CH - 1);
-            const bool okc = t + dl < CH;
-            const float pc = okc ? PP[i][t] : 0.f, qc = okc ? QQ[i][t] : 0.f;
-            const f32x4 di0 = *reinterpret_cast<const f32x4 *>(&Dr[i][c0]), di1 = *reinterpret_cast<const f32x4 *>(&Dr[i][c0 + 4]);
-            const uint4 kiw = *reinterpret_cast<const uint4 *>(&Kr[i][c0]), qiw = *reinterpret_cast<const uint4 *>(&Qr[i][c0]);
-            const float di[8] = {di0[0], di0[1], di0[2], di0[3], di1[0], di1[1], di1[2], di1[3]};
-            const uint32_t kjv[4] = {kjw.x, kjw.y, kjw.z, kjw.w}, kiv[4] = {kiw.x, kiw.y, kiw.z, kiw.w},
-                           qiv[4] = {qiw.x, qiw.y, qiw.z, qiw.w};
+        for (int bb = 0; bb < nb; ++bb) {
+            const bool col = !deep || t < 4 * (bb + 1);   // a column of block bb's products
+            const f32x4 ra = *reinterpret_cast<const f32x4 *>(&RF[w][bb][8 * lq]);
+            const f32x4 rb = *reinterpret_cast<const f32x4 *>(&RF[w][bb][8 * lq + 4]);
+            const float ref[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
+            // row factor f (used where this token is in block bb, whose
+            // reference is then its own) and column factor cs
+            const bool own = bt == bb;
+            float rw[8], qw8[8], cl[8], cs[8], f[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int sh = 16 * (e & 1);
-                const float kj = bf16_to_f32((uint16_t)(kjv[e >> 1] >> sh));
-                const float ki = bf16_to_f32((uint16_t)(kiv[e >> 1] >> sh)), qi = bf16_to_f32((uint16_t)(qiv[e >> 1] >> sh));
-                rr[e] *= dj[e];
-                const float x = kj * rr[e];
-                RP[e] = __builtin_fmaf(pr, x, RP[e]);
-                RM[e] = __builtin_fmaf(qr, x, RM[e]);
-                rc[e] *= di[e];
-                CC[e] = __builtin_fmaf(rc[e], __builtin_fmaf(pc, ki, qc * qi), CC[e]);
+                f[e] = __builtin_amdgcn_exp2f(gl[e] - ref[e]);
+                rw[e] = own ? kf(e) * f[e] : 0.f;
+                qw8[e] = own ? qf(e) * f[e] : 0.f;
+                cs[e] = col ? __builtin_amdgcn_exp2f(ref[e] - gl[e]) : 0.f;
+                cl[e] = kf(e) * cs[e];
+            }
+            bf16x8 rwh, rwl, qwh, qwl, clh, cll;
+            split8(rw, rwh, rwl);
+            split8(qw8, qwh, qwl);
+            split8(cl, clh, cll);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                // C tiles of the factors, hi and lo (exact selector copies); each
+                // product is hi hi + lo hi + hi lo: one K = 32 and one K = 16 MFMA
+                const bf16x4 ccH = pack4(mma32(clh, sel[h], Z4)), ccL = pack4(mma32(cll, sel[h], Z4));
+                const bf16x4 crH = pack4(mma32(rwh, sel[h], Z4)), crL = pack4(mma32(rwl, sel[h], Z4));
+                const bf16x4 cqH = pack4(mma32(qwh, sel[h], Z4)), cqL = pack4(mma32(qwl, sel[h], Z4));
+                const bf16x8 cc2 = cat4(ccH, ccL), cr2 = cat4(crH, crL), cq2 = cat4(cqH, cqL);
+                const f32x4 pk = mma16(ccH, cPTl, mma32(cc2, bPT, Z4));          // (P cl)^T
+                const f32x4 qk = mma16(ccH, cQTl, mma32(cc2, bQT, Z4));          // (Q cl)^T
+                const f32x4 ck = mma16(cqH, cQl, mma32(cq2, bQ, mma16(crH, cPl, mma32(cr2, bP, Z4))));   // (P^T rw + Q^T qw)^T
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * h + i;
+                    RP[e] = own ? f[e] * pk[i] : RP[e];
+                    RM[e] = own ? __builtin_fmaf(f[e], qk[i], RM[e]) : RM[e];
+                    pG[e] += rw[e] * pk[i] + qw8[e] * qk[i] - cl[e] * ck[i];   // rw, qw are 0 off block bb
+                    CC[e] = __builtin_fmaf(cs[e], ck[i], CC[e]);
+                }
             }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pG[e] = kf(e) * (RP[e] - CC[e]) + qf(e) * RM[e];
     }
 
     // ---- assembly: dq, dk, dG (natural-log units), the chunk decay's share at
