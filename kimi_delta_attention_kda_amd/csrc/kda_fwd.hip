@@ -1335,7 +1335,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     using P = BPay<DK>;
     __shared__ float LA[CH][CH + 1], PP[CH][CH + 1], QQ[CH][CH + 1];
     __shared__ float bs[CH], dbp[4][CH], red[4];
-    __shared__ __attribute__((aligned(16))) float RF[4][4][32];   // per wave: block references of its channels
+    __shared__ __attribute__((aligned(16))) float RF[4][2][32];   // per wave: block references of its channels
     // one region, two lives (a barrier between): the per-wave partials of W,
     // then U^T, (beta dy)^T and the per-wave 16 x 16 partials
     __shared__ __attribute__((aligned(16))) unsigned char big[4 * NVT * 64 * 16];
@@ -1375,6 +1375,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         return live ? x : bf16x4{};
     };
     const unsigned char *gr = grows + ((size_t)row * H + head) * (size_t)GRow::BYTES;
+    // every HBM read of the workgroup is issued here, ahead of the gate: S
+    // (column 16 vt + ln, channels c0 .. +7), this wave's two column tiles of
+    // v, dO and dU
+    const float *S0 = Sst + ((size_t)row * H + head) * (size_t)DV * DK;
+    f32x4 sf[NVT][2];
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt) {
+        const float *ps = S0 + (size_t)(16 * vt + ln) * DK + c0;
+        sf[vt][0] = *reinterpret_cast<const f32x4 *>(ps);
+        sf[vt][1] = *reinterpret_cast<const f32x4 *>(ps + 4);
+    }
+    bf16x4 vr[2], dOv[2];
+    f32x4 dUt[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int vt = 2 * w + u;
+        vr[u] = row4(a.v, vt);
+        dOv[u] = row4(dO, vt);
+        dUt[u] = *reinterpret_cast<const f32x4 *>(gr + GRow::DU + vt * 1024 + lane * 16);
+    }
 
     // ---- gate (log2 units) and its chunk-local cumulative sum G; k and q stay
     // packed (bf16 words, zero past the chunk's end) and are unpacked where used
@@ -1401,20 +1421,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
         for (int r = 0; r < 4; ++r) LA[4 * lq + r][ln] = At[r];
     }
     __syncthreads();
-    // S fragments (column 16 vt + ln, channels c0 .. +7) and dS' fragments,
-    // issued after the barrier so that they do not hold registers through the gate
-    const float *S0 = Sst + ((size_t)row * H + head) * (size_t)DV * DK;
-    f32x4 sf[NVT][2];
-    bf16x8 dm[NVT];
+    // S kept as bf16
+    bf16x8 sb[NVT];
 #pragma unroll
-    for (int vt = 0; vt < NVT; ++vt) {
-        const float *ps = S0 + (size_t)(16 * vt + ln) * DK + c0;
-        sf[vt][0] = *reinterpret_cast<const f32x4 *>(ps);
-        sf[vt][1] = *reinterpret_cast<const f32x4 *>(ps + 4);
-    }
-#pragma unroll
-    for (int vt = 0; vt < NVT; ++vt)
-        dm[vt] = *reinterpret_cast<const bf16x8 *>(gr + GRow::DM + (vt * 4 + w) * 1024 + lane * 16);
+    for (int vt = 0; vt < NVT; ++vt) sb[vt] = cat4(pack4(sf[vt][0]), pack4(sf[vt][1]));
 
     // ---- T = (I + beta A)^{-1} = (I + L)(I + L^2)(I + L^4)(I + L^8), L = -beta A,
     // on the fp32 matrix core in C layout (every wave on its own)
@@ -1441,40 +1451,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
     for (int e = 0; e < 4; ++e) eye16[e] = static_cast<__bf16>(eyef[e]);
 
-    // ---- W = k~ S over this wave's channels (partial), dD = sum_v S o dS'
-    float dD[8];
-    bf16x8 sb[NVT];
+    // ---- W = k~ S over this wave's channels (partial)
     {
-        float kt[8], acc[8] = {};
+        float kt[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) kt[e] = kf(e) * __builtin_amdgcn_exp2f(G2[e]);
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) {
-            const float sv[8] = {sf[vt][0][0], sf[vt][0][1], sf[vt][0][2], sf[vt][0][3],
-                                 sf[vt][1][0], sf[vt][1][1], sf[vt][1][2], sf[vt][1][3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(sv[e], static_cast<float>(dm[vt][e]), acc[e]);
-            sb[vt] = pack8(sv);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dD[e] = row16_sum(acc[e]);
         const bf16x8 ktb = pack8(kt);
 #pragma unroll
         for (int vt = 0; vt < NVT; ++vt) Wp[w][vt][lane] = mma32(ktb, sb[vt], Z4);
     }
     __syncthreads();
 
+    // dS' fragments (same lanes and channels as S), wanted from phase 5 on
+    bf16x8 dm[NVT];
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt)
+        dm[vt] = *reinterpret_cast<const bf16x8 *>(gr + GRow::DM + (vt * 4 + w) * 1024 + lane * 16);
     // ---- per column tile of this wave: r = v - W, y = beta r, U^T, dy, dy^T;
     // dv; partials of dbeta, dMqk = dO_s U^T and dy U^T
     {
-        f32x4 dMq = Z4, dBp = Z4, dbl = Z4, W[2], dUt[2];
-        bf16x4 vr[2], dOv[2];
+        f32x4 dMq = Z4, dBp = Z4, dbl = Z4, W[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int vt = 2 * w + u;
-            vr[u] = row4(a.v, vt);
-            dOv[u] = row4(dO, vt);
-            dUt[u] = *reinterpret_cast<const f32x4 *>(gr + GRow::DU + vt * 1024 + lane * 16);
             W[u] = ((Wp[0][vt][lane] + Wp[1][vt][lane]) + Wp[2][vt][lane]) + Wp[3][vt][lane];
         }
         __syncthreads();   // the region's next life
@@ -1532,8 +1531,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     __syncthreads();
 
     // ---- dq~^T, dk~^T, dk^r^T (channels x tokens) over d_v on the matrix core:
-    // S and dS' tiles transposed by products with the identity (exact)
-    f32x4 aq[2] = {Z4, Z4}, ak[2] = {Z4, Z4}, ar[2] = {Z4, Z4};
+    // S and dS' tiles transposed by products with the identity (exact); and
+    // S^T dS' per 16-channel tile, whose diagonal is dD = sum_v S o dS'
+    f32x4 aq[2] = {Z4, Z4}, ak[2] = {Z4, Z4}, ar[2] = {Z4, Z4}, dd[2] = {Z4, Z4};
 #pragma unroll
     for (int u2 = 0; u2 < NVT / 2; ++u2) {
         const int v0 = 2 * u2, v1 = 2 * u2 + 1;
@@ -1547,7 +1547,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
             aq[h] = mma32(as, bo, aq[h]);
             ak[h] = mma32(as, bb, ak[h]);
             ar[h] = mma32(ad, bu, ar[h]);
+            dd[h] = mma32(as, ad, dd[h]);
         }
+    }
+    // dD of channel c0 + 4 h + i: the diagonal entry, held by lane (lq, 4 lq + i)
+    float dD[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dD[4 * h + i] = __shfl(dd[h][i], 20 * lq + i);
+
+    // ---- dq, dk and dG (natural-log units) from the state path, with the
+    // chunk decay's share of dG at the last token; the pair terms add to them
+    float dq[8], dk[8], dG[8];
+    const float qii = QQ[t][t];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float GC2 = row_bcast<15>(G2[e]);
+        const float eg = __builtin_amdgcn_exp2f(G2[e]), er = __builtin_amdgcn_exp2f(GC2 - G2[e]);
+        const float dqt = a.scale * aq[e >> 2][e & 3];
+        const float dkt = -ak[e >> 2][e & 3];
+        const float dkr = ar[e >> 2][e & 3];
+        const float kv = kf(e), qv = qf(e), krv = kv * er;
+        dq[e] = __builtin_fmaf(dqt, eg, qii * kv);        // with Q's diagonal term
+        dk[e] = __builtin_fmaf(dkt, eg, __builtin_fmaf(dkr, er, qii * qv));
+        dG[e] = (dqt * qv + dkt * kv) * eg - dkr * krv;
+        const float gc = row16_sum(dkr * krv) + dD[e] * __builtin_amdgcn_exp2f(GC2);
+        if (t == CH - 1) dG[e] += gc;
     }
 
     // ---- pair terms: RP, RM, CC as above and pG, their share of dG,
@@ -1557,40 +1583,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
     // channels).  Where no channel of the wave decays by more than 2^-200 in
     // the chunk, l = G and r is the midpoint of G over the chunk: every factor
     // within 2^100, exact.  Otherwise l is the cumulative decay with each
-    // token's decay clipped at 2^-24 and the tokens form four blocks of 4,
-    // block b with r_b = l at the end of the previous block (0 for the first):
-    // rows of block b take r_b, columns up to the end of block b take r_b,
-    // every factor within 2^96.  A pair whose true decay gap exceeds 2^-24 is
-    // then taken as at most 2^-24 instead of its smaller true value.
+    // token's decay clipped at 2^-27 and the tokens form two blocks of 8,
+    // block b with r_b the midpoint of l over the block: rows of block b and
+    // columns up to its end take r_b, every factor within 2^95 (a column of an
+    // earlier block has a factor <= 1).  A pair whose true decay gap exceeds
+    // 2^-27 is then taken as at most 2^-27 instead of its smaller true value.
     // Factors, P and Q enter the products as hi + lo bf16 pairs (to ~2^-16).
     // Every pair adds +X to one token's dG and -X to another's, which cancel
     // in the cumulative sum over the chunk, so pG takes both sides from the
     // same factors.  Q's diagonal (whose dG terms cancel exactly) stays out of
     // the products and is added to dq and dk exactly.
-    float RP[8], RM[8], CC[8], pG[8];
     {
-        const float qii = QQ[t][t];
-        const int bt = deep ? t / 4 : 0;   // this token's block
-        // block references of this lane's channels (the midpoint of G for a
-        // single block, else l at the end of block bb - 1, 0 for the first),
-        // through LDS so that the block loop need not be unrolled
+        const int bt = deep ? t / 8 : 0;   // this token's block
+        // block references of this lane's channels (every lane of the row
+        // computes and stores the same values), through LDS so that the block
+        // loop need not be unrolled
         float gl[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            gl[e] = deep ? scan16(fmaxf(gate2(z[e], A, live), -24.f)) : G2[e];
-            const float r0 = deep ? 0.f : 0.5f * (row_bcast<0>(G2[e]) + row_bcast<15>(G2[e]));
-            const float r1 = row_bcast<3>(gl[e]), r2 = row_bcast<7>(gl[e]), r3 = row_bcast<11>(gl[e]);
-            // every lane of the row stores the same values: the row broadcasts
-            // must run with the whole row active (a store under a lane test
-            // would let them sink into it and read inactive lanes)
-            RF[w][0][8 * lq + e] = r0;
-            RF[w][1][8 * lq + e] = r1;
-            RF[w][2][8 * lq + e] = r2;
-            RF[w][3][8 * lq + e] = r3;
-            RP[e] = 0.f;
-            RM[e] = qii * kf(e);
-            CC[e] = qii * qf(e);
-            pG[e] = 0.f;
+            gl[e] = deep ? scan16(fmaxf(gate2(z[e], A, live), -27.f)) : G2[e];
+            const float l0 = row_bcast<0>(gl[e]), l15 = row_bcast<15>(gl[e]);
+            RF[w][0][8 * lq + e] = deep ? 0.5f * (l0 + row_bcast<7>(gl[e])) : 0.5f * (l0 + l15);
+            RF[w][1][8 * lq + e] = 0.5f * (row_bcast<8>(gl[e]) + l15);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_wave_barrier();
@@ -1622,10 +1636,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 sel[h][e] = static_cast<__bf16>((lq == (ln >> 2) && e == 4 * h + (ln & 3)) ? 1.f : 0.f);
-        const int nb = deep ? 4 : 1;
+        const int nb = deep ? 2 : 1;
 #pragma unroll 1
         for (int bb = 0; bb < nb; ++bb) {
-            const bool col = !deep || t < 4 * (bb + 1);   // a column of block bb's products
+            const bool col = !deep || t < 8 * (bb + 1);   // a column of block bb's products
             const f32x4 ra = *reinterpret_cast<const f32x4 *>(&RF[w][bb][8 * lq]);
             const f32x4 rb = *reinterpret_cast<const f32x4 *>(&RF[w][bb][8 * lq + 4]);
             const float ref[8] = {ra[0], ra[1], ra[2], ra[3], rb[0], rb[1], rb[2], rb[3]};
@@ -1659,32 +1673,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int e = 4 * h + i;
-                    RP[e] = own ? f[e] * pk[i] : RP[e];
-                    RM[e] = own ? __builtin_fmaf(f[e], qk[i], RM[e]) : RM[e];
-                    pG[e] += rw[e] * pk[i] + qw8[e] * qk[i] - cl[e] * ck[i];   // rw, qw are 0 off block bb
-                    CC[e] = __builtin_fmaf(cs[e], ck[i], CC[e]);
+                    // R^P, R^M: this token's own block only; C: every block
+                    dq[e] = own ? __builtin_fmaf(f[e], qk[i], dq[e]) : dq[e];
+                    dk[e] = __builtin_fmaf(cs[e], ck[i], own ? __builtin_fmaf(f[e], pk[i], dk[e]) : dk[e]);
+                    dG[e] += rw[e] * pk[i] + qw8[e] * qk[i] - cl[e] * ck[i];   // rw, qw are 0 off block bb
                 }
             }
         }
     }
 
-    // ---- assembly: dq, dk, dG (natural-log units), the chunk decay's share at
-    // the last token, reverse cumulative sum -> dg, then g_raw, dt_bias, A_log
-    float dq[8], dk[8], dgr[8], sA = 0.f;
+    // ---- reverse cumulative sum dG -> dg, then g_raw, dt_bias, A_log
+    float dgr[8], sA = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float GC2 = row_bcast<15>(G2[e]);
-        const float eg = __builtin_amdgcn_exp2f(G2[e]), er = __builtin_amdgcn_exp2f(GC2 - G2[e]);
-        const float dqt = a.scale * aq[e >> 2][e & 3];
-        const float dkt = -ak[e >> 2][e & 3];
-        const float dkr = ar[e >> 2][e & 3];
-        const float kv = kf(e), qv = qf(e), krv = kv * er;
-        dq[e] = __builtin_fmaf(dqt, eg, RM[e]);
-        dk[e] = dkt * eg + dkr * er + RP[e] + CC[e];
-        float dG = (dqt * qv + dkt * kv) * eg - dkr * krv + pG[e];
-        const float gc = row16_sum(dkr * krv) + dD[e] * __builtin_amdgcn_exp2f(GC2);
-        if (t == CH - 1) dG += gc;
-        const float dg = rscan16(dG);
+        const float dg = rscan16(dG[e]);
         const float dz = live ? -A * sigmoid_f(z[e]) * dg : 0.f;
         dgr[e] = dz;
         sA = __builtin_fmaf(dg, gate2(z[e], A, live) * 0.6931471805599453f, sA);   // g in natural-log units (0 on pads)
