@@ -113,17 +113,21 @@ KERNEL_SOURCES = {
     "decode": [_C + "kda_decode.hip"] + _COMMON,
     "extend": [_C + "kda_decode.hip"] + _COMMON,
     "conv_decode": [_C + "kda_decode.hip"] + _COMMON,
-    "backward": [_C + "kda_backward.hip"] + _COMMON,
+    "backward": [_C + "kda_fwd.hip", _C + "kda_backward.hip"] + _COMMON,
+    "bwd_rec": [_C + "kda_fwd.hip"] + _COMMON,
+    "bwd_prep": [_C + "kda_fwd.hip"] + _COMMON,
     "chunk_o": [_C + "kda_chunk_o.hip"] + _COMMON,
 }
 # kernel-name patterns of the instantiations the workloads launch: the
 # headline's one-pass kernel (many chains), the two passes of configs 1 and 3
-# (fewer chains than compute units), the decode family, the backward's main
-# kernel and the chunk-parallel output kernel
+# (fewer chains than compute units), the decode family, the backward's three
+# passes (chunk-parallel gradients, reverse chain, operands) and the
+# chunk-parallel output kernel
 KERNEL_MATCH = {"fwd": "kda::fwd_kernel<128, 128, 4, 2, false>", "prep": "kda::prep_kernel<128>",
                 "rec": "kda::rec_kernel<128, 128, 1, false>", "decode": "kda::decode_kernel",
                 "extend": "kda::extend_kernel", "conv_decode": "kda::conv_decode_kernel",
-                "backward": "kda::bwd_kernel", "chunk_o": "kda::chunk_o_kernel"}
+                "backward": "kda::bwd_chunk_kernel", "bwd_rec": "kda::bwd_rec_kernel",
+                "bwd_prep": "kda::bwd_prep_kernel", "chunk_o": "kda::chunk_o_kernel"}
 
 
 def measured_traffic(kernel):

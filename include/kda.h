@@ -237,15 +237,20 @@ int kda_chunk_o(const void *q, const void *k, const void *v,
  * kda_backward -- gradients of the forward of kda_chunk_fwd for a loss whose
  * gradients with respect to o and to the final states are do and dh_T: the
  * backward pass of [LA-06] (chunkwise form: a reverse loop over chunks from
- * the states stored at chunk boundaries).  Per token, with D the gradient
- * with respect to the state after the token (S' = S Diag(e^g),
- * u = beta (v - S'k), S+ = S' + u k^T, o = S+ scale q):
- *   D += do (scale q)^T;  dq = scale S+^T do;  du = D k;  dv = beta du;
- *   dbeta = du . (v - S'k);  dk = D^T u - beta S'^T du;
- *   dS' = D - beta du k^T;  dg = column sums of dS' o S';  D <- dS' Diag(e^g);
- * then through g = -exp(A_log) softplus(g_raw + dt_bias) and
- * beta = sigmoid(beta_raw) to dg_raw, ddt_bias, dA_log and dbeta_raw, and
- * dh0 = D before the first token.
+ * the states stored at chunk boundaries).  Per chunk of 16 tokens, with S
+ * the state entering it, dS' the gradient with respect to the state leaving
+ * it (S as dk x dv), dO_s = scale do and the chunk's forward as in
+ * kda_chunk_fwd, U = T beta (v - k~ S), O = scale (q~ S + Mqk U),
+ * S' = D S + k^r^T U, where G is the cumulative gate, k~ = k e^G,
+ * q~ = q e^G, k^r = k e^{G_C - G}, D = Diag(e^{G_C}), T = (I - L)^{-1} and
+ * w = T beta k~:
+ *   dU = k^r dS' + Mqk^T dO_s;  dS = D dS' + q~^T dO_s - w^T dU
+ * (the sequential step, a reverse recurrence over chunks), then, for every
+ * chunk in parallel, dv, dbeta, dq, dk and dG from S, dS', dU and the chunk's
+ * pair terms; dg is the reverse cumulative sum of dG within the chunk, and
+ * the chain rule through g = -exp(A_log) softplus(g_raw + dt_bias) and
+ * beta = sigmoid(beta_raw) gives dg_raw, ddt_bias, dA_log and dbeta_raw;
+ * dh0 is the gradient before the first chunk.
  *
  * Inputs: q, k, v, g_raw, beta_raw, A_log, dt_bias, cu_seqlens, scale,
  * B, T, H, n_seq and dtype exactly as given to kda_chunk_fwd_states;
@@ -258,9 +263,9 @@ int kda_chunk_o(const void *q, const void *k, const void *v,
  *                    in the activation dtype;
  *   dA_log [H], ddt_bias [H, dk], dh0 [n_seq, H, dv, dk] float32.
  * workspace: device memory of at least kda_backward_workspace_bytes() bytes,
- * owned by the caller (about 6 KiB per (token, head) for partial column sums,
- * and a small area per block of 16 tokens); its contents on entry do not
- * matter.
+ * owned by the caller (55,812 bytes per (chunk of 16 tokens, head) for the
+ * reverse chain's operands, the per-chunk gradient rows and parameter sums,
+ * plus H * 64 * 129 floats); its contents on entry do not matter.
  * Built for dk = dv = 128 with bfloat16 activations (those of the d = 128
  * forward; other shapes and float32 return KDA_ERR_UNSUPPORTED).  The result
  * is deterministic (no atomics).  Returns KDA_OK or a negative kda_status.

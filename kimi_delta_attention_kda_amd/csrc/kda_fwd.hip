@@ -1318,9 +1318,10 @@ struct BwdOut {
 // and Q = dMqk,
 //   R^P_i = sum_{j<i} P_ij k_j E_ij,  R^M_i = sum_{j<=i} Q_ij k_j E_ij,
 //   C_j = sum_{i>j} P_ij k_i E_ij + sum_{i>=j} Q_ij q_i E_ij,   E_ijc = e^{G_ic - G_jc},
-// are 16 x 16 products in the factored form (rows e^{G}, columns e^{-G})
-// where the chunk's decay stays inside the fp32 range (the same test as the
-// forward's prep), else fp32 running products of the decays.
+// are 16 x 16 MFMA products in the factored form (rows e^{G - r}, columns
+// e^{r - G}) around a reference r per channel: one for the chunk where its
+// decay spans at most 2^200, else one per block of 8 tokens (the pair
+// section below states the bounds).
 //
 // Wave w owns channels 32 w .. +31: lane (lq, ln) holds token ln and channels
 // 32 w + 8 lq .. +7 for all elementwise work, which is also the row fragment

@@ -4,7 +4,8 @@ lengths, a zero-length sequence, h0 and dh_T, gate stress, and one (sequence,
 head) chain of the full prefill workload.  Also: deterministic, and the
 gradients of a zero-length sequence's h0 are its dh_T.
 
-Tolerance (bf16 I/O, the arithmetic in fp32): RMSE/RMS <= 5e-3 per gradient
+Tolerance (bf16 I/O; bf16 MFMA operands, hi + lo bf16 pairs where errors
+cancel or accumulate, fp32 accumulation): RMSE/RMS <= 5e-3 per gradient
 tensor, and max-abs <= 2e-2 * max(1, max |reference|) -- a bf16 output of
 magnitude m is rounded by up to m 2^-9 on its own, so the gradients, whose
 scale is not fixed by the inputs' unit norms, get the forward's max-abs bound
