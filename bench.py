@@ -106,16 +106,17 @@ def source_hash(files):
 
 _C = "kimi_delta_attention_kda_amd/csrc/"
 _COMMON = [_C + "kda_device.hpp", _C + "kda_launch.hpp", "kimi_delta_attention_kda_amd/build.py"]
+_CHUNK = [_C + "kda_chunk.hpp"] + _COMMON
 KERNEL_SOURCES = {
-    "fwd": [_C + "kda_fwd.hip"] + _COMMON,
-    "prep": [_C + "kda_fwd.hip"] + _COMMON,
-    "rec": [_C + "kda_fwd.hip"] + _COMMON,
+    "fwd": [_C + "kda_fwd.hip"] + _CHUNK,
+    "prep": [_C + "kda_fwd.hip"] + _CHUNK,
+    "rec": [_C + "kda_fwd.hip"] + _CHUNK,
     "decode": [_C + "kda_decode.hip"] + _COMMON,
     "extend": [_C + "kda_decode.hip"] + _COMMON,
     "conv_decode": [_C + "kda_decode.hip"] + _COMMON,
-    "backward": [_C + "kda_fwd.hip", _C + "kda_backward.hip"] + _COMMON,
-    "bwd_rec": [_C + "kda_fwd.hip"] + _COMMON,
-    "bwd_prep": [_C + "kda_fwd.hip"] + _COMMON,
+    "backward": [_C + "kda_backward.hip"] + _CHUNK,
+    "bwd_rec": [_C + "kda_backward.hip"] + _CHUNK,
+    "bwd_prep": [_C + "kda_backward.hip"] + _CHUNK,
     "chunk_o": [_C + "kda_chunk_o.hip"] + _COMMON,
 }
 # kernel-name patterns of the instantiations the workloads launch: the

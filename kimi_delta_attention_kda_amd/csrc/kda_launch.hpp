@@ -80,19 +80,8 @@ struct BwdArgs {
     long long T_all;      // total tokens
     float scale;
 };
-// The chunkwise backward (kda_fwd.hip), bf16 and d = 128: the reverse
-// chain's operands for every chunk, the reverse chain over the chunks of each
-// (sequence, head) (dh0 and a gradient row per chunk), then every chunk's
-// gradients in parallel and its parameter sums (at BwdWs::part, [n_rows][H][129]),
-// which the reduction (kda_backward.hip) sums in BWD_SPLIT slices of rows (at
-// BwdWs::red) and then over the slices.  n_rows bounds the chunk rows (rows
-// past the sequences' chunks get zero sums).
-constexpr int BWD_SPLIT = 64;
-struct BwdWs {
-    size_t pay, grow, part, red, bytes;
-};
-BwdWs bwd_ws_layout(long long n_rows, int H);
-hipError_t launch_bwd_chunkwise(const BwdArgs &b, long long n_rows, hipStream_t stream);
+// The chunkwise backward (kda_backward.hip): bf16, d = 128.  The workspace
+// holds every chunk's reverse-chain operands, gradient row and parameter sums.
 size_t bwd_workspace_bytes(int n_seq, int H, long long tokens);
 hipError_t launch_bwd(const BwdArgs &a, int dtype, hipStream_t stream);
 
