@@ -524,6 +524,10 @@ def main():
         bwd_call()
         extra["backward_us"] = round(time_calls(bwd_call, 5, torch) * 1e6, 2)
         extra["backward_over_forward"] = round(extra["backward_us"] / per_cfg["1"]["us"], 2)
+        # algorithmic bytes: q, k, g_raw, v, beta and do read, the five gradients
+        # written (activation dtype), the stored states read once
+        bwd_bytes = p1.tokens * p1.H * (4 * (3 * p1.dk + p1.dv + 1) + 2 * p1.dv) + snap
+        extra["backward_gbs"] = round(bwd_bytes / (extra["backward_us"] * 1e-6) / 1e9, 1)
         del hcb, wsb, dob, ppool
         # T = 4 tokens per row through kda_decode_extend on the decode workload's rows
         de = synth.extend(4, T=EXTEND_T, **{k_: v_ for k_, v_ in synth.DECODE_WORKLOAD.items() if k_ != "name"})
