@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdA
 // are issued from inline assembly: the compiler would otherwise wait for all
 // of them before every LDS read.  Each is counted in this wave's vmcnt, which
 // drains in issue order, so waiting until at most n loads remain outstanding,
-
+// n = the loads issued after chunk x's, guarantees chunk x has landed.
 template <int DK, int DV, int SPW, bool SNAP>
 __global__ __launch_bounds__(64) void rec_kernel(FwdArgs a, const unsigned char *ws)
 {
