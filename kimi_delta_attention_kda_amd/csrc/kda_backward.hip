@@ -123,14 +123,15 @@ struct GRow {
     static constexpr int BYTES = DU + 8 * 1024;
 };
 
-// The reverse chain: one single-wave workgroup per (chain, 16 state columns),
-// chunks from last to first; dS' (fp32, in the forward state's registers and
-// layout) starts from dh_T; for every chunk it leaves dS' and dU in a gradient
-// row, and the gradient before the first chunk goes to dh0.  Operands reach a
-// ring of LDS slots by direct global-to-LDS loads, RING - 1 chunks ahead,
-// counted as in the prefill's rec_kernel.
+// The reverse chain: one workgroup of two waves per (chain, 16 state
+// columns), chunks from last to first: wave 0 carries dS' (fp32, in the
+// forward state's registers and layout) from dh_T, leaves dS' and dU in a
+// gradient row for every chunk and the gradient before the first chunk in
+// dh0; wave 1 only loads.  Operands reach a ring of LDS slots by direct
+// global-to-LDS loads, RING - 1 chunks ahead, issued, counted and handed over
+// (one barrier per chunk) as in the prefill's rec_kernel.
 template <int DK, int DV>
-__global__ __launch_bounds__(64) void bwd_rec_kernel(FwdArgs a, const unsigned char *ws, const float *dh_T,
+__global__ __launch_bounds__(128) void bwd_rec_kernel(FwdArgs a, const unsigned char *ws, const float *dh_T,
                                                       const void *dO, unsigned char *grows, float *dh0)
 {
     constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / 16;
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(FwdArgs a, const unsigned c
     constexpr int SLOT = ND * 1024, DT = NPAY * 1024;
     static_assert((RING - 1) * ND <= 63, "loads in flight exceed the vmcnt field");
     __shared__ __attribute__((aligned(1024))) unsigned char ring[RING * SLOT];
-    const int lane = threadIdx.x, ln = lane & 15, lq = lane >> 4;
+    const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
+    const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 1;
     const int b8 = blockIdx.x / 8;
     const int chain = 8 * (b8 / NSG) + blockIdx.x % 8;
     const int sg = b8 % NSG;
@@ -150,10 +152,7 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(FwdArgs a, const unsigned c
     const size_t H = a.H;
     const int col0 = sg * 16;
     const size_t hbase = (((size_t)c.seq * H + c.head) * DV + col0) * DK;
-    f32x4 dS[NMT];
-#pragma unroll
-    for (int m = 0; m < NMT; ++m)
-        dS[m] = dh_T ? *reinterpret_cast<const f32x4 *>(dh_T + hbase + (size_t)ln * DK + chan(m, lq, 0)) : Z4;
+    f32x4 dS[NMT];   // the reverse chain's gradient (wave 0), from dh_T below
     const size_t cbase = chunk_base(a, c.seq);
     bf16x4 eye;
 #pragma unroll
@@ -215,11 +214,21 @@ __global__ __launch_bounds__(64) void bwd_rec_kernel(FwdArgs a, const unsigned c
             dS[m] = mma16(qc[m], bdO, dS[m]);
         }
     };
-    for (int kk = 0; kk < min(RING - 1, c.nch); ++kk) issue(kk);
-    for (int kk = 0; kk < c.nch; ++kk) {
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the reused slot's reads are done
-        if (kk + RING - 1 < c.nch) issue(kk + RING - 1);
-        vm_wait_chunks<ND>(min(RING - 1, c.nch - 1 - kk));
+    const int nch = c.nch;
+    if (loader) {
+        for (int kk = 0; kk < min(RING - 1, nch); ++kk) issue(kk);
+        for (int kk = 0; kk < nch; ++kk) {
+            vm_wait_chunks<ND>(min(RING - 2, nch - 1 - kk));   // the kk-th chunk has landed
+            lds_barrier();
+            if (kk + RING - 1 < nch) issue(kk + RING - 1);       // into the slot of the previous one
+        }
+        return;
+    }
+#pragma unroll
+    for (int m = 0; m < NMT; ++m)
+        dS[m] = dh_T ? *reinterpret_cast<const f32x4 *>(dh_T + hbase + (size_t)ln * DK + chan(m, lq, 0)) : Z4;
+    for (int kk = 0; kk < nch; ++kk) {
+        lds_barrier();   // the kk-th chunk has landed; every read of the previous one is done
         step(kk);
     }
     if (dh0) {
@@ -776,7 +785,7 @@ hipError_t launch_bwd_chunkwise(const BwdArgs &b, long long n_rows, hipStream_t 
     const long long wgs = 8 * 8 * ((chains + 7) / 8);
     if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (wgs > 0) {
-        hipLaunchKernelGGL((bwd_rec_kernel<128, 128>), dim3((unsigned)wgs), dim3(64), 0, stream, a, ws + l.pay,
+        hipLaunchKernelGGL((bwd_rec_kernel<128, 128>), dim3((unsigned)wgs), dim3(128), 0, stream, a, ws + l.pay,
                            b.dh_T, b.do_, ws + l.grow, b.dh0);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -276,20 +276,25 @@ __global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdA
         *reinterpret_cast<bf16x8 *>(pw + P::WF + (s2 * 64 + lane) * 16) = w_frag2(kt[2 * s2], kt[2 * s2 + 1], ib);
 }
 
-// Pass 2: one wave per (sequence, head, SPW slabs of 16 columns).  Workgroup
-// b takes chain 8 (b / 8 / NSG) + b % 8 and slab group (b / 8) % NSG, so that
-// the slab groups of a chain share blockIdx % 8 (the XCD, whose L2 then serves
-// the chain's operands to all of them; placement only affects speed).
+// Pass 2: one workgroup of two waves per (sequence, head, SPW slabs of 16
+// columns): wave 0 runs the recurrence, wave 1 only loads.  Workgroup b
+// takes chain 8 (b / 8 / NSG) + b % 8 and slab group (b / 8) % NSG, so that
+// the slab groups of a chain share blockIdx % 8 (the XCD, whose L2 then
+// serves the chain's operands to all of them; placement only affects speed).
 //
-// A chunk's operands (its workspace row, padded to whole KiB, and the wave's
-// 16 x 16 SPW bf16 tile of v) reach LDS by direct global-to-LDS loads, RING
-// chunks ahead, so the recurrence never waits on memory latency.  The loads
-// are issued from inline assembly: the compiler would otherwise wait for all
-// of them before every LDS read.  Each is counted in this wave's vmcnt, which
-// drains in issue order, so waiting until at most n loads remain outstanding,
-// n = the loads issued after chunk x's, guarantees chunk x has landed.
+// A chunk's operands (its workspace row, padded to whole KiB, and the
+// slabs' 16 x 16 SPW bf16 tile of v) reach a ring of RING LDS slots by direct
+// global-to-LDS loads, issued by the loader wave RING - 1 chunks ahead, so
+// the recurrence neither waits on memory latency nor spends its own issue
+// cycles on the loads.  The loads are issued from inline assembly (the
+// compiler would otherwise wait for all of them before every LDS read).  Each
+// is counted in the loader's vmcnt, which drains in issue order, so waiting
+// until at most n loads remain outstanding, n = the loads issued after chunk
+// x's, guarantees chunk x has landed.  One barrier per chunk: at barrier x
+// chunk x has landed and the recurrence has read every operand of chunk
+// x - 1, whose slot the loader then refills.
 template <int DK, int DV, int SPW, bool SNAP>
-__global__ __launch_bounds__(64) void rec_kernel(FwdArgs a, const unsigned char *ws)
+__global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char *ws)
 {
     constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * SPW);
     using P = Pay<DK>;
@@ -298,23 +303,17 @@ __global__ __launch_bounds__(64) void rec_kernel(FwdArgs a, const unsigned char 
     constexpr int SLOT = ND * 1024, VT = NPAY * 1024;
     static_assert((RING - 1) * ND <= 63, "loads in flight exceed the vmcnt field");
     __shared__ __attribute__((aligned(1024))) unsigned char ring[RING * SLOT];
-    const int lane = threadIdx.x, ln = lane & 15, lq = lane >> 4;
+    const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
+    const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 1;
     const int b8 = blockIdx.x / 8;
     const int chain = 8 * (b8 / NSG) + blockIdx.x % 8;
     const int sg = b8 % NSG;
     if (chain >= a.n_seq * a.H) return;
-    const Chain c = chain_of(a, chain / a.H, chain % a.H, lane == 0 && sg == 0);
+    const Chain c = chain_of(a, chain / a.H, chain % a.H, threadIdx.x == 0 && sg == 0);
     const size_t H = a.H;
     const int col0 = sg * SPW * 16;
     const size_t hbase = (((size_t)(c.hrow < 0 ? 0 : c.hrow) * H + c.head) * DV + col0) * DK;
-    f32x4 S[SPW][NMT];
-#pragma unroll
-    for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int m = 0; m < NMT; ++m)
-            S[j][m] = (a.h0 && c.hrow >= 0)
-                          ? *reinterpret_cast<const f32x4 *>(a.h0 + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0))
-                          : Z4;
+    f32x4 S[SPW][NMT];   // the state (recurrence wave), from h0 below
     const size_t cbase = chunk_base(a, c.seq);
     // identity as a K = 16 B operand: the product of a row-loaded 16 x 16 tile with it is its C layout
     bf16x4 eye;
@@ -374,12 +373,25 @@ __global__ __launch_bounds__(64) void rec_kernel(FwdArgs a, const unsigned char 
                 store_o(a.o, c.bos + (size_t)x * CH + ln, H, c.head, DV, col0 + 16 * j + 4 * lq, O[j], a.scale);
         }
     };
-    for (int x = 0; x < min(RING - 1, c.nch); ++x) issue(x);
-    for (int x = 0; x < c.nch; ++x) {
-        // slot (x + RING - 1) % RING held chunk x - 1, whose LDS reads are done
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-        if (x + RING - 1 < c.nch) issue(x + RING - 1);
-        vm_wait_chunks<ND>(min(RING - 1, c.nch - 1 - x));   // chunks x + 1 .. x + RING - 1 may still fly
+    const int nch = c.nch;
+    if (loader) {
+        for (int x = 0; x < min(RING - 1, nch); ++x) issue(x);
+        for (int x = 0; x < nch; ++x) {
+            vm_wait_chunks<ND>(min(RING - 2, nch - 1 - x));   // chunk x has landed
+            lds_barrier();
+            if (x + RING - 1 < nch) issue(x + RING - 1);       // into the slot of chunk x - 1
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < SPW; ++j)
+#pragma unroll
+        for (int m = 0; m < NMT; ++m)
+            S[j][m] = (a.h0 && c.hrow >= 0)
+                          ? *reinterpret_cast<const f32x4 *>(a.h0 + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0))
+                          : Z4;
+    for (int x = 0; x < nch; ++x) {
+        lds_barrier();   // chunk x has landed; every read of chunk x - 1 is done
         step(x);
     }
     if (a.h_T && c.hrow >= 0) {
@@ -446,7 +458,7 @@ hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows
     const long long chains = (long long)a.n_seq * a.H;
     const long long wgs2 = 8 * NSG * ((chains + 7) / 8);
     if (wgs2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rec_kernel<DK, DV, SPW, SNAP>), dim3((unsigned)wgs2), dim3(64), 0, stream, a,
+    hipLaunchKernelGGL((rec_kernel<DK, DV, SPW, SNAP>), dim3((unsigned)wgs2), dim3(128), 0, stream, a,
                        (const unsigned char *)ws);
     return hipGetLastError();
 }
