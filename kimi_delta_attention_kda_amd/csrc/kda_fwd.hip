@@ -276,26 +276,31 @@ __global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdA
         *reinterpret_cast<bf16x8 *>(pw + P::WF + (s2 * 64 + lane) * 16) = w_frag2(kt[2 * s2], kt[2 * s2 + 1], ib);
 }
 
-// Pass 2: one workgroup of two waves per (sequence, head, SPW slabs of 16
-// columns): wave 0 runs the recurrence, wave 1 only loads.  Workgroup b
-// takes chain 8 (b / 8 / NSG) + b % 8 and slab group (b / 8) % NSG, so that
-// the slab groups of a chain share blockIdx % 8 (the XCD, whose L2 then
-// serves the chain's operands to all of them; placement only affects speed).
+// Pass 2: one workgroup per (sequence, head, SPW slabs of 16 columns).
+// Workgroup b takes chain 8 (b / 8 / NSG) + b % 8 and slab group
+// (b / 8) % NSG, so that the slab groups of a chain share blockIdx % 8 (the
+// XCD, whose L2 then serves the chain's operands to all of them; placement
+// only affects speed).
 //
 // A chunk's operands (its workspace row, padded to whole KiB, and the
 // slabs' 16 x 16 SPW bf16 tile of v) reach a ring of RING LDS slots by direct
-// global-to-LDS loads, issued by the loader wave RING - 1 chunks ahead, so
-// the recurrence neither waits on memory latency nor spends its own issue
-// cycles on the loads.  The loads are issued from inline assembly (the
+// global-to-LDS loads, RING - 1 chunks ahead, so the recurrence never waits
+// on memory latency.  The loads are issued from inline assembly (the
 // compiler would otherwise wait for all of them before every LDS read).  Each
-// is counted in the loader's vmcnt, which drains in issue order, so waiting
-// until at most n loads remain outstanding, n = the loads issued after chunk
-// x's, guarantees chunk x has landed.  One barrier per chunk: at barrier x
-// chunk x has landed and the recurrence has read every operand of chunk
-// x - 1, whose slot the loader then refills.
+// is counted in its wave's vmcnt, which drains in issue order, so waiting
+// until at most n operations remain outstanding, n = those issued after
+// chunk x's loads, guarantees chunk x has landed.
+//  - Without snapshots the workgroup has two waves: wave 0 runs the
+//    recurrence and wave 1 only loads, so the loads' issue cycles leave the
+//    state's critical path.  One barrier per chunk: at barrier x chunk x has
+//    landed and the recurrence has read every operand of chunk x - 1, whose
+//    slot the loader then refills.
+//  - With snapshots (8 KiB of stores per chunk and slab) one wave issues both
+//    its loads and its stores, which measured faster.
 template <int DK, int DV, int SPW, bool SNAP>
 __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char *ws)
 {
+    constexpr bool LOADER = !SNAP;   // a separate loader wave
     constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * SPW);
     using P = Pay<DK>;
     constexpr int NPAY = (P::BYTES + 1023) / 1024;   // 1 KiB loads of a workspace row
@@ -374,7 +379,7 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
         }
     };
     const int nch = c.nch;
-    if (loader) {
+    if (LOADER && loader) {
         for (int x = 0; x < min(RING - 1, nch); ++x) issue(x);
         for (int x = 0; x < nch; ++x) {
             vm_wait_chunks<ND>(min(RING - 2, nch - 1 - x));   // chunk x has landed
@@ -390,9 +395,20 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
             S[j][m] = (a.h0 && c.hrow >= 0)
                           ? *reinterpret_cast<const f32x4 *>(a.h0 + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0))
                           : Z4;
-    for (int x = 0; x < nch; ++x) {
-        lds_barrier();   // chunk x has landed; every read of chunk x - 1 is done
-        step(x);
+    if constexpr (LOADER) {
+        for (int x = 0; x < nch; ++x) {
+            lds_barrier();   // chunk x has landed; every read of chunk x - 1 is done
+            step(x);
+        }
+    } else {
+        // one wave: its own loads, counted together with its stores
+        for (int x = 0; x < min(RING - 1, nch); ++x) issue(x);
+        for (int x = 0; x < nch; ++x) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot to refill has been read
+            if (x + RING - 1 < nch) issue(x + RING - 1);
+            vm_wait_chunks<ND>(min(RING - 1, nch - 1 - x));   // chunks x + 1 .. x + RING - 1 may still fly
+            step(x);
+        }
     }
     if (a.h_T && c.hrow >= 0) {
 #pragma unroll
@@ -458,7 +474,7 @@ hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows
     const long long chains = (long long)a.n_seq * a.H;
     const long long wgs2 = 8 * NSG * ((chains + 7) / 8);
     if (wgs2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rec_kernel<DK, DV, SPW, SNAP>), dim3((unsigned)wgs2), dim3(128), 0, stream, a,
+    hipLaunchKernelGGL((rec_kernel<DK, DV, SPW, SNAP>), dim3((unsigned)wgs2), dim3(SNAP ? 64 : 128), 0, stream, a,
                        (const unsigned char *)ws);
     return hipGetLastError();
 }
