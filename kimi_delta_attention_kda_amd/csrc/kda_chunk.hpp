@@ -38,7 +38,8 @@
 //      decayed operands, this block's partials of L, L^T and Mqk^T on the
 //      matrix core, layout copies of k~, k^r (and v);
 //   B1 (one wave): sums the partials, masks, beta, INV by Neumann squaring, INV beta;
-//   B2 (stage-A waves 1 ..): w (and u') on the matrix core.
+//   B2 (stage-A waves 1 ..): w on the matrix core (u' = INV beta v is formed
+//      by the recurrence's waves from the v C tiles).
 // The recurrence runs in consumer waves, each owning slabs of 16 state columns
 // in fp32 MFMA accumulators:
 //   W' = w S, Qs^T = S^T q~^T, decay, U = u' - W', O^T = Qs^T + U^T Mqk^T, S += k^r^T U.
@@ -195,15 +196,13 @@ struct Lay {
     static constexpr int NW = NPW + 1 + NCW;       // stage-A waves, the INV wave, consumers
     static constexpr int NTHR = 64 * NW;
     static constexpr int PAY = P::BYTES;          // consumer operands (4 buffers: written from 3 iterations ahead)
-    static constexpr int UP = NVT * 1024;         // u' C tiles [NVT][64] x 16 B fp32 (2 buffers)
-    static constexpr int KT = 0;                  // k~ C tiles [NMT][64] x 8 B  (3 buffers)
+    static constexpr int KT = 0;                  // k~ C tiles [NMT][64] x 8 B  (4 buffers)
     static constexpr int VT = KT + NMT * 512;     // v C tiles  [NVT][64] x 8 B
     static constexpr int KV = VT + NVT * 512;
     static constexpr int PART = NPW * 3 * 1024;   // per stage-A wave: L, L^T, Mqk^T partials (2 buffers)
     static constexpr int O_PAY = 0;
-    static constexpr int O_UP = O_PAY + 4 * PAY;
-    static constexpr int O_KV = O_UP + 2 * UP;
-    static constexpr int O_PART = O_KV + 3 * KV;
+    static constexpr int O_KV = O_PAY + 4 * PAY;
+    static constexpr int O_PART = O_KV + 4 * KV;
     static constexpr int O_BETA = O_PART + 2 * PART;   // beta [16] (2 buffers)
     static constexpr int O_SEQ = O_BETA + 2 * 64;      // the sequence this workgroup takes
     static constexpr int BYTES = O_SEQ + 16;

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a
             if (it >= 0) {
                 const int x = it;
                 const unsigned char *pay = lds + L::O_PAY + (x & 3) * L::PAY;
-                const unsigned char *ups = lds + L::O_UP + (x & 1) * L::UP;
+                const unsigned char *kvx = lds + L::O_KV + (x & 3) * L::KV;
                 if constexpr (SNAP) {
                     const size_t at = (((cbase + x) * H + c.head) * DV + col0) * DK;
 #pragma unroll
@@ -132,9 +132,10 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a
                     kr[m] = *reinterpret_cast<const bf16x4 *>(pay + P::KR + (m * 64 + lane) * 8);
                 }
                 const bf16x4 mq = *reinterpret_cast<const bf16x4 *>(pay + P::MQ + lane * 8);
+                const bf16x4 ibx = *reinterpret_cast<const bf16x4 *>(pay + P::IB + lane * 8);
 #pragma unroll
-                for (int j = 0; j < SPW; ++j)
-                    up[j] = *reinterpret_cast<const f32x4 *>(ups + ((cw * SPW + j) * 64 + lane) * 16);
+                for (int j = 0; j < SPW; ++j)   // u' = INV beta v from the chunk's v C tiles
+                    up[j] = mma16(ibx, *reinterpret_cast<const bf16x4 *>(kvx + L::VT + ((cw * SPW + j) * 64 + lane) * 8), Z4);
                 rec_step<NKB, NMT, SPW>(S, qf, wf, kr, eg, mq, up, O);
                 const int rem = min(CH, c.len - x * CH);
                 if (ln < rem) {
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a
     auto part = [&](int x) { return reinterpret_cast<f32x4 *>(lds + L::O_PART + (x & 1) * L::PART); };
     auto beta = [&](int x) { return reinterpret_cast<float *>(lds + L::O_BETA + (x & 1) * 64); };
     auto pay = [&](int x) { return lds + L::O_PAY + (x & 3) * L::PAY; };
-    auto kv = [&](int x) { return lds + L::O_KV + (x % 3) * L::KV; };
+    auto kv = [&](int x) { return lds + L::O_KV + (x & 3) * L::KV; };
     if (wv == NPW) {
         // the INV wave: stage B1 of chunk it + 2 in iteration it
         for (int it = -3; it < c.nch; ++it) {
@@ -190,19 +191,12 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a
         }
         const int xb = it + 1;
         if (wv > 0 && xb >= 0 && xb < c.nch) {
-            // stage B2: w fragments into the chunk's operands, u' tiles
+            // stage B2: w fragments into the chunk's operands
             const bf16x4 ib = *reinterpret_cast<const bf16x4 *>(pay(xb) + P::IB + lane * 8);
             const unsigned char *kvb = kv(xb);
-            unsigned char *ups = lds + L::O_UP + (xb & 1) * L::UP;
-            for (int job = wv - 1; job < NKB + NVT; job += NPW - 1) {
-                if (job < NKB) {
-                    *reinterpret_cast<bf16x8 *>(pay(xb) + P::WF + (job * 64 + lane) * 16) =
-                        w_frag(kvb + L::KT, ib, job, lane);
-                } else {
-                    const int n = job - NKB;
-                    const bf16x4 vt = *reinterpret_cast<const bf16x4 *>(kvb + L::VT + (n * 64 + lane) * 8);
-                    *reinterpret_cast<f32x4 *>(ups + (n * 64 + lane) * 16) = mma16(ib, vt, Z4);
-                }
+            for (int job = wv - 1; job < NKB; job += NPW - 1) {
+                *reinterpret_cast<bf16x8 *>(pay(xb) + P::WF + (job * 64 + lane) * 16) =
+                    w_frag(kvb + L::KT, ib, job, lane);
             }
         }
         lds_barrier();
