@@ -291,11 +291,12 @@ __global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdA
 //    slot the loader then refills.
 //  - With snapshots (8 KiB of stores per chunk and slab) one wave issues both
 //    its loads and its stores, which measured faster.
-template <int DK, int DV, int SPW, bool SNAP>
-__global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char *ws)
+template <int DK, int DV, int NSW, bool SNAP>
+__global__ __launch_bounds__(64 * (NSW + 1)) void rec_kernel(FwdArgs a, const unsigned char *ws)
 {
     constexpr bool LOADER = !SNAP;   // a separate loader wave
-    constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * SPW);
+    static_assert(LOADER || NSW == 1, "the snapshot form runs one wave per slab group");
+    constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * NSW);
     using P = Pay<DK>;
     constexpr int NPAY = (P::BYTES + 1023) / 1024;   // 1 KiB loads of a workspace row
     constexpr int ND = NPAY + 1;                     // and one for the v tile
@@ -303,16 +304,18 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
     static_assert((RING - 1) * ND <= 63, "loads in flight exceed the vmcnt field");
     __shared__ __attribute__((aligned(1024))) unsigned char ring[RING * SLOT];
     const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
-    const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 1;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool loader = LOADER && wv == NSW;
     const int b8 = blockIdx.x / 8;
     const int chain = 8 * (b8 / NSG) + blockIdx.x % 8;
     const int sg = b8 % NSG;
     if (chain >= a.n_seq * a.H) return;
     const Chain c = chain_of(a, chain / a.H, chain % a.H, threadIdx.x == 0 && sg == 0);
     const size_t H = a.H;
-    const int col0 = sg * SPW * 16;
+    const int cols = sg * NSW * 16;                  // the group's first column
+    const int col0 = cols + 16 * (loader ? 0 : wv);  // this wave's slab
     const size_t hbase = (((size_t)(c.hrow < 0 ? 0 : c.hrow) * H + c.head) * DV + col0) * DK;
-    f32x4 S[SPW][NMT];   // the state (recurrence wave), from h0 below
+    f32x4 S[1][NMT];   // the state of this wave's slab, from h0 below
     const size_t cbase = chunk_base(a, c.seq);
     // identity as a K = 16 B operand: the product of a row-loaded 16 x 16 tile with it is its C layout
     bf16x4 eye;
@@ -320,14 +323,14 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
     for (int e = 0; e < 4; ++e) eye[e] = static_cast<__bf16>(4 * lq + e == ln ? 1.f : 0.f);
     const unsigned ring_lds =
         __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) unsigned char *)ring);
-    // v tile in LDS: token t at t * 32 SPW bytes, 8 columns per lane; for SPW = 1
-    // lanes 32 .. 63 repeat lanes 0 .. 31 into the unused upper half.
-    const int vt_tok = (lane & 63) / (2 * SPW) % 16, vt_col = 8 * ((lane & 63) % (2 * SPW));
+    // v tile of the group in LDS: token t at t * 32 NSW bytes, 8 columns per
+    // lane; for NSW = 1 lanes 32 .. 63 repeat lanes 0 .. 31 into the unused upper half.
+    const int vt_tok = lane / (2 * NSW) % 16, vt_col = 8 * (lane % (2 * NSW));
     auto issue = [&](int x) {   // chunk x's loads into ring slot x % RING
         const unsigned slot = ring_lds + (unsigned)((x % RING) * SLOT);
         dma_bytes<P::BYTES>(ws + ((cbase + x) * H + c.head) * P::BYTES, slot, lane);
         const int rem = min(CH, c.len - x * CH);
-        const uint16_t *v0 = static_cast<const uint16_t *>(a.v) + ((c.bos + (size_t)x * CH) * H + c.head) * DV + col0;
+        const uint16_t *v0 = static_cast<const uint16_t *>(a.v) + ((c.bos + (size_t)x * CH) * H + c.head) * DV + cols;
         dma_group<1>(v0, 0u, (unsigned)(((size_t)min(vt_tok, rem - 1) * H * DV + vt_col) * 2), slot + VT);
     };
     auto step = [&](int x) {
@@ -335,18 +338,13 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
         if constexpr (SNAP) {
             const size_t at = (((cbase + x) * H + c.head) * DV + col0) * DK;
 #pragma unroll
-            for (int j = 0; j < SPW; ++j)
-#pragma unroll
-                for (int m = 0; m < NMT; ++m)
-                    __builtin_nontemporal_store(S[j][m], reinterpret_cast<f32x4 *>(
-                        a.h_chunks + at + (size_t)(16 * j + ln) * DK + chan(m, lq, 0)));
+            for (int m = 0; m < NMT; ++m)
+                __builtin_nontemporal_store(S[0][m], reinterpret_cast<f32x4 *>(
+                    a.h_chunks + at + (size_t)ln * DK + chan(m, lq, 0)));
         }
         // operands from the ring slot, in the order the chunk consumes them:
-        // v as lane (lq, ln) = token ln, columns 4 lq .. +3 of each 16-column slab
-        bf16x4 vv[SPW];
-#pragma unroll
-        for (int j = 0; j < SPW; ++j)
-            vv[j] = *reinterpret_cast<const bf16x4 *>(row + VT + ln * 32 * SPW + (16 * j + 4 * lq) * 2);
+        // v as lane (lq, ln) = token ln, columns 4 lq .. +3 of this wave's slab
+        const bf16x4 vv = *reinterpret_cast<const bf16x4 *>(row + VT + ln * 32 * NSW + (col0 - cols + 4 * lq) * 2);
         const bf16x4 ib = *reinterpret_cast<const bf16x4 *>(row + P::IB + lane * 8);
         bf16x8 qf[NKB], wf[NKB];
         bf16x4 kr[NMT];
@@ -360,20 +358,14 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
         const bf16x4 mq = *reinterpret_cast<const bf16x4 *>(row + P::MQ + lane * 8);
 #pragma unroll
         for (int m = 0; m < NMT; ++m) kr[m] = *reinterpret_cast<const bf16x4 *>(row + P::KR + (m * 64 + lane) * 8);
-        f32x4 up[SPW], O[SPW];
-#pragma unroll
-        for (int j = 0; j < SPW; ++j)   // u' = INV beta v (v in C layout by an identity product)
-            up[j] = mma16(ib, pack4(mma16(vv[j], eye, Z4)), Z4);
-        rec_step<NKB, NMT, SPW>(S, qf, wf, kr, eg, mq, up, O);
+        f32x4 up[1], O[1];
+        up[0] = mma16(ib, pack4(mma16(vv, eye, Z4)), Z4);   // u' = INV beta v (v in C layout by an identity product)
+        rec_step<NKB, NMT, 1>(S, qf, wf, kr, eg, mq, up, O);
         const int rem = min(CH, c.len - x * CH);
-        if (ln < rem) {
-#pragma unroll
-            for (int j = 0; j < SPW; ++j)
-                store_o(a.o, c.bos + (size_t)x * CH + ln, H, c.head, DV, col0 + 16 * j + 4 * lq, O[j], a.scale);
-        }
+        if (ln < rem) store_o(a.o, c.bos + (size_t)x * CH + ln, H, c.head, DV, col0 + 4 * lq, O[0], a.scale);
     };
     const int nch = c.nch;
-    if (LOADER && loader) {
+    if (loader) {
         for (int x = 0; x < min(RING - 1, nch); ++x) issue(x);
         for (int x = 0; x < nch; ++x) {
             vm_wait_chunks<ND>(min(RING - 2, nch - 1 - x));   // chunk x has landed
@@ -383,12 +375,9 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
         return;
     }
 #pragma unroll
-    for (int j = 0; j < SPW; ++j)
-#pragma unroll
-        for (int m = 0; m < NMT; ++m)
-            S[j][m] = (a.h0 && c.hrow >= 0)
-                          ? *reinterpret_cast<const f32x4 *>(a.h0 + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0))
-                          : Z4;
+    for (int m = 0; m < NMT; ++m)
+        S[0][m] = (a.h0 && c.hrow >= 0) ? *reinterpret_cast<const f32x4 *>(a.h0 + hbase + (size_t)ln * DK + chan(m, lq, 0))
+                                        : Z4;
     if constexpr (LOADER) {
         for (int x = 0; x < nch; ++x) {
             lds_barrier();   // chunk x has landed; every read of chunk x - 1 is done
@@ -406,16 +395,11 @@ __global__ __launch_bounds__(128) void rec_kernel(FwdArgs a, const unsigned char
     }
     if (a.h_T && c.hrow >= 0) {
 #pragma unroll
-        for (int j = 0; j < SPW; ++j)
-#pragma unroll
-            for (int m = 0; m < NMT; ++m)
-                *reinterpret_cast<f32x4 *>(a.h_T + hbase + (size_t)(16 * j + ln) * DK + chan(m, lq, 0)) = S[j][m];
+        for (int m = 0; m < NMT; ++m)
+            *reinterpret_cast<f32x4 *>(a.h_T + hbase + (size_t)ln * DK + chan(m, lq, 0)) = S[0][m];
     }
 }
 
-#ifndef KDA_REC_SPW
-#define KDA_REC_SPW 1
-#endif
 
 namespace {
 
@@ -454,8 +438,21 @@ hipError_t launch_one_pass(const FwdArgs &a, int n_cu, hipStream_t stream)
     }
 }
 
+template <int DK, int DV, int NSW, bool SNAP>
+hipError_t launch_rec(const FwdArgs &a, unsigned char *ws, long long chains, hipStream_t stream)
+{
+    constexpr int NSG = DV / (16 * NSW);
+    const long long wgs = 8 * NSG * ((chains + 7) / 8);
+    if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((rec_kernel<DK, DV, NSW, SNAP>), dim3((unsigned)wgs), dim3(SNAP ? 64 : 64 * (NSW + 1)), 0,
+                       stream, a, (const unsigned char *)ws);
+    return hipGetLastError();
+}
+
+// The recurrence takes two slabs per workgroup (one payload load for both)
+// where that still gives every compute unit a workgroup.
 template <int DK, int DV, bool SNAP>
-hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows, hipStream_t stream)
+hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows, int n_cu, hipStream_t stream)
 {
     const long long wgs1 = (n_rows * a.H + PREP_WAVES - 1) / PREP_WAVES;
     if (wgs1 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -464,13 +461,10 @@ hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    constexpr int SPW = KDA_REC_SPW, NSG = DV / (16 * SPW);
     const long long chains = (long long)a.n_seq * a.H;
-    const long long wgs2 = 8 * NSG * ((chains + 7) / 8);
-    if (wgs2 > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rec_kernel<DK, DV, SPW, SNAP>), dim3((unsigned)wgs2), dim3(SNAP ? 64 : 128), 0, stream, a,
-                       (const unsigned char *)ws);
-    return hipGetLastError();
+    if constexpr (!SNAP)
+        if (chains * (DV / 32) >= n_cu) return launch_rec<DK, DV, 2, SNAP>(a, ws, chains, stream);
+    return launch_rec<DK, DV, 1, SNAP>(a, ws, chains, stream);
 }
 
 template <int DK, int DV>
@@ -479,8 +473,8 @@ hipError_t launch_dims(const FwdArgs &a, int n_cu, void *ws, size_t ws_bytes, lo
     const long long chains = (long long)a.n_seq * a.H;
     const bool two = ws && chains < n_cu && ws_bytes >= fwd_workspace_bytes(DK, n_rows, a.H);
     if (two)
-        return a.h_chunks ? launch_two_pass<DK, DV, true>(a, static_cast<unsigned char *>(ws), n_rows, stream)
-                          : launch_two_pass<DK, DV, false>(a, static_cast<unsigned char *>(ws), n_rows, stream);
+        return a.h_chunks ? launch_two_pass<DK, DV, true>(a, static_cast<unsigned char *>(ws), n_rows, n_cu, stream)
+                          : launch_two_pass<DK, DV, false>(a, static_cast<unsigned char *>(ws), n_rows, n_cu, stream);
     return a.h_chunks ? launch_one_pass<DK, DV, true>(a, n_cu, stream) : launch_one_pass<DK, DV, false>(a, n_cu, stream);
 }
 
