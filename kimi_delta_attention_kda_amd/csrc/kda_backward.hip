@@ -123,18 +123,19 @@ struct GRow {
     static constexpr int BYTES = DU + 8 * 1024;
 };
 
-// The reverse chain: one workgroup of two waves per (chain, 16 state
-// columns), chunks from last to first: wave 0 carries dS' (fp32, in the
-// forward state's registers and layout) from dh_T, leaves dS' and dU in a
-// gradient row for every chunk and the gradient before the first chunk in
-// dh0; wave 1 only loads.  Operands reach a ring of LDS slots by direct
-// global-to-LDS loads, RING - 1 chunks ahead, issued, counted and handed over
-// (one barrier per chunk) as in the prefill's rec_kernel.
-template <int DK, int DV>
-__global__ __launch_bounds__(128) void bwd_rec_kernel(FwdArgs a, const unsigned char *ws, const float *dh_T,
+// The reverse chain: one workgroup per (chain, NSW slabs of 16 state
+// columns), chunks from last to first: wave j < NSW carries its slab's dS'
+// (fp32, in the forward state's registers and layout) from dh_T, leaves dS'
+// and dU in a gradient row for every chunk and the gradient before the first
+// chunk in dh0; wave NSW only loads, once for the group.  Operands reach a
+// ring of LDS slots by direct global-to-LDS loads, RING - 1 chunks ahead,
+// issued, counted and handed over (one barrier per chunk) as in the
+// prefill's rec_kernel.
+template <int DK, int DV, int NSW>
+__global__ __launch_bounds__(64 * (NSW + 1)) void bwd_rec_kernel(FwdArgs a, const unsigned char *ws, const float *dh_T,
                                                       const void *dO, unsigned char *grows, float *dh0)
 {
-    constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / 16;
+    constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * NSW);
     static_assert(DK == 128 && DV == 128, "gradient rows are laid out for d = 128");
     using P = BPay<DK>;
     constexpr int NPAY = (P::REC + 1023) / 1024;
@@ -143,14 +144,17 @@ __global__ __launch_bounds__(128) void bwd_rec_kernel(FwdArgs a, const unsigned 
     static_assert((RING - 1) * ND <= 63, "loads in flight exceed the vmcnt field");
     __shared__ __attribute__((aligned(1024))) unsigned char ring[RING * SLOT];
     const int lane = threadIdx.x & 63, ln = lane & 15, lq = lane >> 4;
-    const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 1;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool loader = wv == NSW;
     const int b8 = blockIdx.x / 8;
     const int chain = 8 * (b8 / NSG) + blockIdx.x % 8;
     const int sg = b8 % NSG;
     if (chain >= a.n_seq * a.H) return;
     const Chain c = chain_of(a, chain / a.H, chain % a.H, false);
     const size_t H = a.H;
-    const int col0 = sg * 16;
+    const int cols = sg * NSW * 16;                  // the group's first column
+    const int slab = sg * NSW + (loader ? 0 : wv);   // this wave's slab
+    const int col0 = 16 * slab;
     const size_t hbase = (((size_t)c.seq * H + c.head) * DV + col0) * DK;
     f32x4 dS[NMT];   // the reverse chain's gradient (wave 0), from dh_T below
     const size_t cbase = chunk_base(a, c.seq);
@@ -159,14 +163,15 @@ __global__ __launch_bounds__(128) void bwd_rec_kernel(FwdArgs a, const unsigned 
     for (int e = 0; e < 4; ++e) eye[e] = static_cast<__bf16>(4 * lq + e == ln ? 1.f : 0.f);
     const unsigned ring_lds =
         __builtin_amdgcn_readfirstlane((unsigned)(size_t)(__attribute__((address_space(3))) unsigned char *)ring);
-    const int vt_tok = (lane / 2) % 16, vt_col = 8 * (lane % 2);
+    // dO tile of the group in LDS: token t at t * 32 NSW bytes, 8 columns per lane
+    const int vt_tok = lane / (2 * NSW) % 16, vt_col = 8 * (lane % (2 * NSW));
     // the kk-th chunk walked is chunk nch - 1 - kk
     auto issue = [&](int kk) {
         const int x = c.nch - 1 - kk;
         const unsigned slot = ring_lds + (unsigned)((kk % RING) * SLOT);
         dma_bytes<P::REC>(ws + ((cbase + x) * H + c.head) * P::BYTES, slot, lane);
         const int rem = min(CH, c.len - x * CH);
-        const uint16_t *d0 = static_cast<const uint16_t *>(dO) + ((c.bos + (size_t)x * CH) * H + c.head) * DV + col0;
+        const uint16_t *d0 = static_cast<const uint16_t *>(dO) + ((c.bos + (size_t)x * CH) * H + c.head) * DV + cols;
         // dO rows past the sequence's end are zero gradients: the load re-reads
         // the last live row (in bounds) and the step zeroes it
         dma_group<1>(d0, 0u, (unsigned)(((size_t)min(vt_tok, rem - 1) * H * DV + vt_col) * 2), slot + DT);
@@ -179,9 +184,9 @@ __global__ __launch_bounds__(128) void bwd_rec_kernel(FwdArgs a, const unsigned 
 #pragma unroll
         for (int cb = 0; cb < NKB; ++cb)
             __builtin_nontemporal_store(cat4(pack4(dS[2 * cb]), pack4(dS[2 * cb + 1])),
-                                        reinterpret_cast<bf16x8 *>(g + GRow::DM + (sg * NKB + cb) * 1024 + lane * 16));
+                                        reinterpret_cast<bf16x8 *>(g + GRow::DM + (slab * NKB + cb) * 1024 + lane * 16));
         const int rem = min(CH, c.len - x * CH);
-        bf16x4 dOr = *reinterpret_cast<const bf16x4 *>(row + DT + ln * 32 + 8 * lq);
+        bf16x4 dOr = *reinterpret_cast<const bf16x4 *>(row + DT + ln * 32 * NSW + (col0 - cols + 4 * lq) * 2);
         if (ln >= rem) dOr = bf16x4{};
         const bf16x4 ms = *reinterpret_cast<const bf16x4 *>(row + P::MS + lane * 8);
         bf16x8 kra[NKB];
@@ -204,7 +209,7 @@ __global__ __launch_bounds__(128) void bwd_rec_kernel(FwdArgs a, const unsigned 
         }
         const bf16x4 bdO = pack4(mma16(dOr, eye, Z4));              // C layout of dO (exact)
         dU = mma16(ms, bdO, dU + dU2);
-        __builtin_nontemporal_store(dU, reinterpret_cast<f32x4 *>(g + GRow::DU + sg * 1024 + lane * 16));
+        __builtin_nontemporal_store(dU, reinterpret_cast<f32x4 *>(g + GRow::DU + slab * 1024 + lane * 16));
         const bf16x8 bdU = hilo(dU);
         // dS = D dS' - w^T dU + q~^T dO_s
 #pragma unroll
@@ -781,13 +786,25 @@ hipError_t launch_bwd_chunkwise(const BwdArgs &b, long long n_rows, hipStream_t 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // two slabs per workgroup (one payload load for both) where that still
+    // gives every compute unit a workgroup
     const long long chains = (long long)b.n_seq * b.H;
-    const long long wgs = 8 * 8 * ((chains + 7) / 8);
+    int dev = 0, n_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const bool two = chains * 4 >= n_cu;
+    const long long wgs = 8 * (two ? 4 : 8) * ((chains + 7) / 8);
     if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (wgs > 0) {
-        hipLaunchKernelGGL((bwd_rec_kernel<128, 128>), dim3((unsigned)wgs), dim3(128), 0, stream, a, ws + l.pay,
-                           b.dh_T, b.do_, ws + l.grow, b.dh0);
-        hipError_t e = hipGetLastError();
+        if (two)
+            hipLaunchKernelGGL((bwd_rec_kernel<128, 128, 2>), dim3((unsigned)wgs), dim3(192), 0, stream, a, ws + l.pay,
+                               b.dh_T, b.do_, ws + l.grow, b.dh0);
+        else
+            hipLaunchKernelGGL((bwd_rec_kernel<128, 128, 1>), dim3((unsigned)wgs), dim3(128), 0, stream, a, ws + l.pay,
+                               b.dh_T, b.do_, ws + l.grow, b.dh0);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (items > 0) {
