@@ -270,32 +270,33 @@ __global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdA
         *reinterpret_cast<bf16x8 *>(pw + P::WF + (s2 * 64 + lane) * 16) = w_frag2(kt[2 * s2], kt[2 * s2 + 1], ib);
 }
 
-// Pass 2: one workgroup per (sequence, head, SPW slabs of 16 columns).
-// Workgroup b takes chain 8 (b / 8 / NSG) + b % 8 and slab group
-// (b / 8) % NSG, so that the slab groups of a chain share blockIdx % 8 (the
-// XCD, whose L2 then serves the chain's operands to all of them; placement
-// only affects speed).
+// Pass 2: one workgroup per (sequence, head, NSW slabs of 16 columns), one
+// wave per slab.  Workgroup b takes chain 8 (b / 8 / NSG) + b % 8 and slab
+// group (b / 8) % NSG, so that the slab groups of a chain share blockIdx % 8
+// (the XCD, whose L2 then serves the chain's operands to all of them;
+// placement only affects speed).
 //
 // A chunk's operands (its workspace row, padded to whole KiB, and the
-// slabs' 16 x 16 SPW bf16 tile of v) reach a ring of RING LDS slots by direct
-// global-to-LDS loads, RING - 1 chunks ahead, so the recurrence never waits
-// on memory latency.  The loads are issued from inline assembly (the
-// compiler would otherwise wait for all of them before every LDS read).  Each
-// is counted in its wave's vmcnt, which drains in issue order, so waiting
-// until at most n operations remain outstanding, n = those issued after
-// chunk x's loads, guarantees chunk x has landed.
-//  - Without snapshots the workgroup has two waves: wave 0 runs the
-//    recurrence and wave 1 only loads, so the loads' issue cycles leave the
-//    state's critical path.  One barrier per chunk: at barrier x chunk x has
-//    landed and the recurrence has read every operand of chunk x - 1, whose
+// group's 16 x 16 NSW bf16 tile of v) reach a ring of RING LDS slots by
+// direct global-to-LDS loads, RING - 1 chunks ahead, so the recurrence never
+// waits on memory latency; the slabs of a group share them, which halves the
+// load instructions per slab with NSW = 2 (they, not the arithmetic, set the
+// pace where two workgroups share a compute unit).  The loads are issued
+// from inline assembly (the compiler would otherwise wait for all of them
+// before every LDS read).  Each is counted in its wave's vmcnt, which drains
+// in issue order, so waiting until at most n operations remain outstanding,
+// n = those issued after chunk x's loads, guarantees chunk x has landed.
+//  - With a loader wave (wave NSW), the loads' issue cycles leave the slab
+//    waves' critical path.  One barrier per chunk: at barrier x chunk x has
+//    landed and every slab wave has read every operand of chunk x - 1, whose
 //    slot the loader then refills.
-//  - With snapshots (8 KiB of stores per chunk and slab) one wave issues both
-//    its loads and its stores, which measured faster.
+//  - The snapshot form with one slab per group (8 KiB of snapshot stores per
+//    chunk) runs one wave that issues its loads and stores and waits on its
+//    own count, which measured faster than a loader there.
 template <int DK, int DV, int NSW, bool SNAP>
 __global__ __launch_bounds__(64 * (NSW + 1)) void rec_kernel(FwdArgs a, const unsigned char *ws)
 {
-    constexpr bool LOADER = !SNAP;   // a separate loader wave
-    static_assert(LOADER || NSW == 1, "the snapshot form runs one wave per slab group");
+    constexpr bool LOADER = !SNAP || NSW > 1;   // a separate loader wave (wave NSW)
     constexpr int NKB = DK / 32, NMT = DK / 16, NSG = DV / (16 * NSW);
     using P = Pay<DK>;
     constexpr int NPAY = (P::BYTES + 1023) / 1024;   // 1 KiB loads of a workspace row
@@ -444,7 +445,7 @@ hipError_t launch_rec(const FwdArgs &a, unsigned char *ws, long long chains, hip
     constexpr int NSG = DV / (16 * NSW);
     const long long wgs = 8 * NSG * ((chains + 7) / 8);
     if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((rec_kernel<DK, DV, NSW, SNAP>), dim3((unsigned)wgs), dim3(SNAP ? 64 : 64 * (NSW + 1)), 0,
+    hipLaunchKernelGGL((rec_kernel<DK, DV, NSW, SNAP>), dim3((unsigned)wgs), dim3(SNAP && NSW == 1 ? 64 : 64 * (NSW + 1)), 0,
                        stream, a, (const unsigned char *)ws);
     return hipGetLastError();
 }
@@ -462,8 +463,7 @@ hipError_t launch_two_pass(const FwdArgs &a, unsigned char *ws, long long n_rows
         if (e != hipSuccess) return e;
     }
     const long long chains = (long long)a.n_seq * a.H;
-    if constexpr (!SNAP)
-        if (chains * (DV / 32) >= n_cu) return launch_rec<DK, DV, 2, SNAP>(a, ws, chains, stream);
+    if (chains * (DV / 32) >= n_cu) return launch_rec<DK, DV, 2, SNAP>(a, ws, chains, stream);
     return launch_rec<DK, DV, 1, SNAP>(a, ws, chains, stream);
 }
 
