@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the KDA hot path on one MI355X.
 
-One step = one kda_chunk_fwd over the headline prefill workload (config 2:
+One step = one kda_chunk_fwd over the headline prefill workload (the
 32 packed sequences of U[128, 8192] tokens, H=32, d_k=d_v=128, bf16, fp32
 initial states, chunk 16) followed by one kda_decode_step over the decode
 workload (B=256, H=HV=32, K=V=128, pool of 512 fp32 states, 8 pad rows).
@@ -13,13 +13,13 @@ Mtok*head/s (token-heads per call / mean device time per call).  Device times
 come from HIP events recorded on the stream the kernels run on.  `roofline`
 describes the headline prefill's kernel (one launch per call on this
 workload) against MI355X's HBM peak, from the workload's algorithmic bytes.
-`configs` gives every config of the contract: the fp32 tiny prefill (0), the
+`configs` gives every workload of the set, keyed 0-4: the fp32 tiny prefill (0), the
 B=4 T=4096 prefill (1), the headline (2), the T=131072 single-sequence
 prefill (3) and the decode step (4), each with its time, throughput, achieved
 GB/s and TFLOP/s and their fractions of the HBM and bf16 MFMA peaks.
 `cpu_baseline` is the fp64 oracle (plain C, OpenMP over chains) on a bounded
 sample of the headline workload, timed on the host cores.  Outside the step,
-on config 1's shapes: the pool-addressed prefill, the materialised form
+on the B=4 T=4096 prefill's shapes: the pool-addressed prefill, the materialised form
 (kda_chunk_fwd_states, then the chunk-parallel output pass) and kda_backward;
 on the decode workload's rows: kda_decode_extend (T = 4) and
 kda_conv_decode_step (width 4).  `copy_reference` is a plain device copy of
@@ -44,7 +44,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 F32_MFMA_PEAK_TFLOPS = 157.3    # dense fp32 MFMA
 PROFILES = os.path.join(ROOT, "profiles")
-HEADLINE = 2                    # the prefill config the headline is quoted on
+HEADLINE = 2                    # key of the prefill workload the headline is quoted on
 
 
 def prefill_flops_per_tokhead(dk, dv, C=16):
@@ -120,12 +120,12 @@ KERNEL_SOURCES = {
     "chunk_o": [_C + "kda_chunk_o.hip"] + _COMMON,
 }
 # kernel-name patterns of the instantiations the workloads launch: the
-# headline's one-pass kernel (many chains), the two passes of configs 1 and 3
+# headline's one-pass kernel (many chains), the two passes of the few-chain prefills
 # (fewer chains than compute units), the decode family, the backward's three
 # passes (chunk-parallel gradients, reverse chain, operands) and the
 # chunk-parallel output kernel
 KERNEL_MATCH = {"fwd": "kda::fwd_kernel<128, 128, 4, 2, false>", "prep": "kda::prep_kernel<128>",
-                "rec": "kda::rec_kernel<128, 128, 1, false>", "decode": "kda::decode_kernel",
+                "rec": "kda::rec_kernel<128, 128, 2, false>", "decode": "kda::decode_kernel",
                 "extend": "kda::extend_kernel", "conv_decode": "kda::conv_decode_kernel",
                 "backward": "kda::bwd_chunk_kernel", "bwd_rec": "kda::bwd_rec_kernel",
                 "bwd_prep": "kda::bwd_prep_kernel", "chunk_o": "kda::chunk_o_kernel"}
@@ -455,7 +455,7 @@ def main():
     dec_graph_avg = evg[0].elapsed_time(evg[1]) * 1e-3 / K
     del dgraph
 
-    # ---------------- every prefill config, timed the same way (the headline's own
+    # ---------------- every prefill workload, timed the same way (the headline's own
     # timing is the step's)
     per_cfg = {}
     for i in cfg_ids:
@@ -489,7 +489,7 @@ def main():
                     "roofline_us": round(dbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
                     "timing": "HIP graph of the K decode steps, per step"}
 
-    # ---------------- outside the step, on config 1's shapes and the decode workload
+    # ---------------- outside the step, on the B=4 T=4096 prefill's shapes and the decode workload
     extra = {}
     if not args.profile and 1 in probs:
         p1, pin1, o1, hT1, _ = probs[1]
