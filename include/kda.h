@@ -105,7 +105,8 @@ typedef enum {
  *     kda_chunk_fwd_workspace_bytes() bytes and the (sequence, head) chains are
  *     fewer than the compute units): a fully parallel pass writes every
  *     chunk's consumer operands into the workspace, then one wave per
- *     (sequence, head, 16 state columns) runs the recurrence from them.
+ *     (sequence, head, 16 state columns), in workgroups of one or two such
+ *     waves and a loader wave, runs the recurrence from them.
  * Both give the same results up to rounding order.  No workgroup waits on
  * another.  Packed sequences are scheduled longest first (up to 128).
  *

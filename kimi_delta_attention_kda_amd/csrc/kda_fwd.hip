@@ -31,9 +31,10 @@
 //     compute units: every chunk's prep runs once, all chunks in parallel, and
 //     its consumer operands (q~, w, k^r, e^{G_C}, Mqk^T, INV beta; 13.5 KiB
 //     per chunk and head at d_k = 128) go to the caller's workspace; then one
-//     single-wave workgroup per (sequence, head, 16 columns) walks the chunks,
-//     its operands arriving RING - 1 chunks ahead in an LDS ring, forming
-//     u' = INV beta v from its own columns of v and running the recurrence.
+//     wave per (sequence, head, 16 columns) walks the chunks, its operands
+//     arriving RING - 1 chunks ahead in an LDS ring (issued by a loader wave
+//     that serves one or two such waves), forming u' = INV beta v from its own
+//     columns of v and running the recurrence.
 //     No workgroup waits on another in either pass.
 #include <stdint.h>
 
