@@ -143,15 +143,35 @@ __device__ __forceinline__ f32x4 prod(f32x4 XT, f32x4 Y) { return mma16(pack4(XT
 
 // DPP inside a 16-lane row: inclusive scan over the row's 16 tokens, and the
 // broadcast of lane n of the row.
+// Both read 0 from a source lane outside the row (bound control set), so no
+// register has to be cleared first.
+template <int CTRL>
+__device__ __forceinline__ float dpp_z(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF,
+                                                                 true));
+}
 __device__ __forceinline__ float scan16(float x) {
-    x += dpp_f<0x111>(x);
-    x += dpp_f<0x112>(x);
-    x += dpp_f<0x114>(x);
-    x += dpp_f<0x118>(x);
+    x += dpp_z<0x111>(x);
+    x += dpp_z<0x112>(x);
+    x += dpp_z<0x114>(x);
+    x += dpp_z<0x118>(x);
     return x;
 }
+// The same scan over 8 independent values, step by step across all of them
+// (each step's 8 operations are independent, so no DPP read waits on the
+// write just before it).
+__device__ __forceinline__ void scan16x8(float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += dpp_z<0x111>(x[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += dpp_z<0x112>(x[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += dpp_z<0x114>(x[e]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] += dpp_z<0x118>(x[e]);
+}
 template <int N>
-__device__ __forceinline__ float row_bcast(float x) { return dpp_f<0x150 + N>(x); }
+__device__ __forceinline__ float row_bcast(float x) { return dpp_z<0x150 + N>(x); }
 
 __device__ __forceinline__ void lds_barrier() {   // LDS-only barrier: global loads stay in flight
     __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0)
@@ -289,31 +309,38 @@ struct Prep {
     __device__ __forceinline__ void stage_a_core(const In<VPW> &in, int rem, Out &o) const {
         const bool live = t < rem;
         const float nA = live ? -A_exp : 0.f;
-        float kf[8], qfv[8], gv[8], Gm[8], GC[8], kd[8], qd[8], krv[8];
-        const uint32_t kw[4] = {in.k.x, in.k.y, in.k.z, in.k.w};
-        const uint32_t qw[4] = {in.q.x, in.q.y, in.q.z, in.q.w};
+        float kf[8], qfv[8], gv[8], Gm[8], kd[8], qd[8], krv[8];
+        // pad tokens: k and q read as zero (their rows repeat the last live row)
+        const uint32_t lm = live ? 0xffffffffu : 0u;
+        const uint32_t kw[4] = {in.k.x & lm, in.k.y & lm, in.k.z & lm, in.k.w & lm};
+        const uint32_t qw[4] = {in.q.x & lm, in.q.y & lm, in.q.z & lm, in.q.w & lm};
         const uint32_t aw[4] = {in.a.x, in.a.y, in.a.z, in.a.w};
-        bool deep = false;
+        // the gate is never positive, so G falls along the chunk and its lowest value
+        // over all lanes is the lowest chunk total G_C
+        float gmin = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int sh = (e & 1) ? 0 : 16;
             const uint32_t mk = (e & 1) ? 0xffff0000u : 0xffffffffu;
-            kf[e] = live ? __builtin_bit_cast(float, (kw[e >> 1] << sh) & mk) : 0.f;
-            qfv[e] = live ? __builtin_bit_cast(float, (qw[e >> 1] << sh) & mk) : 0.f;
+            kf[e] = __builtin_bit_cast(float, (kw[e >> 1] << sh) & mk);
+            qfv[e] = __builtin_bit_cast(float, (qw[e >> 1] << sh) & mk);
             const float af = __builtin_bit_cast(float, (aw[e >> 1] << sh) & mk);
             const float y = __builtin_fmaf(af, kLog2e, dtl[e]);        // (a + dt_bias) log2 e
             const float sp = y > 20.0f * kLog2e ? y : __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(y));
             gv[e] = nA * sp;                                            // gate, log2 units; pads do not decay
-            Gm[e] = scan16(gv[e]);
-            GC[e] = row_bcast<15>(Gm[e]);
-            deep |= GC[e] < -100.f;
+            Gm[e] = gv[e];
+        }
+        scan16x8(Gm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            gmin = fminf(gmin, Gm[e]);
             o.e1[e] = __builtin_amdgcn_exp2f(Gm[e]);
             kd[e] = kf[e] * o.e1[e];
             qd[e] = qfv[e] * o.e1[e];
         }
         o.bkd = pack8(kd);
         o.bqd = pack8(qd);
-        if (__ballot(deep) == 0) {
+        if (__ballot(gmin < -100.f) == 0) {
             // mild: rows k~ (<= 1), columns k 2^-G (<= 2^100); k^r = k 2^-G 2^{G_C}
             float kh[8];
 #pragma unroll
@@ -331,7 +358,7 @@ struct Prep {
             float Gp[8], Bf1[8], R[8], Rq[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                krv[e] = kf[e] * __builtin_amdgcn_exp2f(GC[e] - Gm[e]);
+                krv[e] = kf[e] * __builtin_amdgcn_exp2f(row_bcast<15>(Gm[e]) - Gm[e]);
                 Gp[e] = scan16(fmaxf(gv[e], -CLIP));
                 Bf1[e] = row_bcast<7>(Gp[e]);
                 const float f = __builtin_amdgcn_exp2f(Gp[e] - (t >= 8 ? Bf1[e] : 0.f));   // <= 1
