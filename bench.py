@@ -34,6 +34,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -235,25 +236,46 @@ def measured_mfma():
 
 def trace_summary(trace_dir, title, command, out_name):
     """profiles/<out_name>.md: the per-kernel table of a rocprofv3 --kernel-trace
-    --stats run (its kernel_stats.csv), with the command that made it."""
-    stats = None
+    --stats run (its kernel_stats.csv), with the command that made it.  Where the
+    run also left its kernel_trace.csv and the command names `--steps N`, a
+    column gives each kernel's mean over its last N dispatches: the timed steps
+    (warm-up dispatches, run while the GPU's clocks still ramp, excluded)."""
+    stats = trace = None
     for root, _, files in os.walk(trace_dir):
         for f in files:
             if f.endswith("kernel_stats.csv"):
                 stats = os.path.join(root, f)
+            elif f.endswith("kernel_trace.csv"):
+                trace = os.path.join(root, f)
     if stats is None:
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     with open(stats) as fh:
         rows = list(csv.DictReader(fh))
+    m = re.search(r"--steps (\d+)", command)
+    last = {}
+    if trace is not None and m:
+        n = int(m.group(1))
+        durs = {}
+        with open(trace) as fh:
+            for r in csv.DictReader(fh):
+                durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        last = {k: sum(v[-n:]) / n for k, v in durs.items() if len(v) >= n}
+    head = "| kernel | calls | average ns | min ns | max ns | share of GPU time |"
+    rule = "|---|---|---|---|---|---|"
+    if last:
+        head += f" average ns, last {n} dispatches |"
+        rule += "---|"
     lines = [f"# {title}", "", "One MI355X (gfx950), ROCm 7.2, rocprofv3.  Command (from the repository root"
-             " on the GPU machine, `$R` = that root):", "", "```", command, "```", "",
-             "| kernel | calls | average ns | min ns | max ns | share of GPU time |", "|---|---|---|---|---|---|"]
+             " on the GPU machine, `$R` = that root):", "", "```", command, "```", "", head, rule]
     for r in rows:
         name = r["Name"].replace("|", "/")
         if len(name) > 90:
             name = name[:90]
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
-                     f"{float(r['MaxNs']):.0f} | {float(r['Percentage']):.1f} % |")
+        line = (f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {float(r['MinNs']):.0f} | "
+                f"{float(r['MaxNs']):.0f} | {float(r['Percentage']):.1f} % |")
+        if last:
+            line += f" {last[r['Name']]:.0f} |" if r["Name"] in last else " |"
+        lines.append(line)
     with open(os.path.join(PROFILES, out_name + ".md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(os.path.join(PROFILES, out_name + ".md"))
