@@ -314,16 +314,17 @@ def cpu_model():
 
 
 def time_calls(fn, reps, torch):
-    """Mean seconds per call of fn() over reps back-to-back calls, from HIP
-    events recorded on the current stream between the calls."""
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    """Mean seconds per call of fn() over reps back-to-back calls, from two HIP
+    events recorded on the current stream before the first call and after the
+    last (no marker between the calls, so none adds its own gap)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     ev[0].record()
-    for s in range(reps):
+    for _ in range(reps):
         fn()
-        ev[s + 1].record()
+    ev[1].record()
     torch.cuda.synchronize()
-    return sum(ev[s].elapsed_time(ev[s + 1]) for s in range(reps)) * 1e-3 / reps
+    return ev[0].elapsed_time(ev[1]) * 1e-3 / reps
 
 
 def main():
