@@ -252,13 +252,17 @@ struct Prep {
     float A_exp, dtl[8];
     bf16x8 sel_c[2], sel_v[2];
 
-    __device__ __forceinline__ void init(const FwdArgs &a, int head, int wave, int lane_) {
+    // the channel block and lane (all that load needs)
+    __device__ __forceinline__ void place(int wave, int lane_) {
         w = wave;
         lane = lane_;
         ln = lane & 15;
         lq = lane >> 4;
         t = ln;
         r = lq;
+    }
+    __device__ __forceinline__ void init(const FwdArgs &a, int head, int wave, int lane_) {
+        place(wave, lane_);
         A_exp = expf(a.A_log[head]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) dtl[e] = a.dt_bias[(size_t)head * DK + 32 * w + 8 * r + e] * kLog2e;

@@ -237,14 +237,21 @@ __global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdA
     f32x4 Lm = Z4, LT = Z4, MT = Z4;
     bf16x4 kt[NMT];
     float beta = 0.f;
+    // every block's inputs are requested before the first is used: the two
+    // halves of each 256-byte row of q, k and g_raw arrive together
+    In<0> in[NPW];
+#pragma unroll
+    for (int w = 0; w < NPW; ++w) {
+        Prep<DK, 0> pr;
+        pr.place(w, lane);
+        pr.load(in[w], a, p.bos, p.len, p.x, head, 0, 0, 0, 0);
+    }
 #pragma unroll
     for (int w = 0; w < NPW; ++w) {
         Prep<DK, 0> pr;
         pr.init(a, head, w, lane);
-        In<0> in;
-        pr.load(in, a, p.bos, p.len, p.x, head, 0, 0, 0, 0);
         typename Prep<DK, 0>::Out o;
-        pr.stage_a_core(in, rem, o);
+        pr.stage_a_core(in[w], rem, o);
         *reinterpret_cast<bf16x8 *>(pw + P::QF + (w * 64 + lane) * 16) = o.bqd;
         pr.store_eg(o, reinterpret_cast<float *>(pw + P::EG));
         Lm += o.pL;
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(64 * PREP_WAVES) KDA_PREP_OCC void prep_kernel(FwdA
             kt[2 * w + h] = pr.ctile(o.bkd, h);
             *reinterpret_cast<bf16x4 *>(pw + P::KR + ((2 * w + h) * 64 + lane) * 8) = pr.ctile(o.bkr, h);
         }
-        if (w == 0) beta = ln < rem ? sigmoid_f(bf16_to_f32(in.b)) : 0.f;
+        if (w == 0) beta = ln < rem ? sigmoid_f(bf16_to_f32(in[0].b)) : 0.f;
     }
     // beta of tokens 4 lq .. +3 and of token ln, through this wave's LDS row
     if (lq == 0) l_beta[wv][ln] = beta;
