@@ -12,8 +12,11 @@
 // The fp32 build serves the small fp32 workload, whose tolerance (1e-4
 // max-abs) asks for fp32 arithmetic throughout.  One 256-thread workgroup per
 // (sequence, head) walks its chunks in order with everything in LDS:
-//   * gate, cumulative gate and per-token decays per channel (one thread per
-//     channel, the 16 tokens in order);
+//   * the next chunk's inputs loaded into registers while the current chunk
+//     computes;
+//   * gate and per-token decays per (token, channel), the cumulative gate per
+//     channel (one thread per channel, 16 adds), the decayed operands per
+//     (token, channel);
 //   * L and Mqk exactly: for column j the factor e^{G_i - G_j} of rows i >= j
 //     is the running product of the tokens' decays (all <= 1), so no factored
 //     e^{+-G} can overflow; the channel sums are 16-lane DPP reductions;
@@ -48,7 +51,7 @@ struct F32Lay {
     float v[CH][DV], u[CH][DV];
     float S[DK][DV];
     float Lm[CH][CH], Mq[CH][CH];
-    float beta[CH], eg[DK];
+    float beta[CH], eg[DK], gc[DK];
 };
 
 }  // namespace
@@ -95,6 +98,34 @@ __global__ __launch_bounds__(NTHR) void fwd_f32_kernel(FwdArgs a)
     const float *gr = static_cast<const float *>(a.g_raw), *v = static_cast<const float *>(a.v);
     const float *br = static_cast<const float *>(a.beta_raw);
     float *o = static_cast<float *>(a.o);
+    // Thread tid takes elements tid + NTHR r of a chunk's 16 x DK (and 16 x DV)
+    // tiles: always channel tid % DK, tokens tid / DK + 4 r.
+    constexpr int NE = CH * DK / NTHR, NV = CH * DV / NTHR;
+    static_assert(NTHR % DK == 0 && NTHR % DV == 0, "element ownership");
+    const int ce = tid % DK;
+    const float dtb = a.dt_bias[(size_t)head * DK + ce];
+    float rq[NE], rk[NE], rg[NE], rv[NV], rb = 0.f;
+    // chunk x's inputs into the registers (rows past the sequence's end are
+    // not read; they are zeroed when the registers are stored)
+    auto load = [&](int x) {
+        const int rem = min(CH, len - x * CH);
+        const size_t tok0 = bos + (size_t)x * CH;
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+            const int tt = (tid + NTHR * r) / DK;
+            const size_t g = ((tok0 + min(tt, rem - 1)) * H + head) * DK + ce;
+            rq[r] = q[g];
+            rk[r] = k[g];
+            rg[r] = gr[g];
+        }
+#pragma unroll
+        for (int r = 0; r < NV; ++r) {
+            const int i = tid + NTHR * r, tt = i / DV;
+            rv[r] = v[((tok0 + min(tt, rem - 1)) * H + head) * DV + i % DV];
+        }
+        if (tid < CH) rb = br[(tok0 + min(tid, rem - 1)) * H + head];
+    };
+    if (nch > 0) load(0);
     sync_lds();
 
     for (int x = 0; x < nch; ++x) {
@@ -104,42 +135,47 @@ __global__ __launch_bounds__(NTHR) void fwd_f32_kernel(FwdArgs a)
             const size_t at = ((cbase + x) * H + head) * DV * DK;
             for (int i = tid; i < DK * DV; i += NTHR) a.h_chunks[at + i] = sm.S[i % DK][i / DK];
         }
-        // ---- inputs (pad tokens: zero)
-        for (int i = tid; i < CH * DK; i += NTHR) {
-            const int tt = i / DK, cc = i % DK;
+        // ---- inputs (pad tokens: zero), the gate and the per-token decays
+#pragma unroll
+        for (int r = 0; r < NE; ++r) {
+            const int tt = (tid + NTHR * r) / DK;
             const bool live = tt < rem;
-            const size_t g = ((tok0 + tt) * H + head) * DK + cc;
-            sm.q[tt][cc] = live ? q[g] : 0.f;
-            sm.k[tt][cc] = live ? k[g] : 0.f;
-            sm.kt[tt][cc] = live ? gr[g] : 0.f;   // g_raw, replaced below by k~
+            sm.q[tt][ce] = live ? rq[r] : 0.f;
+            sm.k[tt][ce] = live ? rk[r] : 0.f;
+            const float g = live ? -A_exp * softplus_f(rg[r] + dtb) : 0.f;
+            sm.kt[tt][ce] = g;   // the gate, replaced below by its cumulative sum, then by k~
+            sm.dd[tt][ce] = expf(g);
         }
-        for (int i = tid; i < CH * DV; i += NTHR) {
-            const int tt = i / DV, vv = i % DV;
-            sm.v[tt][vv] = tt < rem ? v[((tok0 + tt) * H + head) * DV + vv] : 0.f;
+#pragma unroll
+        for (int r = 0; r < NV; ++r) {
+            const int i = tid + NTHR * r, tt = i / DV;
+            sm.v[tt][i % DV] = tt < rem ? rv[r] : 0.f;
         }
-        if (tid < CH) sm.beta[tid] = tid < rem ? sigmoid_f(br[(tok0 + tid) * H + head]) : 0.f;
+        if (tid < CH) sm.beta[tid] = tid < rem ? sigmoid_f(rb) : 0.f;
+        if (x + 1 < nch) load(x + 1);   // in flight while this chunk computes
         sync_lds();
-        // ---- gate per channel: decays, cumulative gate, decayed operands
+        // ---- cumulative gate per channel
         if (tid < DK) {
-            const int cc = tid;
-            const float dtb = a.dt_bias[(size_t)head * DK + cc];
             float G = 0.f;
-            float Gs[CH];
 #pragma unroll
             for (int tt = 0; tt < CH; ++tt) {
-                const float g = tt < rem ? -A_exp * softplus_f(sm.kt[tt][cc] + dtb) : 0.f;
-                G += g;
-                Gs[tt] = G;
-                sm.dd[tt][cc] = expf(g);
+                G += sm.kt[tt][tid];
+                sm.kt[tt][tid] = G;
             }
+            sm.eg[tid] = expf(G);
+            sm.gc[tid] = G;
+        }
+        sync_lds();
+        // ---- decayed operands per (token, channel)
+        const float GC = sm.gc[ce];   // the chunk's total gate in this channel
 #pragma unroll
-            for (int tt = 0; tt < CH; ++tt) {
-                const float e = expf(Gs[tt]);
-                sm.kt[tt][cc] = sm.k[tt][cc] * e;
-                sm.qt[tt][cc] = sm.q[tt][cc] * e * a.scale;
-                sm.kr[tt][cc] = sm.k[tt][cc] * expf(G - Gs[tt]);
-            }
-            sm.eg[cc] = expf(G);
+        for (int r = 0; r < NE; ++r) {
+            const int tt = (tid + NTHR * r) / DK;
+            const float Gs = sm.kt[tt][ce];
+            const float e = expf(Gs);
+            sm.kt[tt][ce] = sm.k[tt][ce] * e;
+            sm.qt[tt][ce] = sm.q[tt][ce] * e * a.scale;
+            sm.kr[tt][ce] = sm.k[tt][ce] * expf(GC - Gs);
         }
         sync_lds();
         // ---- L and Mqk: thread (j, cg) sums channels cg, cg + 16, ...; rows i >= j
