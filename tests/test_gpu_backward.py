@@ -105,6 +105,13 @@ def test_backward_gate_stress_no_dhT():
     check(p, 502, what="bwd gate-stress", with_dhT=False)
 
 
+def test_backward_many_chains_short():
+    """64 (sequence, head) chains of 40 tokens: the reverse chain takes two slabs
+    per workgroup here (the small cases above take one); three heads are checked."""
+    p = synth.prefill(505, B=1, T=40, H=64, dk=128, dv=128, dtype="bf16", with_h0=True)
+    check(p, 505, heads=[0, 37, 63], what="bwd B1 T40 H64", params=False)
+
+
 def test_backward_deterministic():
     p = synth.prefill(503, B=2, T=50, H=2, dk=128, dv=128, dtype="bf16", with_h0=True)
     g1, _, _ = run(p, 503)
