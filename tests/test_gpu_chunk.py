@@ -49,6 +49,7 @@ SMALL = [
     dict(B=1, T=200, H=4, dk=128, dv=128, dtype="bf16", gate_stress=0.05),
     dict(B=1, T=64, H=2, dk=64, dv=64, dtype="f32", gate_stress=0.1, A_log_hi=math.log(64)),
     dict(B=2, T=45, H=2, dk=64, dv=128, dtype="f32", with_h0=True),
+    dict(B=1, T=1003, H=2, dk=64, dv=64, dtype="f32", with_h0=True),
 ]
 
 
