@@ -90,6 +90,10 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a
     if (wv > NPW) {
         // ======================================================= consumer
         const int cw = wv - NPW - 1;
+        // wave priority 1 here and in the stage-A waves, the B1 wave keeps 0: B1
+        // has slack in every iteration, and the wave that shares a SIMD with a
+        // stage-A wave and B1 sets the pace
+        __builtin_amdgcn_s_setprio(1);
         f32x4 S[SPW][NMT];
 #pragma unroll
         for (int j = 0; j < SPW; ++j) {
@@ -174,6 +178,7 @@ __global__ __launch_bounds__(64 * (DK / 32 + 1 + NCW)) void fwd_kernel(FwdArgs a
         }
         return;
     }
+    __builtin_amdgcn_s_setprio(1);   // as the consumers (the B1 wave keeps 0)
     Prep<DK, VPW> pr;
     pr.init(a, c.head, wv, lane);
     In<VPW> in0, in1;
